@@ -1,0 +1,192 @@
+"""The oracle pinned against brute force, closed forms and invariants (CPU).
+
+The pages print no worked example, output values or error bound, so every pin
+here comes from the mathematics of the method: see ``tests/pins.py``.  The
+mutation tests plant plausible mistakes in a copy of the oracle's C source,
+compile that copy on the CPU, and check that the pins reject it -- evidence
+that the pins can tell a right oracle from a wrong one.
+"""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_passes_pin(pin):
+    pin(oracle.scan)
+
+
+def test_linear_attention_pin_rejects_strict_mask():
+    # The convention check: the A = 0 closed form with a strictly lower mask
+    # (the reading y_t = c_t^T h_{t-1}) must NOT match the oracle.
+    pr = pins.problem(41, b=1, L=12, nh=2, p=3, n=5, h0=True)
+    pr["A"] = np.zeros_like(pr["A"])
+    y, _, _ = oracle.scan(**pr)
+    y_strict = pins.linear_attention(pr["x"], pr["dt"], pr["B"], pr["C"], pr["D"], pr["h0"], k=-1)
+    assert pins.rel_err(y, y_strict) > 1e-2
+
+
+def test_chunked_reference_with_strict_mask_disagrees():
+    pr = pins.problem(5, L=9)
+    y, _, _ = oracle.scan(**pr)
+    yc, _ = pins.chunked(**pr, T=4, strict_mask=True)
+    assert pins.rel_err(y, yc) > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# helpers of the oracle package
+# ---------------------------------------------------------------------------
+
+
+def test_chunk_cumsum_matches_loop_definition():
+    rng = np.random.default_rng(3)
+    b, L, nh, T = 2, 37, 3, 8
+    dt = rng.uniform(0, 2, (b, L, nh))
+    A = -rng.uniform(1, 5, nh)
+    G = oracle.chunk_cumsum(dt, A, T)
+    nc = -(-L // T)
+    assert G.shape == (b, nh, nc * T)
+    for bi in range(b):
+        for h in range(nh):
+            for c in range(nc):
+                run = 0.0
+                for i in range(T):
+                    t = c * T + i
+                    if t < L:
+                        run += A[h] * dt[bi, t, h]
+                    assert abs(G[bi, h, t] - run) <= 1e-12 * max(1.0, abs(run))
+
+
+def test_chunk_states_match_bruteforce():
+    pr = pins.problem(8, b=2, L=19, nh=4, p=3, n=5, g=2, h0=False)
+    T = 6
+    S = oracle.chunk_states(pr["x"], pr["dt"], pr["A"], pr["B"], pr["C"], T)
+    nc = -(-19 // T)
+    assert S.shape == (2, 4, nc, 3, 5)
+    for c in range(nc):
+        sl = slice(c * T, min(19, (c + 1) * T))
+        part = {k: (v[:, sl] if k in ("x", "dt", "B", "C") else v) for k, v in pr.items()}
+        _, fr = pins.bruteforce(**part)
+        assert pins.rel_err(S[:, :, c], fr) < 1e-11
+
+
+def test_chunk_start_states_match_chunked_reference():
+    pr = pins.problem(9, b=1, L=21, nh=2, p=3, n=4, h0=True)
+    T = 5
+    ck = oracle.chunk_start_states(pr["x"], pr["dt"], pr["A"], pr["B"], pr["C"], T, pr["h0"])
+    assert ck.shape[2] == 5
+    np.testing.assert_allclose(ck[:, :, 0], pr["h0"], rtol=0, atol=0)
+    for c in range(1, 5):
+        pre = {k: (v[:, : c * T] if k in ("x", "dt", "B", "C") else v) for k, v in pr.items()}
+        _, fr = pins.chunked(**pre, T=T)
+        assert pins.rel_err(ck[:, :, c], fr) < 1e-12
+
+
+def test_oracle_rejects_bad_arguments():
+    pr = pins.problem(1)
+    with pytest.raises(ValueError):
+        oracle.scan(pr["x"], pr["dt"], pr["A"][:1], pr["B"], pr["C"])
+    with pytest.raises(ValueError):
+        oracle.scan(pr["x"], pr["dt"], pr["A"], pr["B"], pr["C"][:, :, :, :2])
+
+
+# ---------------------------------------------------------------------------
+# golden fixtures
+# ---------------------------------------------------------------------------
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_golden_scalar_halving():
+    """Hand-derived values (geometric series), see the fixture's citation."""
+    with open(os.path.join(GOLDEN, "scalar_halving.json")) as f:
+        g = json.load(f)
+    L = len(g["y"])
+    x = np.ones((1, L, 1, 1))
+    dt = np.ones((1, L, 1))
+    A = np.array([-np.log(2.0)])
+    B = np.ones((1, L, 1, 1))
+    C = np.ones((1, L, 1, 1))
+    y, fin, _ = oracle.scan(x, dt, A, B, C)
+    np.testing.assert_allclose(y[0, :, 0, 0], g["y"], rtol=1e-14)
+    np.testing.assert_allclose(fin[0, 0, 0, 0], g["y"][-1], rtol=1e-14)
+
+
+def test_golden_oracle_regression():
+    """The oracle still produces what ``make_golden.py`` stored from it."""
+    with open(os.path.join(GOLDEN, "oracle_tiny.json")) as f:
+        g = json.load(f)
+    inp = {k: (None if v is None else np.array(v, np.float64)) for k, v in g["inputs"].items()}
+    y, fin, _ = oracle.scan(**inp)
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(fin, np.array(g["final"]), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# mutation tests: planted mistakes must be caught by the pins
+# ---------------------------------------------------------------------------
+
+_SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
+
+MUTANTS = {
+    # readout with the pre-update state (the h_{t-1} reading)
+    "readout_before_update": (
+        "                    s[n] = decay * s[n] + (dt_t * B_t[n]) * x_tp;\n"
+        "                    /* y_t = c_t^T h_t  (post-update state) */\n"
+        "                    acc += C_t[n] * s[n];\n",
+        "                    acc += C_t[n] * s[n];\n"
+        "                    s[n] = decay * s[n] + (dt_t * B_t[n]) * x_tp;\n"),
+    "dropped_skip": ("acc + d_skip * x_tp;", "acc;"),
+    "decay_sign": ("exp(A[h] * dt_t)", "exp(-A[h] * dt_t)"),
+    "group_mapping": ("const int64_t g = h / heads_per_group;",
+                      "const int64_t g = h % ngroups;"),
+    "transposed_initial_state": ("h0[((b * nheads + h) * headdim + p) * dstate + n]",
+                                 "h0[((b * nheads + h) * dstate + n) * headdim + p]"),
+    "missing_dt_in_input": ("(dt_t * B_t[n]) * x_tp", "B_t[n] * x_tp"),
+    "decay_after_input": ("s[n] = decay * s[n] + (dt_t * B_t[n]) * x_tp;",
+                          "s[n] = decay * (s[n] + (dt_t * B_t[n]) * x_tp);"),
+    "checkpoint_off_by_one": ("t % ckpt_stride == 0", "(t + 1) % ckpt_stride == 0"),
+    "y_uses_B_not_C": ("acc += C_t[n] * s[n];", "acc += B_t[n] * s[n];"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_libs(tmp_path_factory):
+    src = open(_SRC).read()
+    d = tmp_path_factory.mktemp("mutants")
+    libs = {}
+    for name, (old, new) in MUTANTS.items():
+        assert old in src, "mutation target vanished: %s" % name
+        cpath = d / (name + ".c")
+        cpath.write_text(src.replace(old, new, 1))
+        so = d / ("lib" + name + ".so")
+        subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(cpath),
+                        "-o", str(so), "-lm"], check=True)
+        libs[name] = oracle.load_library(str(so))
+    return libs
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, mutant_libs):
+    lib = mutant_libs[name]
+
+    def scan(*a, **k):
+        return oracle.scan_with(lib, *a, **k)
+
+    failed = []
+    for pin in pins.ALL_PINS:
+        if pin is pins.pin_bruteforce_mp:
+            continue  # slow; the fp64 brute force covers the same ground
+        try:
+            pin(scan)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, "no pin caught mutant %s" % name
