@@ -1,0 +1,148 @@
+/*
+ * ssd.h -- C ABI of libssd: the Mamba-2 chunked SSD forward pass on gfx950.
+ *
+ * The operation ("Accelerating Mamba-2 with High-Performance Forward Pass
+ * Kernels in NVIDIA CUDA Tile", section "Mamba-2 architecture"): for every
+ * batch b and head h, with group g = h / (nheads / ngroups),
+ *
+ *     h_t = exp(A[h] dt_t) h_{t-1} + dt_t B_t x_t^T        (state, dstate x headdim)
+ *     y_t = C_t^T h_t + D[h] x_t                          (readout after the update)
+ *
+ * evaluated chunk by chunk as the pages' three stages (cumulative sum of
+ * a_t = A dt_t per chunk; state jump across chunks; chunk output with the
+ * causal mask that keeps the diagonal).  The result equals the recurrence up to
+ * floating-point rounding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are dense, row-major (C-contiguous) DEVICE buffers owned by the
+ *   caller.  The library allocates nothing, keeps no pointer after a call
+ *   returns, holds no mutable global state and is reentrant.
+ * - x, dt, B, C and y have the element type `shape->dtype` (fp32 or bf16); A,
+ *   D, the workspace and both state tensors are always fp32.
+ * - Layouts (the tile layouts of the pages' kernel sections):
+ *       x, y            (batch, seqlen, nheads, headdim)
+ *       dt              (batch, seqlen, nheads)
+ *       A, D            (nheads)
+ *       B, C            (batch, seqlen, ngroups, dstate)
+ *       initial_states,
+ *       final_states    (batch, nheads, headdim, dstate)   -- the state h^T
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *   the call returns without synchronising.  Buffers must stay valid until the
+ *   stream reaches that point.  A fault inside a kernel surfaces at the
+ *   caller's next synchronisation of the stream.
+ * - Preconditions not checked (checking would need a device read): A <= 0 and
+ *   dt >= 0 (so every a_t <= 0, which is what keeps the chunk-output
+ *   exponentials bounded), and finite inputs.  Violating them gives
+ *   unspecified values, never an out-of-bounds access.
+ * - All argument checks happen before the first launch; on any error nothing
+ *   is enqueued and the outputs are untouched.  No exception crosses the ABI.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERROR_INVALID_VALUE = 1, /* NULL required pointer, negative size, nheads % ngroups != 0, aliasing */
+    SSD_ERROR_UNSUPPORTED = 2,   /* valid problem outside the sizes the kernels are built for */
+    SSD_ERROR_MISALIGNED = 3,    /* a pointer below its required alignment */
+    SSD_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than ssd_chunk_scan_fwd_workspace_size */
+    SSD_ERROR_LAUNCH = 5         /* the HIP runtime refused a launch or an event record */
+} ssd_status;
+
+/* Keep the per-chunk input states s_c and the chunk-start states h_c in two
+ * separate workspace regions (tests read both).  Without it the state-passing
+ * stage overwrites s_c with h_c in place. */
+enum { SSD_FLAG_KEEP_INTERMEDIATES = 1u };
+
+typedef struct {
+    int64_t batch;    /* >= 0 (0: nothing to do) */
+    int64_t seqlen;   /* >= 0 (0: final_states = initial_states or 0) */
+    int64_t nheads;   /* >= 1 */
+    int64_t headdim;  /* P: supported 32, 64, 128 */
+    int64_t dstate;   /* N: supported multiples of 16 in [16, 256] */
+    int64_t ngroups;  /* >= 1, divides nheads; heads share B/C contiguously */
+    int32_t dtype;    /* ssd_dtype */
+    uint32_t flags;   /* SSD_FLAG_* */
+} ssd_shape;
+
+/* Byte offsets of the intermediates inside the workspace (each 256-byte
+ * aligned).  Lp = nchunks * chunk_size, nchunks = ceil(seqlen / chunk_size).
+ *   G2  fp32 (batch, nheads, Lp): log2(e) * per-chunk inclusive cumsum of A dt
+ *       (the pages' G, kept in base-2 units so kernels use exp2); positions
+ *       past seqlen are padded with dt = 0 and so stay flat.
+ *   DT  fp32 (batch, nheads, Lp): dt widened to fp32, head-major, zero padded.
+ *   S   fp32 (batch, nheads, nchunks, headdim, dstate): after the call, the
+ *       chunk-start states h_c (the state before the chunk's first token);
+ *       with SSD_FLAG_KEEP_INTERMEDIATES, the per-chunk input states s_c
+ *       (what a chunk alone adds to a zero state).
+ *   H   (only with SSD_FLAG_KEEP_INTERMEDIATES) same shape as S: h_c. */
+typedef struct {
+    size_t g2, dt, s, h, total;
+    int64_t nchunks, padded_len;
+} ssd_workspace_layout;
+
+/* Workspace bytes for this problem; 0 when the shape or chunk size is invalid
+ * or unsupported. */
+size_t ssd_chunk_scan_fwd_workspace_size(const ssd_shape *shape, int64_t chunk_size);
+
+/* Fill *layout for this problem (host only, no device access). */
+ssd_status ssd_chunk_scan_fwd_workspace_layout(const ssd_shape *shape, int64_t chunk_size,
+                                               ssd_workspace_layout *layout);
+
+/* The forward pass.
+ *   x, dt, B, C      inputs (dtype), 16-byte aligned (dt: element aligned)
+ *   A                fp32 (nheads), required
+ *   D                fp32 (nheads), NULL => no skip term
+ *   chunk_size       T: 64, 128 or 256
+ *   initial_states   fp32 or NULL => zero state; may alias final_states
+ *   y                output (dtype), 16-byte aligned; must not overlap any input
+ *   final_states     fp32 output or NULL => not written; the state after the
+ *                    last token
+ *   workspace        device scratch of at least
+ *                    ssd_chunk_scan_fwd_workspace_size(shape, chunk_size)
+ *                    bytes, 256-byte aligned; its contents on entry are
+ *                    ignored and on return hold the intermediates described by
+ *                    ssd_workspace_layout
+ *   stream           hipStream_t or NULL
+ * Four kernels run in stream order: chunk cumsum, chunk state, state passing,
+ * chunk output. */
+ssd_status ssd_chunk_scan_fwd(const ssd_shape *shape,
+                              const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              int64_t chunk_size, const float *initial_states,
+                              void *y, float *final_states,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Same as ssd_chunk_scan_fwd; in addition records the five hipEvent_t in
+ * stage_events[0..4] on `stream` before the first kernel, between the kernels
+ * and after the last, so a caller can time each stage.  stage_events must
+ * point to 5 valid events. */
+ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape,
+                                       const void *x, const void *dt, const float *A,
+                                       const void *B, const void *C, const float *D,
+                                       int64_t chunk_size, const float *initial_states,
+                                       void *y, float *final_states,
+                                       void *workspace, size_t workspace_bytes, void *stream,
+                                       void *const *stage_events);
+
+/* Static, human-readable description of a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

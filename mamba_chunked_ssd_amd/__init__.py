@@ -1,0 +1,237 @@
+"""mamba_chunked_ssd_amd -- the Mamba-2 chunked SSD forward pass on MI355X (gfx950).
+
+A thin ctypes binding over ``libssd.so`` (C ABI in ``include/ssd.h``).  It only
+marshals arguments: torch provides device memory and the current stream, and
+every step of the forward pass runs in the library's HIP kernels.  There is no
+CPU fallback: if the library is missing, importing works but any call raises.
+
+    y = chunk_scan_fwd(x, dt, A, B, C, D, chunk_size=256)
+    y, final = chunk_scan_fwd(..., initial_states=h0, return_final_states=True)
+
+The operation is the selective state-space recurrence of "Accelerating Mamba-2
+with High-Performance Forward Pass Kernels in NVIDIA CUDA Tile" (section
+"Mamba-2 architecture"): h_t = exp(A dt_t) h_{t-1} + dt_t B_t x_t^T,
+y_t = C_t^T h_t + D x_t, for every batch and head.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssd.so")
+
+SSD_DTYPE_F32 = 0
+SSD_DTYPE_BF16 = 1
+SSD_FLAG_KEEP_INTERMEDIATES = 1
+
+STATUS = {
+    0: "SSD_OK",
+    1: "SSD_ERROR_INVALID_VALUE",
+    2: "SSD_ERROR_UNSUPPORTED",
+    3: "SSD_ERROR_MISALIGNED",
+    4: "SSD_ERROR_WORKSPACE",
+    5: "SSD_ERROR_LAUNCH",
+}
+
+# Symbols include/ssd.h declares (checked by the CPU tests).
+EXPORTS = [
+    "ssd_chunk_scan_fwd_workspace_size",
+    "ssd_chunk_scan_fwd_workspace_layout",
+    "ssd_chunk_scan_fwd",
+    "ssd_chunk_scan_fwd_profiled",
+    "ssd_status_string",
+    "ssd_version",
+]
+
+
+class SSDError(RuntimeError):
+    """A non-OK status from libssd."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s: %s (%s)" % (where, STATUS.get(status, "status %d" % status), status_string(status))
+        super().__init__(msg)
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [
+        ("g2", ctypes.c_size_t),
+        ("dt", ctypes.c_size_t),
+        ("s", ctypes.c_size_t),
+        ("h", ctypes.c_size_t),
+        ("total", ctypes.c_size_t),
+        ("nchunks", ctypes.c_int64),
+        ("padded_len", ctypes.c_int64),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libssd.so (built in-tree by ``mamba_chunked_ssd_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                "libssd.so is not built (%s); run `python -m mamba_chunked_ssd_amd.build` "
+                "or __graft_entry__.build()" % p)
+        lib = ctypes.CDLL(p)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        sp = ctypes.POINTER(Shape)
+        lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [sp, i64]
+        lib.ssd_chunk_scan_fwd_workspace_size.restype = sz
+        lib.ssd_chunk_scan_fwd_workspace_layout.argtypes = [sp, i64, ctypes.POINTER(WorkspaceLayout)]
+        lib.ssd_chunk_scan_fwd_workspace_layout.restype = ctypes.c_int
+        fwd_args = [sp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+        lib.ssd_chunk_scan_fwd.argtypes = fwd_args
+        lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_profiled.argtypes = fwd_args + [ctypes.POINTER(ctypes.c_void_p)]
+        lib.ssd_chunk_scan_fwd_profiled.restype = ctypes.c_int
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_version.argtypes = []
+        lib.ssd_version.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().ssd_status_string(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "?"
+
+
+def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, keep=False) -> Shape:
+    if dtype in ("bf16", SSD_DTYPE_BF16):
+        code = SSD_DTYPE_BF16
+    elif dtype in ("f32", SSD_DTYPE_F32):
+        code = SSD_DTYPE_F32
+    else:
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return Shape(batch, seqlen, nheads, headdim, dstate, ngroups, code,
+                 SSD_FLAG_KEEP_INTERMEDIATES if keep else 0)
+
+
+def workspace_size(shape: Shape, chunk_size: int) -> int:
+    return int(load_library().ssd_chunk_scan_fwd_workspace_size(ctypes.byref(shape), chunk_size))
+
+
+def workspace_layout(shape: Shape, chunk_size: int) -> WorkspaceLayout:
+    lay = WorkspaceLayout()
+    st = load_library().ssd_chunk_scan_fwd_workspace_layout(ctypes.byref(shape), chunk_size,
+                                                            ctypes.byref(lay))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_workspace_layout")
+    return lay
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states=None,
+                   return_final_states: bool = False, *, out=None, final_out=None,
+                   workspace=None, keep_intermediates: bool = False, stream=None,
+                   events=None):
+    """Run ``ssd_chunk_scan_fwd`` on the current (or given) stream.
+
+    x (b, L, nh, p) and dt (b, L, nh), B/C (b, L, g, n): float32 or bfloat16,
+    all the same dtype; A (nh,), D (nh,) or None, initial_states
+    (b, nh, p, n) or None: float32.  Returns y, or (y, final_states).
+    ``workspace`` (uint8 device tensor) may be passed to reuse an allocation;
+    with ``keep_intermediates`` its layout is :func:`workspace_layout` of the
+    shape with the keep flag.  ``events``: 5 raw hipEvent_t handles (ints) to
+    record around the four stages (``ssd_chunk_scan_fwd_profiled``).
+    """
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x and B must be 4-D")
+    b, L, nh, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    if x.dtype == torch.bfloat16:
+        dname = "bf16"
+    elif x.dtype == torch.float32:
+        dname = "f32"
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a ROCm device (got %s)" % dev)
+    _check(x, "x", x.dtype, (b, L, nh, p), dev)
+    _check(dt, "dt", x.dtype, (b, L, nh), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    _check(B, "B", x.dtype, (b, L, g, n), dev)
+    _check(C, "C", x.dtype, (b, L, g, n), dev)
+    if D is not None:
+        _check(D, "D", torch.float32, (nh,), dev)
+    if initial_states is not None:
+        _check(initial_states, "initial_states", torch.float32, (b, nh, p, n), dev)
+    shape = make_shape(b, L, nh, p, n, g, dname, keep_intermediates)
+    need = workspace_size(shape, chunk_size)  # 0 if invalid: the call reports why
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    y = out if out is not None else torch.empty_like(x)
+    if out is not None:
+        _check(out, "out", x.dtype, (b, L, nh, p), dev)
+    fin = None
+    if return_final_states or final_out is not None:
+        fin = final_out if final_out is not None else torch.empty((b, nh, p, n), dtype=torch.float32, device=dev)
+        _check(fin, "final_states", torch.float32, (b, nh, p, n), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    args = [ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            int(chunk_size), _ptr(initial_states), _ptr(y), _ptr(fin), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(s)]
+    if events is None:
+        st = lib.ssd_chunk_scan_fwd(*args)
+        where = "ssd_chunk_scan_fwd"
+    else:
+        ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) for e in events])
+        st = lib.ssd_chunk_scan_fwd_profiled(*args, ev)
+        where = "ssd_chunk_scan_fwd_profiled"
+    if st != 0:
+        raise SSDError(st, where)
+    if return_final_states:
+        return y, fin
+    return y

@@ -1,0 +1,120 @@
+// k1_cumsum.hip -- stage 1: per-chunk cumulative sum of the log decay.
+//
+// "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+// CUDA Tile", section "Kernel 1: Computing cumulative sums": the chunked
+// equations need G, the running sum of a_t = A dt_t inside each chunk
+// (restarting at every chunk), in both later stages, so it is computed once
+// and stored.  It is kept in base-2 units (G2 = log2(e) G) so that the later
+// stages use the native exp2.
+//
+// Design for gfx950: one block per (chunk, 16-head tile, batch).  The block
+// stages the chunk's dt tile [T tokens x 16 heads] in LDS (the token-major
+// input makes a per-head read strided), then each wave scans one head's chunk:
+// every lane sums T/64 consecutive tokens serially, the 64 lane totals are
+// scanned with wave shuffles, and each lane adds its exclusive prefix.  The
+// scan runs on a_t already scaled by log2(e), so rounding errors of the prefix
+// cancel in the differences G2_i - G2_j that the later stages exponentiate.
+// Outputs are head-major (batch, nheads, padded_len), so each (head, chunk)
+// is one contiguous run of T floats for the later stages; dt is also written
+// there widened to fp32.  Tokens past seqlen are treated as dt = 0: G2 stays
+// flat and DT is 0.
+#include "ssd_device.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kHeadTile = 16;
+
+template <typename Tin>
+__device__ __forceinline__ float load_dt(const Tin *p);
+template <>
+__device__ __forceinline__ float load_dt<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load_dt<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+template <typename Tin, int T>
+__global__ __launch_bounds__(256) void k1_cumsum(const Tin *__restrict__ dt,
+                                                 const float *__restrict__ A,
+                                                 float *__restrict__ G2, float *__restrict__ DT,
+                                                 int64_t seqlen, int nheads, int64_t Lp) {
+    constexpr int E = T / 64;  // tokens per lane
+    __shared__ float s_dt[kHeadTile][T + 1];
+
+    const int c = blockIdx.x;
+    const int h0 = blockIdx.y * kHeadTile;
+    const int64_t b = blockIdx.z;
+    const int tid = threadIdx.x;
+
+    // Stage dt[b, cT + t, h0 + j] -> s_dt[j][t]; consecutive threads read
+    // consecutive heads of one token.
+    for (int idx = tid; idx < T * kHeadTile; idx += 256) {
+        const int t = idx / kHeadTile, j = idx % kHeadTile;
+        const int64_t tok = (int64_t)c * T + t;
+        float v = 0.f;
+        if (tok < seqlen && h0 + j < nheads) v = load_dt(dt + (b * seqlen + tok) * nheads + h0 + j);
+        s_dt[j][t] = v;
+    }
+    __syncthreads();
+
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int j = wave; j < kHeadTile; j += 4) {
+        const int h = h0 + j;
+        if (h >= nheads) break;  // wave-uniform
+        const float a2 = A[h] * kLog2e;
+        float d[E], run[E];
+        float tot = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            d[e] = s_dt[j][lane * E + e];
+            tot += a2 * d[e];
+            run[e] = tot;
+        }
+        // Inclusive scan of the lane totals across the wave.
+        float inc = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += up;
+        }
+        const float excl = inc - tot;
+        float *g = G2 + (b * nheads + h) * Lp + (int64_t)c * T + lane * E;
+        float *o = DT + (b * nheads + h) * Lp + (int64_t)c * T + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            g[e] = excl + run[e];
+            o[e] = d[e];
+        }
+    }
+}
+
+template <typename Tin, int T>
+hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, float *G2, float *DT,
+                    hipStream_t stream) {
+    dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadTile - 1) / kHeadTile),
+              (unsigned)p.batch);
+    hipLaunchKernelGGL((k1_cumsum<Tin, T>), grid, dim3(256), 0, stream, dt, A, G2, DT, p.seqlen,
+                       (int)p.nheads, p.padded_len);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, float *G2, float *DT,
+                        hipStream_t stream) {
+    switch (p.chunk) {
+        case 64: return launch_t<Tin, 64>(p, dt, A, G2, DT, stream);
+        case 128: return launch_t<Tin, 128>(p, dt, A, G2, DT, stream);
+        case 256: return launch_t<Tin, 256>(p, dt, A, G2, DT, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, float *G2,
+                               float *DT, hipStream_t stream) {
+    if (p.bf16) return launch_dtype(p, static_cast<const uint16_t *>(dt), A, G2, DT, stream);
+    return launch_dtype(p, static_cast<const float *>(dt), A, G2, DT, stream);
+}
+
+}  // namespace ssd

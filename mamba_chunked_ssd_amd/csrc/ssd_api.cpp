@@ -1,0 +1,291 @@
+// ssd_api.cpp -- the C ABI of libssd (declared in include/ssd.h).
+//
+// Host side only: argument validation, workspace layout, the per-shape launch
+// plan, and the four stage launches on the caller's stream ("Accelerating
+// Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA CUDA Tile": the
+// three-kernel split of the forward pass listed at the end of section "Mamba-2
+// architecture", with the state stage split in two: the parallel per-chunk
+// contraction and the sequential carry).  Validation touches no HIP API, so
+// every error path runs without a device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+
+#include "../../include/ssd.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxI32 = std::numeric_limits<int32_t>::max();
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool chunk_supported(int64_t t) { return t == 64 || t == 128 || t == 256; }
+bool headdim_supported(int64_t p) { return p == 32 || p == 64 || p == 128; }
+bool dstate_supported(int64_t n) { return n >= 16 && n <= 256 && n % 16 == 0; }
+
+// Shape checks shared by the size query and the forward call.
+ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
+    if (s == nullptr) return SSD_ERROR_INVALID_VALUE;
+    if (s->batch < 0 || s->seqlen < 0 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
+        s->ngroups < 1 || chunk < 1)
+        return SSD_ERROR_INVALID_VALUE;
+    if (s->nheads % s->ngroups != 0) return SSD_ERROR_INVALID_VALUE;
+    if (s->dtype != SSD_DTYPE_F32 && s->dtype != SSD_DTYPE_BF16) return SSD_ERROR_INVALID_VALUE;
+    if ((s->flags & ~(uint32_t)SSD_FLAG_KEEP_INTERMEDIATES) != 0) return SSD_ERROR_INVALID_VALUE;
+    if (!chunk_supported(chunk) || !headdim_supported(s->headdim) || !dstate_supported(s->dstate))
+        return SSD_ERROR_UNSUPPORTED;
+
+    Problem q;
+    q.batch = s->batch;
+    q.seqlen = s->seqlen;
+    q.nheads = s->nheads;
+    q.headdim = s->headdim;
+    q.dstate = s->dstate;
+    q.ngroups = s->ngroups;
+    q.chunk = chunk;
+    q.nchunks = (s->seqlen + chunk - 1) / chunk;
+    q.padded_len = q.nchunks * chunk;
+    q.heads_per_group = s->nheads / s->ngroups;
+    q.bf16 = s->dtype == SSD_DTYPE_BF16;
+
+    // Every element count must fit int64; kernel-side scalar parameters fit int32.
+    int64_t t, e;
+    if (!mul_ok(q.batch, q.seqlen, &t) || !mul_ok(t, q.nheads, &e) || !mul_ok(e, q.headdim, &e))
+        return SSD_ERROR_UNSUPPORTED;
+    if (!mul_ok(t, q.ngroups, &e) || !mul_ok(e, q.dstate, &e)) return SSD_ERROR_UNSUPPORTED;
+    int64_t st;
+    if (!mul_ok(q.batch, q.nheads, &st) || !mul_ok(st, q.nchunks, &st) ||
+        !mul_ok(st, q.headdim * q.dstate, &st) || st > std::numeric_limits<int64_t>::max() / 8)
+        return SSD_ERROR_UNSUPPORTED;
+    if (q.nheads > kMaxI32 || q.nchunks > kMaxI32 || q.ngroups > kMaxI32 || q.batch > 65535)
+        return SSD_ERROR_UNSUPPORTED;
+    // Launch geometry limits (work-items per grid dimension < 2^32).
+    const int64_t tiles = q.batch * q.nchunks * q.ngroups * q.heads_per_group;  // upper bound on blocks
+    if (tiles > ((int64_t)1 << 31) / 512) return SSD_ERROR_UNSUPPORTED;
+    const int64_t k3_threads = q.batch * q.nheads * q.headdim * q.dstate / 4;
+    if (k3_threads > ((int64_t)1 << 31)) return SSD_ERROR_UNSUPPORTED;
+    if ((q.nheads + 15) / 16 > 65535) return SSD_ERROR_UNSUPPORTED;
+    *p = q;
+    return SSD_OK;
+}
+
+ssd_workspace_layout layout_for(const Problem &p, bool keep) {
+    ssd_workspace_layout l;
+    std::memset(&l, 0, sizeof(l));
+    const size_t seq = (size_t)p.batch * p.nheads * p.padded_len * sizeof(float);
+    const size_t states = (size_t)p.batch * p.nheads * p.nchunks * p.headdim * p.dstate * sizeof(float);
+    size_t off = 0;
+    l.g2 = off;
+    off = align_up(off + seq);
+    l.dt = off;
+    off = align_up(off + seq);
+    l.s = off;
+    off = align_up(off + states);
+    l.h = keep ? off : l.s;
+    if (keep) off = align_up(off + states);
+    l.total = off;
+    l.nchunks = p.nchunks;
+    l.padded_len = p.padded_len;
+    return l;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void *ptr, size_t bytes) {
+    return Range{(uintptr_t)ptr, (uintptr_t)ptr + bytes};
+}
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Pick heads-per-block for a stage whose blocks each handle one (batch, chunk,
+// group) and a run of heads: each block pays a fixed set-up cost (staging the
+// shared B / C B^T tiles, ~`setup` head-equivalents) plus one unit per head,
+// and `slots` blocks run concurrently.  Minimise the modelled makespan.
+int pick_heads_per_block(const Problem &p, int64_t slots, double setup) {
+    const int64_t base = p.batch * p.nchunks * p.ngroups;
+    const int64_t hpg = p.heads_per_group;
+    if (base == 0) return 1;
+    double best = std::numeric_limits<double>::max();
+    int best_hb = (int)hpg;
+    for (int64_t hb = 1; hb <= hpg; ++hb) {
+        const int64_t nhb = (hpg + hb - 1) / hb;
+        if (hb > 1 && (hpg + hb - 2) / (hb - 1) == nhb) continue;  // same split as hb - 1
+        const int64_t blocks = base * nhb;
+        const double rounds = (double)((blocks + slots - 1) / slots);
+        const double cost = rounds * ((double)hb + setup);
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_hb = (int)hb;
+        }
+    }
+    return best_hb;
+}
+
+const int kNumCUs = 256;
+
+}  // namespace
+
+Plan make_plan(const Problem &p) {
+    Plan plan;
+    plan.k2_heads_per_block = pick_heads_per_block(p, 2 * kNumCUs, 1.0);
+    plan.k4_heads_per_block = pick_heads_per_block(p, kNumCUs, 1.0);
+    return plan;
+}
+
+}  // namespace ssd
+
+using namespace ssd;
+
+extern "C" {
+
+size_t ssd_chunk_scan_fwd_workspace_size(const ssd_shape *shape, int64_t chunk_size) {
+    Problem p;
+    if (check_shape(shape, chunk_size, &p) != SSD_OK) return 0;
+    return layout_for(p, (shape->flags & SSD_FLAG_KEEP_INTERMEDIATES) != 0).total;
+}
+
+ssd_status ssd_chunk_scan_fwd_workspace_layout(const ssd_shape *shape, int64_t chunk_size,
+                                               ssd_workspace_layout *layout) {
+    if (layout == nullptr) return SSD_ERROR_INVALID_VALUE;
+    Problem p;
+    const ssd_status st = check_shape(shape, chunk_size, &p);
+    if (st != SSD_OK) return st;
+    *layout = layout_for(p, (shape->flags & SSD_FLAG_KEEP_INTERMEDIATES) != 0);
+    return SSD_OK;
+}
+
+static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt, const float *A,
+                          const void *B, const void *C, const float *D, int64_t chunk_size,
+                          const float *init, void *y, float *final_states, void *workspace,
+                          size_t workspace_bytes, void *stream_handle, void *const *events) {
+    Problem p;
+    const ssd_status st = check_shape(shape, chunk_size, &p);
+    if (st != SSD_OK) return st;
+    const bool keep = (shape->flags & SSD_FLAG_KEEP_INTERMEDIATES) != 0;
+    const ssd_workspace_layout lay = layout_for(p, keep);
+    const size_t esz = p.bf16 ? 2 : 4;
+
+    const size_t tok = (size_t)(p.batch * p.seqlen);
+    const size_t x_bytes = tok * p.nheads * p.headdim * esz;
+    const size_t dt_bytes = tok * p.nheads * esz;
+    const size_t bc_bytes = tok * p.ngroups * p.dstate * esz;
+    const size_t hd_bytes = (size_t)p.nheads * sizeof(float);
+    const size_t st_bytes = (size_t)p.batch * p.nheads * p.headdim * p.dstate * sizeof(float);
+    const bool has_tokens = tok > 0;
+
+    // required pointers
+    if (has_tokens && (x == nullptr || dt == nullptr || A == nullptr || B == nullptr ||
+                       C == nullptr || y == nullptr))
+        return SSD_ERROR_INVALID_VALUE;
+    if (p.batch > 0 && lay.total > 0 && workspace == nullptr) return SSD_ERROR_WORKSPACE;
+    if (workspace_bytes < lay.total) return SSD_ERROR_WORKSPACE;
+    if (events != nullptr)
+        for (int i = 0; i < 5; ++i)
+            if (events[i] == nullptr) return SSD_ERROR_INVALID_VALUE;
+
+    // alignment
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, esz) || !aligned(A, 4) || !aligned(D, 4) || !aligned(init, 16) ||
+        !aligned(final_states, 16) || !aligned(workspace, kAlign))
+        return SSD_ERROR_MISALIGNED;
+
+    // aliasing: outputs must not overlap inputs or each other; final_states may
+    // be the very same buffer as initial_states.
+    const Range ry = range_of(y, x_bytes);
+    const Range rws = range_of(workspace, lay.total);
+    const Range rfin = range_of(final_states, final_states ? st_bytes : 0);
+    const Range rinit = range_of(init, init ? st_bytes : 0);
+    const Range ins[] = {range_of(x, x_bytes), range_of(dt, dt_bytes), range_of(A, hd_bytes),
+                         range_of(B, bc_bytes), range_of(C, bc_bytes),
+                         range_of(D, D ? hd_bytes : 0), rinit};
+    for (const Range &r : ins) {
+        if (overlap(ry, r) || overlap(rws, r)) return SSD_ERROR_INVALID_VALUE;
+        if (&r != &ins[6] && overlap(rfin, r)) return SSD_ERROR_INVALID_VALUE;
+    }
+    if (overlap(rfin, rinit) && (void *)final_states != (const void *)init) return SSD_ERROR_INVALID_VALUE;
+    if (overlap(ry, rws) || overlap(ry, rfin) || overlap(rws, rfin)) return SSD_ERROR_INVALID_VALUE;
+
+    if (p.batch == 0) return SSD_OK;  // nothing to compute
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    float *G2 = reinterpret_cast<float *>(ws + lay.g2);
+    float *DTf = reinterpret_cast<float *>(ws + lay.dt);
+    float *S = reinterpret_cast<float *>(ws + lay.s);
+    float *Hs = reinterpret_cast<float *>(ws + lay.h);
+    const Plan plan = make_plan(p);
+
+    auto record = [&](int i) -> bool {
+        if (events == nullptr) return true;
+        return hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess;
+    };
+    if (!record(0)) return SSD_ERROR_LAUNCH;
+    if (p.nchunks > 0) {
+        if (launch_chunk_cumsum(p, dt, A, G2, DTf, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
+    }
+    if (!record(1)) return SSD_ERROR_LAUNCH;
+    if (p.nchunks > 0) {
+        if (launch_chunk_state(p, plan, x, B, G2, DTf, S, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
+    }
+    if (!record(2)) return SSD_ERROR_LAUNCH;
+    if (launch_state_pass(p, S, Hs, G2, init, final_states, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
+    if (!record(3)) return SSD_ERROR_LAUNCH;
+    if (p.nchunks > 0) {
+        if (launch_chunk_out(p, plan, x, B, C, G2, DTf, D, Hs, y, stream) != hipSuccess)
+            return SSD_ERROR_LAUNCH;
+    }
+    if (!record(4)) return SSD_ERROR_LAUNCH;
+    return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_fwd(const ssd_shape *shape, const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D, int64_t chunk_size,
+                              const float *initial_states, void *y, float *final_states,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    return forward(shape, x, dt, A, B, C, D, chunk_size, initial_states, y, final_states, workspace,
+                   workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape, const void *x, const void *dt,
+                                       const float *A, const void *B, const void *C, const float *D,
+                                       int64_t chunk_size, const float *initial_states, void *y,
+                                       float *final_states, void *workspace, size_t workspace_bytes,
+                                       void *stream, void *const *stage_events) {
+    if (stage_events == nullptr) return SSD_ERROR_INVALID_VALUE;
+    return forward(shape, x, dt, A, B, C, D, chunk_size, initial_states, y, final_states, workspace,
+                   workspace_bytes, stream, stage_events);
+}
+
+const char *ssd_status_string(ssd_status s) {
+    switch (s) {
+        case SSD_OK: return "ok";
+        case SSD_ERROR_INVALID_VALUE: return "invalid argument (NULL pointer, bad size, or aliasing)";
+        case SSD_ERROR_UNSUPPORTED: return "unsupported size (chunk_size 64/128/256, headdim 32/64/128, dstate 16..256 step 16)";
+        case SSD_ERROR_MISALIGNED: return "misaligned pointer (16 B for x/B/C/y/states, 256 B for workspace)";
+        case SSD_ERROR_WORKSPACE: return "workspace missing or smaller than ssd_chunk_scan_fwd_workspace_size()";
+        case SSD_ERROR_LAUNCH: return "the HIP runtime refused a kernel launch or event record";
+    }
+    return "unknown status";
+}
+
+int ssd_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// ssd_device.h -- device-side helpers shared by the libssd kernels (gfx950).
+//
+// Vector types for the MFMA operands, bf16 storage conversions (round to
+// nearest even through the hardware pack instruction), the hi/lo bf16 split
+// used for fp32-valued MFMA operands, and the MFMA wrappers.
+//
+// MFMA lane layouts used throughout (64-lane wave, l = lane, g = l / 16):
+//   v_mfma_f32_16x16x32_bf16:  A lane holds A[m = l%16][k = 8g .. 8g+7]
+//                              B lane holds B[k = 8g .. 8g+7][n = l%16]
+//   v_mfma_f32_16x16x4_f32:    A lane holds A[m = l%16][k = g]
+//                              B lane holds B[k = g][n = l%16]
+//   both:                      D lane holds D[m = 4g + r][n = l%16], r = 0..3
+// A contraction is a sum over k, so any fixed relabelling of k applied to both
+// operands gives the same product; the kernels use that freedom to feed MFMA
+// output fragments back in as A operands without a register shuffle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+// Low / high bf16 of a packed dword, widened exactly.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> one dword of two bf16 (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    floatx2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// hi = bf16(v), lo = bf16(v - hi) for two values at once; hi + lo carries
+// about 16 significant bits of v.
+struct HiLo {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ HiLo split_bf16(float a, float b) {
+    HiLo r;
+    r.hi = pack_bf16(a, b);
+    r.lo = pack_bf16(a - bf16lo(r.hi), b - bf16hi(r.hi));
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ floatx4 mfma_bf16(const u32x4 &a, const u32x4 &b, const floatx4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma_f32(float a, float b, const floatx4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace ssd

@@ -1,0 +1,73 @@
+// ssd_internal.h -- interface between the C-ABI host code (ssd_api.cpp) and
+// the four kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Problem description after validation, with the derived sizes every stage
+// needs.  All element counts are int64.
+struct Problem {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int64_t nchunks;          // ceil(seqlen / chunk)
+    int64_t padded_len;       // nchunks * chunk
+    int64_t heads_per_group;  // nheads / ngroups
+    bool bf16;                // element type of x, dt, B, C, y
+};
+
+// Launch configuration chosen on the host per problem.
+struct Plan {
+    int k2_heads_per_block;   // heads of one group sharing a staged B chunk
+    int k4_heads_per_block;   // heads of one group sharing one C B^T tile set
+};
+
+Plan make_plan(const Problem &p);
+
+// Each launcher enqueues one kernel on `stream` and returns hipSuccess or the
+// launch error.  Buffers follow the layouts documented in include/ssd.h.
+
+// Stage 1: per-chunk inclusive cumsum of log2(e) * A * dt -> G2, and dt
+// widened to fp32 -> DT; both head-major (batch, nheads, padded_len).
+hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A,
+                               float *G2, float *DT, hipStream_t stream);
+
+// Stage 2: per-chunk input state s_c = sum_t exp2(G2_last - G2_t) DT_t x_t B_t^T,
+// written as (batch, nheads, nchunks, headdim, dstate) fp32.
+hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
+                              const float *G2, const float *DT, float *S, hipStream_t stream);
+
+// Stage 3: h_0 = init (or 0); for each chunk store h_c then
+// h_{c+1} = exp2(G2_last,c) h_c + s_c; final = h_nchunks.  H may equal S.
+hipError_t launch_state_pass(const Problem &p, const float *S, float *H, const float *G2,
+                             const float *init, float *final_states, hipStream_t stream);
+
+// Stage 4: chunk output
+// y_i = exp2(G2_i) C_i h_c + sum_{j<=i} exp2(G2_i - G2_j) (C_i . B_j) DT_j x_j + D x_i.
+hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
+                            const void *C, const float *G2, const float *DT, const float *D,
+                            const float *H, void *y, hipStream_t stream);
+
+// Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
+// CU).  The template parameter is the kernel itself, so each kernel caches
+// its own "done" flag; a racing second call only repeats a harmless set.
+template <auto Kernel>
+hipError_t allow_lds(size_t bytes) {
+    static bool done = false;
+    if (done || bytes <= 65536) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Remap a hardware block index so that consecutive logical indices land on
+// the same XCD: logical = (hw % 8) * (n / 8) + hw / 8 when n % 8 == 0.
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+    if (n % 8 != 0) return hw;
+    return (hw % 8) * (n / 8) + hw / 8;
+}
+
+}  // namespace ssd

@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+read its intermediates back.  Nothing here computes the method."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mamba_chunked_ssd_amd as ssd
+
+LOG2E = 1.4426950408889634
+# spec tolerance on max |err| / rms(ref)
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def nerr(a, ref) -> float:
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if a.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(a)):
+        return float("inf")
+    rms = np.sqrt(np.mean(ref ** 2))
+    if rms == 0.0:
+        return float(np.max(np.abs(a - ref)))
+    return float(np.max(np.abs(a - ref)) / rms)
+
+
+def to_device(inp: dict, dtype: str, dev="cuda"):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            out[k] = None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+        out[k] = t.to(tdt) if k in ("x", "dt", "B", "C") else t
+    return out
+
+
+def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = True):
+    """Forward pass; returns numpy fp64 dict with y, final and (keep) G2/DT/S/H."""
+    t = to_device(inp, dtype)
+    b, L, nh, p = t["x"].shape
+    g, n = t["B"].shape[2], t["B"].shape[3]
+    ws = None
+    lay = None
+    if keep:
+        shape = ssd.make_shape(b, L, nh, p, n, g, dtype, keep=True)
+        lay = ssd.workspace_layout(shape, chunk)
+        ws = torch.empty(max(lay.total, 1), dtype=torch.uint8, device="cuda")
+    res = ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=chunk,
+                             initial_states=t["h0"], return_final_states=final, workspace=ws,
+                             keep_intermediates=keep)
+    torch.cuda.synchronize()
+    if final:
+        y, fin = res
+    else:
+        y, fin = res, None
+    out = {"y": y.double().cpu().numpy(), "final": None if fin is None else fin.double().cpu().numpy()}
+    if keep:
+        nc, Lp = lay.nchunks, lay.padded_len
+
+        def view(off, shape):
+            cnt = int(np.prod(shape))
+            return ws[off: off + 4 * cnt].view(torch.float32).reshape(shape).double().cpu().numpy()
+
+        out["G2"] = view(lay.g2, (b, nh, Lp))
+        out["DT"] = view(lay.dt, (b, nh, Lp))
+        out["S"] = view(lay.s, (b, nh, nc, p, n))
+        out["H"] = view(lay.h, (b, nh, nc, p, n))
+    return out

@@ -1,0 +1,197 @@
+"""The C ABI on the CPU: exports, workspace arithmetic and argument checks.
+
+No kernel runs here.  The argument-check tests pass fake (never dereferenced)
+device addresses to calls that validation must reject before any HIP call;
+they are skipped when a GPU is visible, so that a validation bug can never turn
+one of them into a real launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mamba_chunked_ssd_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        from mamba_chunked_ssd_amd import build
+        build.build()
+    return ssd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    assert declared_functions() == sorted(ssd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ssd_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        ssd.load_library(str(tmp_path / "libssd.so"))
+
+
+def test_status_strings(lib):
+    assert lib.ssd_status_string(0) == b"ok"
+    for code in range(1, 6):
+        assert len(lib.ssd_status_string(code)) > 10
+    assert lib.ssd_version() == 100
+
+
+def shape(**kw):
+    d = dict(batch=2, seqlen=1000, nheads=8, headdim=64, dstate=128, ngroups=2, dtype="bf16")
+    d.update(kw)
+    keep = d.pop("keep", False)
+    return ssd.make_shape(d["batch"], d["seqlen"], d["nheads"], d["headdim"], d["dstate"],
+                          d["ngroups"], d["dtype"], keep)
+
+
+def test_workspace_size_formula(lib):
+    for T in (64, 128, 256):
+        for keep in (False, True):
+            s = shape(keep=keep)
+            nc = -(-1000 // T)
+            seq = 4 * 2 * 8 * nc * T
+            st = 4 * 2 * 8 * nc * 64 * 128
+            up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+            want = up(seq) * 2 + up(st) * (2 if keep else 1)
+            assert ssd.workspace_size(s, T) == want
+            lay = ssd.workspace_layout(s, T)
+            assert lay.total == want and lay.nchunks == nc and lay.padded_len == nc * T
+            offs = [lay.g2, lay.dt, lay.s, lay.h]
+            assert all(o % 256 == 0 for o in offs)
+            assert lay.g2 == 0 and lay.dt == up(seq) and lay.s == 2 * up(seq)
+            assert (lay.h == lay.s) != keep
+
+
+@pytest.mark.parametrize("bad", [
+    dict(nheads=6, ngroups=4),       # nheads % ngroups != 0
+    dict(batch=-1), dict(seqlen=-5), dict(nheads=0), dict(ngroups=0),
+])
+def test_workspace_size_invalid_is_zero(lib, bad):
+    assert ssd.workspace_size(shape(**bad), 256) == 0
+
+
+@pytest.mark.parametrize("bad", [dict(headdim=48), dict(dstate=24), dict(dstate=272), dict(headdim=256)])
+def test_unsupported_sizes(lib, bad):
+    assert ssd.workspace_size(shape(**bad), 256) == 0
+    lay = ssd.WorkspaceLayout()
+    assert lib.ssd_chunk_scan_fwd_workspace_layout(ctypes.byref(shape(**bad)), 256, ctypes.byref(lay)) == 2
+
+
+def test_unsupported_chunk(lib):
+    for T in (0, 32, 100, 512):
+        assert ssd.workspace_size(shape(), T) == 0
+
+
+# ---------------------------------------------------------------------------
+# forward-call argument checks with fake device addresses (rejected before any
+# HIP call)
+# ---------------------------------------------------------------------------
+
+GiB = 1 << 30
+
+
+class Fake:
+    """Disjoint, 256-byte aligned fake device addresses."""
+
+    def __init__(self):
+        self.base = 1 << 44
+
+    def __call__(self, off=0):
+        self.base += 64 * GiB
+        return self.base + off
+
+
+def call(lib, s, T=256, ws_bytes=None, **over):
+    f = Fake()
+    p = dict(x=f(), dt=f(), A=f(), B=f(), C=f(), D=f(), init=None, y=f(), fin=f(), ws=f())
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = max(ssd.workspace_size(s, T), 1)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)  # noqa: E731
+    return lib.ssd_chunk_scan_fwd(ctypes.byref(s), v(p["x"]), v(p["dt"]), v(p["A"]), v(p["B"]),
+                                  v(p["C"]), v(p["D"]), T, v(p["init"]), v(p["y"]), v(p["fin"]),
+                                  v(p["ws"]), ws_bytes, None)
+
+
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(),
+    reason="fake device addresses are only passed where no GPU can be reached")
+
+
+@no_gpu
+def test_null_required_pointers(lib):
+    for k in ("x", "dt", "A", "B", "C", "y"):
+        assert call(lib, shape(), **{k: None}) == 1, k
+
+
+@no_gpu
+def test_null_shape_is_invalid(lib):
+    assert lib.ssd_chunk_scan_fwd(None, *([None] * 6), 256, None, None, None, None, 0, None) == 1
+
+
+@no_gpu
+def test_bad_shapes(lib):
+    assert call(lib, shape(nheads=6, ngroups=4)) == 1
+    assert call(lib, shape(headdim=48)) == 2
+    assert call(lib, shape(), T=100) == 2
+    assert call(lib, shape(dtype="f32"), T=256, ws_bytes=1) == 4   # workspace too small
+
+
+@no_gpu
+def test_workspace_checks(lib):
+    s = shape()
+    need = ssd.workspace_size(s, 256)
+    assert call(lib, s, ws_bytes=need - 1) == 4
+    assert call(lib, s, ws=None) == 4
+
+
+@no_gpu
+def test_misaligned_pointers(lib):
+    f = Fake()
+    for k in ("x", "B", "C", "y"):
+        assert call(lib, shape(), **{k: f() + 8}) == 3, k
+    assert call(lib, shape(), fin=f() + 4) == 3
+    assert call(lib, shape(), init=f() + 4) == 3
+    assert call(lib, shape(), ws=f() + 128) == 3
+    assert call(lib, shape(), A=f() + 2) == 3
+    assert call(lib, shape(dtype="f32"), dt=f() + 2) == 3
+
+
+@no_gpu
+def test_aliasing_rejected(lib):
+    f = Fake()
+    x = f()
+    assert call(lib, shape(), x=x, y=x) == 1                      # y over x
+    assert call(lib, shape(), x=x, y=x + 1024 * 256) == 1         # partial overlap
+    ws = f()
+    assert call(lib, shape(), ws=ws, fin=ws) == 1                 # final over workspace
+    assert call(lib, shape(), B=ws, ws=ws) == 1                   # workspace over input
+    init = f()
+    assert call(lib, shape(), init=init, fin=init + 256) == 1     # partial init/final overlap
+
+
+def test_empty_batch_is_a_noop(lib):
+    # batch == 0: nothing to compute, so no pointer is needed and nothing launches
+    s = shape(batch=0)
+    assert lib.ssd_chunk_scan_fwd(ctypes.byref(s), *([None] * 6), 256, None, None, None, None, 0, None) == 0
