@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-2 chunked SSD forward pass (libssd) on one MI355X.
+
+A step is one full ``ssd_chunk_scan_fwd`` call -- all four stages (chunk
+cumsum, chunk state, state passing, chunk output) -- over one batch of seeded
+synthetic input already resident in HBM.  The default workload is the
+Mamba-2 2.7B-shaped layer (batch 2, seqlen 2048, 80 heads, headdim 64,
+dstate 128, 1 group, chunk 256, bf16 inputs, fp32 accumulation and fp32 y).
+
+Prints ONE JSON line: tokens/s, per-stage times from HIP events recorded on
+the library's stream inside the timed region, the roofline of the dominant
+kernel, and the fp64 CPU oracle timed on this host as a reference baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/s at 1 MI355X + % of min(HBM,MFMA) roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA
+STAGES = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_out"]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes and MFMA flops per stage (what the method must move or
+# compute; intermediates fp32; C B^T once per group; triangles with diagonal)
+# ---------------------------------------------------------------------------
+def stage_model(w, y_bytes: int) -> dict:
+    e = 2 if w.dtype == "bf16" else 4
+    B, L, NH, P, N, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    NC = -(-L // T)
+    tok_h = B * L * NH
+    states = 4 * B * NH * NC * P * N
+    init = 4 * B * NH * P * N if w.init_std > 0 else 0
+    final = 4 * B * NH * P * N
+    m = {
+        "chunk_cumsum": (tok_h * (e + 4), 0.0),
+        "chunk_state": (tok_h * P * e + B * L * G * N * e + tok_h * (e + 4) + states,
+                        2.0 * B * L * NH * N * P),
+        "state_pass": (2 * states + 4 * B * NH * NC + init + final, 0.0),
+        "chunk_out": (tok_h * P * (e + y_bytes) + tok_h * (e + 4) + 2 * B * L * G * N * e + states,
+                      float(B * NC * G * T * (T + 1) * N + B * NC * NH * T * (T + 1) * P
+                            + 2 * B * L * NH * N * P)),
+    }
+    e2e_bytes = tok_h * P * (e + y_bytes) + tok_h * e + 2 * B * L * G * N * e + init + final
+    m["e2e"] = (e2e_bytes, m["chunk_state"][1] + m["chunk_out"][1])
+    return m
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs (events, device sync)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the HIP runtime)
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed (%d)" % rc)
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return float(out.value)
+
+    def destroy(self, ev: int):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def cpu_baseline(w, inp, reps: int) -> dict:
+    """The fp64 oracle, as it stands, on this host's cores (whole workload)."""
+    import oracle
+    ncores = len(os.sched_getaffinity(0))
+    oracle.scan(inp["x"][:, :64], inp["dt"][:, :64], inp["A"], inp["B"][:, :64], inp["C"][:, :64])
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+        times.append(time.perf_counter() - t0)
+    best = min(times)
+    threads = int(os.environ.get("OMP_NUM_THREADS", ncores))
+    return {
+        "value": w.tokens / best,
+        "unit": "tokens/s",
+        "cores": min(threads, ncores),
+        "kind": "oracle",
+        "sample": "whole workload (%d tokens, all heads), fp64 sequential recurrence, best of %d runs "
+                  "of %.2f s" % (w.tokens, reps, best),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mamba2_2p7b_layer_bf16")
+    ap.add_argument("--y-dtype", choices=["f32", "input"], default="f32",
+                    help="y element type: fp32 (default) or the input type")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps after a 1 GiB cache-flush write (reported separately)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy (for scaling rocprofv3 FETCH/WRITE counters)")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print("bench.py: this build measures one GPU; --gpus %d is not supported "
+              "(run with --gpus 1)" % a.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mamba_chunked_ssd_amd as ssd
+    import ssd_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py: no ROCm GPU visible", file=sys.stderr)
+        return 2
+    w = si.BY_NAME[a.workload]
+    inp = si.generate(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    ydt = torch.float32 if a.y_dtype == "f32" else tdt
+    t = {}
+    for k, v in inp.items():
+        if v is None:
+            t[k] = None
+            continue
+        x = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+        t[k] = x.to(tdt) if k in ("x", "dt", "B", "C") else x
+    y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=ydt, device=dev)
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    shape = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype,
+                           y_dtype="bf16" if ydt == torch.bfloat16 else "f32")
+    ws = torch.empty(ssd.workspace_size(shape, w.chunk_size), dtype=torch.uint8, device=dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=w.chunk_size,
+                           initial_states=t["h0"], y_dtype=ydt, out=y, final_out=fin, workspace=ws,
+                           stream=stream.cuda_stream, events=events)
+
+    if a.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps; 5 events per step around the stages
+    evs = [[hip.event() for _ in range(5)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_stage = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(4)] for e in evs])
+    for e in evs:
+        for ev in e:
+            hip.destroy(ev)
+    stage_ms = per_stage.mean(axis=0)
+    ms_per_step = elapsed * 1e3 / a.steps
+
+    model = stage_model(w, 4 if ydt == torch.float32 else (2 if w.dtype == "bf16" else 4))
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    stages = {}
+    for j, name in enumerate(STAGES):
+        byts, flops = model[name]
+        t_s = stage_ms[j] * 1e-3
+        floor = max(byts / (PEAK_HBM_GBS * 1e9), flops / (peak_tf * 1e12))
+        stages[name] = {"us": round(stage_ms[j] * 1e3, 3), "GB_s": round(byts / t_s / 1e9, 1),
+                        "TFLOP_s": round(flops / t_s / 1e12, 2),
+                        "roofline_frac": round(floor / t_s, 4)}
+    dom = STAGES[int(np.argmax(stage_ms))]
+    dj = STAGES.index(dom)
+    dbytes, dflops = model[dom]
+    t_dom = stage_ms[dj] * 1e-3
+    hbm_t = dbytes / (PEAK_HBM_GBS * 1e9)
+    mfma_t = dflops / (peak_tf * 1e12)
+    if hbm_t >= mfma_t:
+        roof = {"bound": "hbm", "achieved": round(dbytes / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(dbytes / t_dom / 1e9 / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(dflops / t_dom / 1e12, 2), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(dflops / t_dom / 1e12 / peak_tf, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    e2e_bytes, e2e_flops = model["e2e"]
+    e2e_t = ms_per_step * 1e-3
+    e2e_floor = max(e2e_bytes / (PEAK_HBM_GBS * 1e9), e2e_flops / (peak_tf * 1e12))
+    sigma_floor = sum(max(model[s][0] / (PEAK_HBM_GBS * 1e9), model[s][1] / (peak_tf * 1e12))
+                      for s in STAGES)
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.tokens / e2e_t, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_size": w.chunk_size, "accumulate": "f32",
+                   "y_dtype": "f32" if ydt == torch.float32 else w.dtype,
+                   "initial_states": w.init_std > 0, "parallelism": "single_gpu"},
+        "roofline": roof,
+        "stages": stages,
+        "e2e_roofline_frac": round(e2e_floor / e2e_t, 4),
+        "e2e_stage_sum_roofline_frac": round(sigma_floor / e2e_t, 4),
+    }
+
+    if a.cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        cold = []
+        for _ in range(min(a.steps, 20)):
+            flush.fill_(1.0)
+            e = [hip.event() for _ in range(5)]
+            step(e)
+            torch.cuda.synchronize()
+            cold.append([hip.elapsed_ms(e[j], e[j + 1]) for j in range(4)])
+            for ev in e:
+                hip.destroy(ev)
+        cold = np.array(cold).mean(axis=0)
+        out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES)}
+        out["cold_tokens_per_s"] = round(w.tokens / (cold.sum() * 1e-3), 1)
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -18,8 +18,10 @@
  * - All tensors are dense, row-major (C-contiguous) DEVICE buffers owned by the
  *   caller.  The library allocates nothing, keeps no pointer after a call
  *   returns, holds no mutable global state and is reentrant.
- * - x, dt, B, C and y have the element type `shape->dtype` (fp32 or bf16); A,
- *   D, the workspace and both state tensors are always fp32.
+ * - x, dt, B and C have the element type `shape->dtype` (fp32 or bf16); y has
+ *   `shape->y_dtype`, which is either fp32 or the input type.  A, D, the
+ *   workspace and both state tensors are always fp32.  All arithmetic is fp32
+ *   (fp64 for the running decay sum); bf16 inputs are widened exactly.
  * - Layouts (the tile layouts of the pages' kernel sections):
  *       x, y            (batch, seqlen, nheads, headdim)
  *       dt              (batch, seqlen, nheads)
@@ -71,15 +73,23 @@ typedef struct {
     int64_t headdim;  /* P: supported 32, 64, 128 */
     int64_t dstate;   /* N: supported multiples of 16 in [16, 256] */
     int64_t ngroups;  /* >= 1, divides nheads; heads share B/C contiguously */
-    int32_t dtype;    /* ssd_dtype */
+    int32_t dtype;    /* ssd_dtype of x, dt, B, C */
     uint32_t flags;   /* SSD_FLAG_* */
+    int32_t y_dtype;  /* ssd_dtype of y: SSD_DTYPE_F32 (0, the zero-initialised
+                         default) or the input dtype.  An fp32 y keeps the full
+                         fp32-accumulated result; a bf16 y adds one rounding
+                         (relative error <= 2^-9 per element). */
+    int32_t reserved; /* must be 0 */
 } ssd_shape;
 
 /* Byte offsets of the intermediates inside the workspace (each 256-byte
  * aligned).  Lp = nchunks * chunk_size, nchunks = ceil(seqlen / chunk_size).
- *   G2  fp32 (batch, nheads, Lp): log2(e) * per-chunk inclusive cumsum of A dt
- *       (the pages' G, kept in base-2 units so kernels use exp2); positions
- *       past seqlen are padded with dt = 0 and so stay flat.
+ *   G2  fp32 pair (batch, nheads, Lp) at g2_hi and g2_lo: log2(e) * the
+ *       per-chunk inclusive cumsum of A dt (the pages' G, kept in base-2 units
+ *       so kernels use exp2), summed in fp64 and stored as hi + lo floats so
+ *       that differences of nearby entries stay accurate however large the
+ *       sum grows within a chunk; positions past seqlen are padded with dt = 0
+ *       and so stay flat.
  *   DT  fp32 (batch, nheads, Lp): dt widened to fp32, head-major, zero padded.
  *   S   fp32 (batch, nheads, nchunks, headdim, dstate): after the call, the
  *       chunk-start states h_c (the state before the chunk's first token);
@@ -87,7 +97,7 @@ typedef struct {
  *       (what a chunk alone adds to a zero state).
  *   H   (only with SSD_FLAG_KEEP_INTERMEDIATES) same shape as S: h_c. */
 typedef struct {
-    size_t g2, dt, s, h, total;
+    size_t g2_hi, g2_lo, dt, s, h, total;
     int64_t nchunks, padded_len;
 } ssd_workspace_layout;
 
@@ -105,7 +115,7 @@ ssd_status ssd_chunk_scan_fwd_workspace_layout(const ssd_shape *shape, int64_t c
  *   D                fp32 (nheads), NULL => no skip term
  *   chunk_size       T: 64, 128 or 256
  *   initial_states   fp32 or NULL => zero state; may alias final_states
- *   y                output (dtype), 16-byte aligned; must not overlap any input
+ *   y                output (y_dtype), 16-byte aligned; must not overlap any input
  *   final_states     fp32 output or NULL => not written; the state after the
  *                    last token
  *   workspace        device scratch of at least

@@ -65,12 +65,15 @@ class Shape(ctypes.Structure):
         ("ngroups", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("y_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [
-        ("g2", ctypes.c_size_t),
+        ("g2_hi", ctypes.c_size_t),
+        ("g2_lo", ctypes.c_size_t),
         ("dt", ctypes.c_size_t),
         ("s", ctypes.c_size_t),
         ("h", ctypes.c_size_t),
@@ -123,15 +126,18 @@ def status_string(status: int) -> str:
         return "?"
 
 
-def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, keep=False) -> Shape:
+def _dtype_code(dtype) -> int:
     if dtype in ("bf16", SSD_DTYPE_BF16):
-        code = SSD_DTYPE_BF16
-    elif dtype in ("f32", SSD_DTYPE_F32):
-        code = SSD_DTYPE_F32
-    else:
-        raise ValueError("dtype must be 'f32' or 'bf16'")
-    return Shape(batch, seqlen, nheads, headdim, dstate, ngroups, code,
-                 SSD_FLAG_KEEP_INTERMEDIATES if keep else 0)
+        return SSD_DTYPE_BF16
+    if dtype in ("f32", SSD_DTYPE_F32):
+        return SSD_DTYPE_F32
+    raise ValueError("dtype must be 'f32' or 'bf16'")
+
+
+def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, keep=False,
+               y_dtype="f32") -> Shape:
+    return Shape(batch, seqlen, nheads, headdim, dstate, ngroups, _dtype_code(dtype),
+                 SSD_FLAG_KEEP_INTERMEDIATES if keep else 0, _dtype_code(y_dtype), 0)
 
 
 def workspace_size(shape: Shape, chunk_size: int) -> int:
@@ -171,14 +177,15 @@ def _check(t, name, dtype, shape, device):
 
 
 def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states=None,
-                   return_final_states: bool = False, *, out=None, final_out=None,
-                   workspace=None, keep_intermediates: bool = False, stream=None,
-                   events=None):
+                   return_final_states: bool = False, *, y_dtype=None, out=None,
+                   final_out=None, workspace=None, keep_intermediates: bool = False,
+                   stream=None, events=None):
     """Run ``ssd_chunk_scan_fwd`` on the current (or given) stream.
 
     x (b, L, nh, p) and dt (b, L, nh), B/C (b, L, g, n): float32 or bfloat16,
     all the same dtype; A (nh,), D (nh,) or None, initial_states
-    (b, nh, p, n) or None: float32.  Returns y, or (y, final_states).
+    (b, nh, p, n) or None: float32.  ``y_dtype`` (torch dtype): float32 (the
+    default) or the input dtype.  Returns y, or (y, final_states).
     ``workspace`` (uint8 device tensor) may be passed to reuse an allocation;
     with ``keep_intermediates`` its layout is :func:`workspace_layout` of the
     shape with the keep flag.  ``events``: 5 raw hipEvent_t handles (ints) to
@@ -208,13 +215,17 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
         _check(D, "D", torch.float32, (nh,), dev)
     if initial_states is not None:
         _check(initial_states, "initial_states", torch.float32, (b, nh, p, n), dev)
-    shape = make_shape(b, L, nh, p, n, g, dname, keep_intermediates)
+    ytype = torch.float32 if y_dtype is None else y_dtype
+    if ytype not in (torch.float32, x.dtype):
+        raise TypeError("y_dtype must be float32 or the input dtype")
+    shape = make_shape(b, L, nh, p, n, g, dname, keep_intermediates,
+                       "bf16" if ytype == torch.bfloat16 else "f32")
     need = workspace_size(shape, chunk_size)  # 0 if invalid: the call reports why
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    y = out if out is not None else torch.empty_like(x)
+    y = out if out is not None else torch.empty((b, L, nh, p), dtype=ytype, device=dev)
     if out is not None:
-        _check(out, "out", x.dtype, (b, L, nh, p), dev)
+        _check(out, "out", ytype, (b, L, nh, p), dev)
     fin = None
     if return_final_states or final_out is not None:
         fin = final_out if final_out is not None else torch.empty((b, nh, p, n), dtype=torch.float32, device=dev)

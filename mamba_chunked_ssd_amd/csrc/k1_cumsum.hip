@@ -12,8 +12,10 @@
 // input makes a per-head read strided), then each wave scans one head's chunk:
 // every lane sums T/64 consecutive tokens serially, the 64 lane totals are
 // scanned with wave shuffles, and each lane adds its exclusive prefix.  The
-// scan runs on a_t already scaled by log2(e), so rounding errors of the prefix
-// cancel in the differences G2_i - G2_j that the later stages exponentiate.
+// sum runs in fp64 and is stored as two floats, G2 = hi + lo: within a chunk
+// |G2| can reach thousands while the later stages exponentiate differences
+// G2_i - G2_j of nearby tokens, and (hi_i - hi_j) + (lo_i - lo_j) keeps those
+// differences accurate to fp32 relative precision instead of to ulp(|G2|).
 // Outputs are head-major (batch, nheads, padded_len), so each (head, chunk)
 // is one contiguous run of T floats for the later stages; dt is also written
 // there widened to fp32.  Tokens past seqlen are treated as dt = 0: G2 stays
@@ -36,8 +38,9 @@ __device__ __forceinline__ float load_dt<uint16_t>(const uint16_t *p) { return b
 template <typename Tin, int T>
 __global__ __launch_bounds__(256) void k1_cumsum(const Tin *__restrict__ dt,
                                                  const float *__restrict__ A,
-                                                 float *__restrict__ G2, float *__restrict__ DT,
-                                                 int64_t seqlen, int nheads, int64_t Lp) {
+                                                 float *__restrict__ G2hi, float *__restrict__ G2lo,
+                                                 float *__restrict__ DT, int64_t seqlen, int nheads,
+                                                 int64_t Lp) {
     constexpr int E = T / 64;  // tokens per lane
     __shared__ float s_dt[kHeadTile][T + 1];
 
@@ -61,45 +64,48 @@ __global__ __launch_bounds__(256) void k1_cumsum(const Tin *__restrict__ dt,
     for (int j = wave; j < kHeadTile; j += 4) {
         const int h = h0 + j;
         if (h >= nheads) break;  // wave-uniform
-        const float a2 = A[h] * kLog2e;
-        float d[E], run[E];
-        float tot = 0.f;
+        const double a2 = (double)A[h] * 1.4426950408889634;  // log2(e)
+        float d[E];
+        double run[E];
+        double tot = 0.0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             d[e] = s_dt[j][lane * E + e];
-            tot += a2 * d[e];
+            tot += a2 * (double)d[e];
             run[e] = tot;
         }
         // Inclusive scan of the lane totals across the wave.
-        float inc = tot;
+        double inc = tot;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float up = __shfl_up(inc, off, 64);
+            const double up = __shfl_up(inc, off, 64);
             if (lane >= off) inc += up;
         }
-        const float excl = inc - tot;
-        float *g = G2 + (b * nheads + h) * Lp + (int64_t)c * T + lane * E;
-        float *o = DT + (b * nheads + h) * Lp + (int64_t)c * T + lane * E;
+        const double excl = inc - tot;
+        const int64_t base = (b * nheads + h) * Lp + (int64_t)c * T + lane * E;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            g[e] = excl + run[e];
-            o[e] = d[e];
+            const double g = excl + run[e];
+            const float hi = (float)g;
+            G2hi[base + e] = hi;
+            G2lo[base + e] = (float)(g - (double)hi);
+            DT[base + e] = d[e];
         }
     }
 }
 
 template <typename Tin, int T>
-hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, float *G2, float *DT,
+hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
                     hipStream_t stream) {
     dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadTile - 1) / kHeadTile),
               (unsigned)p.batch);
-    hipLaunchKernelGGL((k1_cumsum<Tin, T>), grid, dim3(256), 0, stream, dt, A, G2, DT, p.seqlen,
-                       (int)p.nheads, p.padded_len);
+    hipLaunchKernelGGL((k1_cumsum<Tin, T>), grid, dim3(256), 0, stream, dt, A, G2.hi, G2.lo, DT,
+                       p.seqlen, (int)p.nheads, p.padded_len);
     return hipGetLastError();
 }
 
 template <typename Tin>
-hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, float *G2, float *DT,
+hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
                         hipStream_t stream) {
     switch (p.chunk) {
         case 64: return launch_t<Tin, 64>(p, dt, A, G2, DT, stream);
@@ -111,7 +117,7 @@ hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, float *
 
 }  // namespace
 
-hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, float *G2,
+hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
                                float *DT, hipStream_t stream) {
     if (p.bf16) return launch_dtype(p, static_cast<const uint16_t *>(dt), A, G2, DT, stream);
     return launch_dtype(p, static_cast<const float *>(dt), A, G2, DT, stream);

@@ -70,8 +70,9 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 template <int T, int P>
 __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const float *__restrict__ G2, const float *__restrict__ DT, float *__restrict__ S,
-    int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
+    const float *__restrict__ G2hi, const float *__restrict__ G2lo, const float *__restrict__ DT,
+    float *__restrict__ S, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
+    int nhb) {
     constexpr int KS = T / 32;   // k-steps of the contraction over tokens
     constexpr int PT = P / 16;   // 16-row tiles of headdim
     constexpr int TO = T / 8;    // token octets
@@ -153,27 +154,26 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
                 rows[r] = *reinterpret_cast<const u32x4 *>(x + ((b * L + tok) * NH + h) * P + po * 8);
         }
     };
-    // Scale by w_t = exp2(G2_last - G2_t) dt_t, split into hi/lo bf16 and
+    // Scale by w_t = exp2(G2_last - G2_t) dt_t (G2 differences formed from the
+    // hi/lo pair), split into hi/lo bf16 and
     // write the unit transposed into xhi / xlo.
     auto store_x = [&](int h, const u32x4 (&rows)[8]) {
         if (!has_unit) return;
-        const float *g2 = G2 + ((int64_t)b * NH + h) * Lp + t0;
-        const float *dd = DT + ((int64_t)b * NH + h) * Lp + t0;
-        const float glast = g2[T - 1];
+        const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
+        const float *gh = G2hi + hoff;
+        const float *gl = G2lo + hoff;
+        const float *dd = DT + hoff;
+        const float lh = gh[T - 1], ll = gl[T - 1];
         float wt[8];
-        {
-            const float4 ga = *reinterpret_cast<const float4 *>(g2 + to * 8);
-            const float4 gb = *reinterpret_cast<const float4 *>(g2 + to * 8 + 4);
-            const float4 da = *reinterpret_cast<const float4 *>(dd + to * 8);
-            const float4 db = *reinterpret_cast<const float4 *>(dd + to * 8 + 4);
-            wt[0] = fast_exp2(glast - ga.x) * da.x;
-            wt[1] = fast_exp2(glast - ga.y) * da.y;
-            wt[2] = fast_exp2(glast - ga.z) * da.z;
-            wt[3] = fast_exp2(glast - ga.w) * da.w;
-            wt[4] = fast_exp2(glast - gb.x) * db.x;
-            wt[5] = fast_exp2(glast - gb.y) * db.y;
-            wt[6] = fast_exp2(glast - gb.z) * db.z;
-            wt[7] = fast_exp2(glast - gb.w) * db.w;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float4 a = *reinterpret_cast<const float4 *>(gh + to * 8 + 4 * q);
+            const float4 l = *reinterpret_cast<const float4 *>(gl + to * 8 + 4 * q);
+            const float4 d = *reinterpret_cast<const float4 *>(dd + to * 8 + 4 * q);
+            wt[4 * q + 0] = fast_exp2((lh - a.x) + (ll - l.x)) * d.x;
+            wt[4 * q + 1] = fast_exp2((lh - a.y) + (ll - l.y)) * d.y;
+            wt[4 * q + 2] = fast_exp2((lh - a.z) + (ll - l.z)) * d.z;
+            wt[4 * q + 3] = fast_exp2((lh - a.w) + (ll - l.w)) * d.w;
         }
         u32x4 hi[8], lo[8];
 #pragma unroll
@@ -249,9 +249,9 @@ constexpr int kSlab = 64;  // tokens of w*x staged in LDS at a time
 
 template <int T, int P>
 __global__ __launch_bounds__(512) void k2_chunk_state_f32(
-    const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ G2,
-    const float *__restrict__ DT, float *__restrict__ S, int64_t L, int NH, int N, int G, int NC,
-    int64_t Lp, int HPG, int HB, int nhb) {
+    const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ G2hi,
+    const float *__restrict__ G2lo, const float *__restrict__ DT, float *__restrict__ S, int64_t L,
+    int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
     constexpr int KS = T / 4;        // k-steps (4 tokens each) over the chunk
     constexpr int PT = P / 16;
     constexpr int LDP = P + 16;      // padded LDS row (floats)
@@ -285,9 +285,11 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
         }
 
     for (int h = h_begin; h < h_end; ++h) {
-        const float *g2 = G2 + ((int64_t)b * NH + h) * Lp + t0;
-        const float *dd = DT + ((int64_t)b * NH + h) * Lp + t0;
-        const float glast = g2[T - 1];
+        const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
+        const float *gh = G2hi + hoff;
+        const float *gl = G2lo + hoff;
+        const float *dd = DT + hoff;
+        const float lh = gh[T - 1], ll = gl[T - 1];
         int tid_o = tid;  // opaque lane coordinates, as in the bf16 kernel
         asm volatile("" : "+v"(tid_o));
         const int l16 = tid_o & 15, g4 = (tid_o >> 4) & 3;
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
                 float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (t0 + t < L) {
                     xv = *reinterpret_cast<const float4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
-                    const float wt = fast_exp2(glast - g2[t]) * dd[t];
+                    const float wt = fast_exp2((lh - gh[t]) + (ll - gl[t])) * dd[t];
                     xv.x *= wt; xv.y *= wt; xv.z *= wt; xv.w *= wt;
                 }
                 *reinterpret_cast<float4 *>(&xs[tt * LDP + 4 * p4]) = xv;
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
 
 template <int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B,
-                     const float *G2, const float *DT, float *S, hipStream_t stream) {
+                     G2View G2, const float *DT, float *S, hipStream_t stream) {
     const int HB = plan.k2_heads_per_block;
     const int nhb = (int)((p.heads_per_group + HB - 1) / HB);
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
@@ -344,18 +346,21 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
     if (p.bf16) {
         // one 8x8 (token, headdim) unit of the x tile per thread
         const int waves = (int)std::max<int64_t>((p.dstate + 31) / 32, (T / 8) * (P / 8) / 64);
-        const size_t lds = (size_t)2 * P * T * 2;
+        constexpr size_t lds = (size_t)2 * P * T * 2;
+        static_assert(lds <= 160 * 1024, "stage-2 LDS budget exceeded");
         if (allow_lds<k2_chunk_state_bf16<T, P>>(lds) != hipSuccess) return hipErrorInvalidValue;
         hipLaunchKernelGGL((k2_chunk_state_bf16<T, P>), dim3((unsigned)blocks), dim3(64 * waves),
                            lds, stream, static_cast<const uint16_t *>(x),
-                           static_cast<const uint16_t *>(B), G2, DT, S, p.seqlen, (int)p.nheads,
+                           static_cast<const uint16_t *>(B), G2.hi, G2.lo, DT, S, p.seqlen,
+                           (int)p.nheads,
                            (int)p.dstate, (int)p.ngroups, (int)p.nchunks, p.padded_len,
                            (int)p.heads_per_group, HB, nhb);
     } else {
         const int waves = (int)((p.dstate + 31) / 32);
         hipLaunchKernelGGL((k2_chunk_state_f32<T, P>), dim3((unsigned)blocks), dim3(64 * waves), 0,
                            stream, static_cast<const float *>(x), static_cast<const float *>(B),
-                           G2, DT, S, p.seqlen, (int)p.nheads, (int)p.dstate, (int)p.ngroups,
+                           G2.hi, G2.lo, DT, S, p.seqlen, (int)p.nheads, (int)p.dstate,
+                           (int)p.ngroups,
                            (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB, nhb);
     }
     return hipGetLastError();
@@ -363,7 +368,7 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
 
 template <int T>
 hipError_t launch_t(const Problem &p, const Plan &plan, const void *x, const void *B,
-                    const float *G2, const float *DT, float *S, hipStream_t stream) {
+                    G2View G2, const float *DT, float *S, hipStream_t stream) {
     switch (p.headdim) {
         case 32: return launch_tp<T, 32>(p, plan, x, B, G2, DT, S, stream);
         case 64: return launch_tp<T, 64>(p, plan, x, B, G2, DT, S, stream);
@@ -375,7 +380,7 @@ hipError_t launch_t(const Problem &p, const Plan &plan, const void *x, const voi
 }  // namespace
 
 hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
-                              const float *G2, const float *DT, float *S, hipStream_t stream) {
+                              G2View G2, const float *DT, float *S, hipStream_t stream) {
     switch (p.chunk) {
         case 64: return launch_t<64>(p, plan, x, B, G2, DT, S, stream);
         case 128: return launch_t<128>(p, plan, x, B, G2, DT, S, stream);

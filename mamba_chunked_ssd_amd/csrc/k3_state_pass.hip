@@ -25,7 +25,8 @@ namespace {
 constexpr int kDepth = 8;
 
 __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
-                                                     const float *__restrict__ G2,
+                                                     const float *__restrict__ G2hi,
+                                                     const float *__restrict__ G2lo,
                                                      const float *init, float *final_states,
                                                      int64_t n_vec, int64_t pn_vec,
                                                      int64_t nchunks, int64_t Lp, int T) {
@@ -38,7 +39,8 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
 
     float4 h = make_float4(0.f, 0.f, 0.f, 0.f);
     if (init != nullptr) h = reinterpret_cast<const float4 *>(init)[bh * pn_vec + e];
-    const float *g2 = G2 + bh * Lp + (T - 1);
+    const float *g2h = G2hi + bh * Lp + (T - 1);
+    const float *g2l = G2lo + bh * Lp + (T - 1);
 
     for (int64_t c0 = 0; c0 < nchunks; c0 += kDepth) {
         float4 s[kDepth];
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
         for (int k = 0; k < kDepth; ++k) {
             if (c0 + k < nchunks) {
                 s[k] = Sv[((bh * nchunks) + c0 + k) * pn_vec + e];
-                dec[k] = g2[(c0 + k) * T];
+                dec[k] = g2h[(c0 + k) * T] + g2l[(c0 + k) * T];
             }
         }
 #pragma unroll
@@ -67,14 +69,15 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
 
 }  // namespace
 
-hipError_t launch_state_pass(const Problem &p, const float *S, float *H, const float *G2,
+hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View G2,
                              const float *init, float *final_states, hipStream_t stream) {
     const int64_t pn_vec = p.headdim * p.dstate / 4;
     const int64_t n_vec = p.batch * p.nheads * pn_vec;
     if (n_vec == 0) return hipSuccess;
     const int64_t blocks = (n_vec + 255) / 256;
-    hipLaunchKernelGGL(k3_state_pass, dim3((unsigned)blocks), dim3(256), 0, stream, S, H, G2, init,
-                       final_states, n_vec, pn_vec, p.nchunks, p.padded_len, (int)p.chunk);
+    hipLaunchKernelGGL(k3_state_pass, dim3((unsigned)blocks), dim3(256), 0, stream, S, H, G2.hi,
+                       G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
+                       (int)p.chunk);
     return hipGetLastError();
 }
 

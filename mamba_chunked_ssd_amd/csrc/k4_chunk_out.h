@@ -1,4 +1,5 @@
-// k4_chunk_out.hip -- stage 4: the chunk output, fused.
+// k4_chunk_out.h -- stage 4: the chunk output, fused (kernel templates; the
+// k4_*.hip translation units instantiate them per input/output type).
 //
 // "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
 // CUDA Tile", section "Mamba-2 architecture", chunk output with decay
@@ -35,50 +36,85 @@
 // and the second factor (times dt_j) is tabulated once per head and token, so
 // a lane needs one exp2 per tile instead of four.  The next head's x, h_c and
 // decay data are loaded into registers while the current head computes.
+#pragma once
+
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
 namespace ssd {
-namespace {
+namespace k4 {
 
 // Wave w owns row tiles I0 = w and I1 = T/16 - 1 - w.  Its S slots are laid
 // out as [I0: J = 0..I0][pad to even][I1: J = 0..I1][pad to even]; the total
 // is always T/16 + 2 and a pair (2q, 2q + 1) never straddles the two tiles.
 __device__ __forceinline__ int slot_base1(int I0) { return (I0 + 2) & ~1; }
 
+// Per-head decay tables (T floats each, in LDS) for the tokens of the chunk:
+//   gh[t] + gl[t] = G2_t (the hi/lo pair),  dts[t] = dt_t,
+//   cfs[t] = exp2(G2_e(t) - G2_t) dt_t with e(t) the last token of t's 16-tile.
+// Every exponent below is a difference formed as (hi_i - hi_j) + (lo_i - lo_j).
+struct Tables {
+    float *gh, *gl, *cfs, *dts;
+};
+
+__device__ __forceinline__ void head_tables(const Tables &tb, int t, float gh, float gl, float geh,
+                                            float gel, float d) {
+    tb.gh[t] = gh;
+    tb.gl[t] = gl;
+    tb.cfs[t] = fast_exp2((geh - gh) + (gel - gl)) * d;
+    tb.dts[t] = d;
+}
+
 // Decay-and-dt weighted values of one S tile slot for this lane: row
-// i = 16 I + l16, columns j = 16 J + 4 g4 + r.  Tables (per head, in LDS):
-//   g2s[t] = G2_t,  cfs[t] = exp2(G2_e(t) - G2_t) dt_t,  lgs[t] = G2_t - log2(dt_t).
-__device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, float g2i,
-                                            const float *g2s, const float *cfs,
-                                            const float *lgs, int l16, int g4, float (&v)[4]) {
+// i = 16 I + l16 (G2_i = gih + gil), columns j = 16 J + 4 g4 + r.  On the
+// diagonal tile the exponent is the exact difference G2_i - G2_j (0 for j = i)
+// and the mask is a select taken before exp2; off the diagonal both factors of
+// exp2(G2_i - G2_e) exp2(G2_e - G2_j) have exponents <= 0.
+__device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, float gih, float gil,
+                                            const Tables &tb, int l16, int g4, float (&v)[4]) {
     if (J > I) {
         v[0] = v[1] = v[2] = v[3] = 0.f;
     } else if (J < I) {
-        const float rf = fast_exp2(g2i - g2s[16 * J + 15]);
-        const float4 cf = *reinterpret_cast<const float4 *>(cfs + 16 * J + 4 * g4);
+        const int e = 16 * J + 15;
+        const float rf = fast_exp2((gih - tb.gh[e]) + (gil - tb.gl[e]));
+        const float4 cf = *reinterpret_cast<const float4 *>(tb.cfs + 16 * J + 4 * g4);
         v[0] = s[0] * (rf * cf.x);
         v[1] = s[1] * (rf * cf.y);
         v[2] = s[2] * (rf * cf.z);
         v[3] = s[3] * (rf * cf.w);
     } else {
-        const float4 lg = *reinterpret_cast<const float4 *>(lgs + 16 * J + 4 * g4);
-        const float lgv[4] = {lg.x, lg.y, lg.z, lg.w};
+        const float4 jh = *reinterpret_cast<const float4 *>(tb.gh + 16 * J + 4 * g4);
+        const float4 jl = *reinterpret_cast<const float4 *>(tb.gl + 16 * J + 4 * g4);
+        const float4 dj = *reinterpret_cast<const float4 *>(tb.dts + 16 * J + 4 * g4);
+        const float hv[4] = {jh.x, jh.y, jh.z, jh.w};
+        const float lv[4] = {jl.x, jl.y, jl.z, jl.w};
+        const float dv[4] = {dj.x, dj.y, dj.z, dj.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const bool keep = (4 * g4 + r) <= l16;  // j <= i (diagonal kept)
-            const float arg = keep ? (g2i - lgv[r]) : -INFINITY;
-            v[r] = keep ? s[r] * fast_exp2(arg) : 0.f;
+            const float arg = keep ? ((gih - hv[r]) + (gil - lv[r])) : -INFINITY;
+            v[r] = keep ? s[r] * (fast_exp2(arg) * dv[r]) : 0.f;
         }
     }
 }
 
-// Fill the per-head decay tables for token t of the chunk.
-__device__ __forceinline__ void head_tables(float g, float ge, float d, int t, float *g2s,
-                                            float *cfs, float *lgs) {
-    g2s[t] = g;
-    cfs[t] = fast_exp2(ge - g) * d;
-    lgs[t] = g - __builtin_amdgcn_logf(d);  // d == 0 -> +inf -> weight 0
+// exp2(G2) of the four accumulator rows 16 I + 4 g4 + r
+__device__ __forceinline__ void row_decay(const Tables &tb, int I, int g4, float (&e)[4]) {
+    const float4 h = *reinterpret_cast<const float4 *>(tb.gh + 16 * I + 4 * g4);
+    const float4 l = *reinterpret_cast<const float4 *>(tb.gl + 16 * I + 4 * g4);
+    e[0] = fast_exp2(h.x + l.x);
+    e[1] = fast_exp2(h.y + l.y);
+    e[2] = fast_exp2(h.z + l.z);
+    e[3] = fast_exp2(h.w + l.w);
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_out(OutT *p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
+    *p = (uint16_t)(pack_bf16(v, 0.f) & 0xffffu);
 }
 
 // ---------------------------------------------------------------------------
@@ -99,11 +135,28 @@ __device__ __forceinline__ int h_off(int row, int chunk) {  // chunk = n / 8
 
 __device__ __forceinline__ uint32_t sel_half(int q) { return (q & 1) ? 0x07060302u : 0x05040100u; }
 
+// gfx950 LDS per CU (and the most one block may use)
+constexpr size_t kLdsBytes = 160 * 1024;
+
+// LDS of the bf16 kernel: x^T tile, the h hi/lo tiles when they fit, decay tables.
 template <int T, int P, int NKMAX>
+struct Bf16Lds {
+    static constexpr size_t x = (size_t)P * T * 2;
+    static constexpr size_t h = (size_t)2 * P * (NKMAX * 32) * 2;
+    static constexpr size_t tables = (size_t)4 * T * 4;
+    // h is staged in LDS when everything fits; otherwise its fragments are read
+    // from global memory (L2) and split into hi/lo in registers.
+    static constexpr bool h_in_lds = x + h + tables <= kLdsBytes;
+    static constexpr size_t total = x + (h_in_lds ? h : 0) + tables;
+    static_assert(total <= kLdsBytes, "stage-4 LDS budget exceeded");
+};
+
+template <int T, int P, int NKMAX, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const uint16_t *__restrict__ Cm, const float *__restrict__ G2, const float *__restrict__ DT,
-    const float *__restrict__ Dv, const float *__restrict__ H, uint16_t *__restrict__ y,
+    const uint16_t *__restrict__ Cm, const float *__restrict__ G2hi, const float *__restrict__ G2lo,
+    const float *__restrict__ DT, const float *__restrict__ Dv, const float *__restrict__ H,
+    OutT *__restrict__ y,
     int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
     constexpr int NT16 = T / 16;
     constexpr int NSLOT = NT16 + 2;
@@ -116,14 +169,16 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     constexpr int HCH = NPAD / 8;                     // 8-element chunks per h row
     constexpr int HUNITS = P * HCH;
     constexpr int HPASS = (HUNITS + NTHR - 1) / NTHR;
+    constexpr int HREG = Bf16Lds<T, P, NKMAX>::h_in_lds ? HPASS : 1;
 
+    using Lds = Bf16Lds<T, P, NKMAX>;
+    constexpr bool kHinLds = Lds::h_in_lds;
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char *xt = lds;                          // [P][T] bf16
-    unsigned char *hhi = xt + P * T * 2;              // [P][NPAD] bf16
-    unsigned char *hlo = hhi + P * NPAD * 2;          // [P][NPAD] bf16
-    float *g2s = reinterpret_cast<float *>(hlo + P * NPAD * 2);
-    float *cfs = g2s + T;
-    float *lgs = cfs + T;
+    unsigned char *hhi = xt + Lds::x;                 // [P][NPAD] bf16 (if kHinLds)
+    unsigned char *hlo = hhi + Lds::h / 2;            // [P][NPAD] bf16 (if kHinLds)
+    float *tbase = reinterpret_cast<float *>(xt + Lds::x + (kHinLds ? Lds::h : 0));
+    const Tables tb{tbase, tbase + T, tbase + 2 * T, tbase + 3 * T};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -146,8 +201,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
 
     // ---------------- per-head data, loaded one head ahead ----------------
     u32x4 xr[XPASS][4];   // unit: 4 tokens x 8 headdim columns
-    floatx4 hr[HPASS][2]; // unit: 8 consecutive fp32 of one h row
-    float sg = 0.f, sge = 0.f, sdt = 0.f;
+    floatx4 hr[HREG][2];  // unit: 8 consecutive fp32 of one h row
+    float sgh = 0.f, sgl = 0.f, seh = 0.f, sel = 0.f, sdt = 0.f;
     auto load_head = [&](int h) {
 #pragma unroll
         for (int ps = 0; ps < XPASS; ++ps) {
@@ -162,21 +217,25 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
             }
         }
         const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
+        if constexpr (kHinLds) {
 #pragma unroll
-        for (int ps = 0; ps < HPASS; ++ps) {
-            const int u = tid + ps * NTHR;
-            const int ch = u % HCH, p = u / HCH;
-            hr[ps][0] = hr[ps][1] = zero4();
-            if (u < HUNITS && 8 * ch < N) {
-                hr[ps][0] = *reinterpret_cast<const floatx4 *>(hp + p * N + 8 * ch);
-                hr[ps][1] = *reinterpret_cast<const floatx4 *>(hp + p * N + 8 * ch + 4);
+            for (int ps = 0; ps < HPASS; ++ps) {
+                const int u = tid + ps * NTHR;
+                const int ch = u % HCH, p = u / HCH;
+                hr[ps][0] = hr[ps][1] = zero4();
+                if (u < HUNITS && 8 * ch < N) {
+                    hr[ps][0] = *reinterpret_cast<const floatx4 *>(hp + p * N + 8 * ch);
+                    hr[ps][1] = *reinterpret_cast<const floatx4 *>(hp + p * N + 8 * ch + 4);
+                }
             }
         }
         if (tid < T) {
-            const float *g2p = G2 + ((int64_t)b * NH + h) * Lp + t0;
-            sg = g2p[tid];
-            sge = g2p[tid | 15];
-            sdt = DT[((int64_t)b * NH + h) * Lp + t0 + tid];
+            const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
+            sgh = G2hi[hoff + tid];
+            sgl = G2lo[hoff + tid];
+            seh = G2hi[hoff + (tid | 15)];
+            sel = G2lo[hoff + (tid | 15)];
+            sdt = DT[hoff + tid];
         }
     };
     auto stage_head = [&]() {
@@ -197,7 +256,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
 #pragma unroll
         for (int ps = 0; ps < HPASS; ++ps) {
             const int u = tid + ps * NTHR;
-            if (u < HUNITS) {
+            if (kHinLds && u < HUNITS) {
                 const int ch = u % HCH, p = u / HCH;
                 u32x4 hi, lo;
                 { const HiLo s2 = split_bf16(hr[ps][0][0], hr[ps][0][1]); hi[0] = s2.hi; lo[0] = s2.lo; }
@@ -208,7 +267,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                 *reinterpret_cast<u32x4 *>(hlo + h_off<NPAD>(p, ch)) = lo;
             }
         }
-        if (tid < T) head_tables(sg, sge, sdt, tid, g2s, cfs, lgs);
+        if (tid < T) head_tables(tb, tid, sgh, sgl, seh, sel, sdt);
     };
 
     if (h_begin < h_end) load_head(h_begin);
@@ -274,14 +333,31 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
 
         // inter-chunk term C_i h_c (h split into hi + lo)
+        const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
 #pragma unroll
         for (int ks = 0; ks < NKMAX; ++ks) {
             if (ks >= nk) continue;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const int off = h_off<NPAD>(16 * pt + l16, 4 * ks + g4);
-                const u32x4 hh = *reinterpret_cast<const u32x4 *>(hhi + off);
-                const u32x4 hl = *reinterpret_cast<const u32x4 *>(hlo + off);
+                u32x4 hh, hl;
+                if constexpr (kHinLds) {
+                    const int off = h_off<NPAD>(16 * pt + l16, 4 * ks + g4);
+                    hh = *reinterpret_cast<const u32x4 *>(hhi + off);
+                    hl = *reinterpret_cast<const u32x4 *>(hlo + off);
+                } else {
+                    // lane reads h[p][32 ks + 8 g4 .. +7]; columns past dstate are 0
+                    floatx4 v0 = zero4(), v1 = zero4();
+                    const int n0 = 32 * ks + 8 * g4;
+                    if (n0 < N) {
+                        const float *src = hp + (16 * pt + l16) * N + n0;
+                        v0 = *reinterpret_cast<const floatx4 *>(src);
+                        v1 = *reinterpret_cast<const floatx4 *>(src + 4);
+                    }
+                    const HiLo a = split_bf16(v0[0], v0[1]), bq = split_bf16(v0[2], v0[3]);
+                    const HiLo cq = split_bf16(v1[0], v1[1]), dq = split_bf16(v1[2], v1[3]);
+                    hh = u32x4{a.hi, bq.hi, cq.hi, dq.hi};
+                    hl = u32x4{a.lo, bq.lo, cq.lo, dq.lo};
+                }
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
                     acc[ii][pt] = mfma_bf16(cfr[ii][ks], hh, acc[ii][pt]);
@@ -292,8 +368,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         // rows i = 16 I + 4 g4 + r take exp2(G2_i)
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            const float4 gv = *reinterpret_cast<const float4 *>(g2s + 16 * (ii ? I1 : I0) + 4 * g4);
-            const float e[4] = {fast_exp2(gv.x), fast_exp2(gv.y), fast_exp2(gv.z), fast_exp2(gv.w)};
+            float e[4];
+            row_decay(tb, ii ? I1 : I0, g4, e);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -304,15 +380,15 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         for (int ii = 0; ii < 2; ++ii) {
             const int I = ii ? I1 : I0;
             const int kb = ii ? base1 : 0, kend = ii ? NSLOT : base1;
-            const float g2i = g2s[16 * I + l16];
+            const float gih = tb.gh[16 * I + l16], gil = tb.gl[16 * I + l16];
 #pragma unroll
             for (int q = 0; q < NSLOT / 2; ++q) {
                 const int k0 = 2 * q;
                 if (k0 < kb || k0 >= kend) continue;  // wave-uniform
                 const int Ja = k0 - kb, Jb = Ja + 1;
                 float va[4], vb[4];
-                tile_values(S[k0], Ja, I, g2i, g2s, cfs, lgs, l16, g4, va);
-                tile_values(S[k0 + 1], Jb, I, g2i, g2s, cfs, lgs, l16, g4, vb);
+                tile_values(S[k0], Ja, I, gih, gil, tb, l16, g4, va);
+                tile_values(S[k0 + 1], Jb, I, gih, gil, tb, l16, g4, vb);
                 u32x4 ahi, alo;
                 { const HiLo s2 = split_bf16(va[0], va[1]); ahi[0] = s2.hi; alo[0] = s2.lo; }
                 { const HiLo s2 = split_bf16(va[2], va[3]); ahi[1] = s2.hi; alo[1] = s2.lo; }
@@ -343,8 +419,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                 for (int r = 0; r < 4; ++r) {
                     const int64_t row = t0 + 16 * I + 4 * g4 + r;
                     if (row < L) {
-                        const float o = acc[ii][pt][r] + Dh * xv[r];
-                        y[((b * L + row) * NH + h) * P + p] = (uint16_t)(pack_bf16(o, 0.f) & 0xffffu);
+                        store_out(&y[((b * L + row) * NH + h) * P + p], acc[ii][pt][r] + Dh * xv[r]);
                     }
                 }
             }
@@ -356,11 +431,12 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
 // ---------------------------------------------------------------------------
 // fp32 path
 // ---------------------------------------------------------------------------
-template <int T, int P>
+template <int T, int P, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ Cm,
-    const float *__restrict__ G2, const float *__restrict__ DT, const float *__restrict__ Dv,
-    const float *__restrict__ H, float *__restrict__ y, int64_t L, int NH, int N, int G, int NC,
+    const float *__restrict__ G2hi, const float *__restrict__ G2lo, const float *__restrict__ DT,
+    const float *__restrict__ Dv, const float *__restrict__ H, OutT *__restrict__ y, int64_t L,
+    int NH, int N, int G, int NC,
     int64_t Lp, int HPG, int HB, int nhb) {
     constexpr int NT16 = T / 16;
     constexpr int NSLOT = NT16 + 2;
@@ -372,9 +448,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 
     extern __shared__ __align__(16) unsigned char lds[];
     float *xs = reinterpret_cast<float *>(lds);       // [T][LDP]
-    float *g2s = xs + T * LDP;
-    float *cfs = g2s + T;
-    float *lgs = cfs + T;
+    const Tables tb{xs + T * LDP, xs + T * LDP + T, xs + T * LDP + 2 * T, xs + T * LDP + 3 * T};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -398,7 +472,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     const float *crow[2] = {Cm + ((b * L + rowC[0]) * G + gi) * N, Cm + ((b * L + rowC[1]) * G + gi) * N};
 
     floatx4 xr[XPASS];
-    float sg = 0.f, sge = 0.f, sdt = 0.f;
+    float sgh = 0.f, sgl = 0.f, seh = 0.f, sel = 0.f, sdt = 0.f;
     auto load_head = [&](int h) {
 #pragma unroll
         for (int ps = 0; ps < XPASS; ++ps) {
@@ -409,10 +483,12 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 xr[ps] = *reinterpret_cast<const floatx4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
         }
         if (tid < T) {
-            const float *g2p = G2 + ((int64_t)b * NH + h) * Lp + t0;
-            sg = g2p[tid];
-            sge = g2p[tid | 15];
-            sdt = DT[((int64_t)b * NH + h) * Lp + t0 + tid];
+            const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
+            sgh = G2hi[hoff + tid];
+            sgl = G2lo[hoff + tid];
+            seh = G2hi[hoff + (tid | 15)];
+            sel = G2lo[hoff + (tid | 15)];
+            sdt = DT[hoff + tid];
         }
     };
     auto stage_head = [&]() {
@@ -424,7 +500,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 *reinterpret_cast<floatx4 *>(xs + t * LDP + 4 * p4) = xr[ps];
             }
         }
-        if (tid < T) head_tables(sg, sge, sdt, tid, g2s, cfs, lgs);
+        if (tid < T) head_tables(tb, tid, sgh, sgl, seh, sel, sdt);
     };
 
     if (h_begin < h_end) load_head(h_begin);
@@ -492,8 +568,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
         }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            const float4 gv = *reinterpret_cast<const float4 *>(g2s + 16 * (ii ? I1 : I0) + 4 * g4);
-            const float e[4] = {fast_exp2(gv.x), fast_exp2(gv.y), fast_exp2(gv.z), fast_exp2(gv.w)};
+            float e[4];
+            row_decay(tb, ii ? I1 : I0, g4, e);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -504,13 +580,13 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
         for (int ii = 0; ii < 2; ++ii) {
             const int I = ii ? I1 : I0;
             const int kb = ii ? base1 : 0, kend = ii ? NSLOT : base1;
-            const float g2i = g2s[16 * I + l16];
+            const float gih = tb.gh[16 * I + l16], gil = tb.gl[16 * I + l16];
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
                 const int J = k - kb;
                 if (k < kb || k >= kend || J > I) continue;  // wave-uniform
                 float v[4];
-                tile_values(S[k], J, I, g2i, g2s, cfs, lgs, l16, g4, v);
+                tile_values(S[k], J, I, gih, gil, tb, l16, g4, v);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float *xrow = xs + (16 * J + 4 * g4 + r) * LDP + l16;
@@ -530,7 +606,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * I + 4 * g4 + r;
                     const int64_t row = t0 + i;
-                    if (row < L) y[((b * L + row) * NH + h) * P + p] = acc[ii][pt][r] + Dh * xs[i * LDP + p];
+                    if (row < L)
+                        store_out(&y[((b * L + row) * NH + h) * P + p], acc[ii][pt][r] + Dh * xs[i * LDP + p]);
                 }
             }
         }
@@ -538,68 +615,86 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     }
 }
 
-template <int T, int P, int NKMAX>
-hipError_t launch_bf16(const Problem &p, int HB, int nhb, int64_t blocks, const void *x, const void *B,
-                       const void *C, const float *G2, const float *DT, const float *D, const float *H,
-                       void *y, hipStream_t stream) {
-    constexpr auto kern = k4_chunk_out_bf16<T, P, NKMAX>;
-    const size_t lds = (size_t)P * T * 2 + (size_t)2 * P * (NKMAX * 32) * 2 + (size_t)3 * T * 4;
+// ---------------------------------------------------------------------------
+// launch: InT is the input element type, OutT the element type of y
+// ---------------------------------------------------------------------------
+template <int T, int P, int NKMAX, typename OutT>
+hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
+                          const void *B, const void *C, G2View G2, const float *DT, const float *D,
+                          const float *H, void *y, hipStream_t stream) {
+    constexpr auto kern = k4_chunk_out_bf16<T, P, NKMAX, OutT>;
+    const size_t lds = Bf16Lds<T, P, NKMAX>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
-                       static_cast<const uint16_t *>(C), G2, DT, D, H, static_cast<uint16_t *>(y),
-                       p.seqlen, (int)p.nheads, (int)p.dstate, (int)p.ngroups, (int)p.nchunks,
-                       p.padded_len, (int)p.heads_per_group, HB, nhb);
-    return hipSuccess;
+                       static_cast<const uint16_t *>(C), G2.hi, G2.lo, DT, D, H,
+                       static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.dstate,
+                       (int)p.ngroups, (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB,
+                       nhb);
+    return hipGetLastError();
 }
 
-template <int T, int P>
+template <int T, int P, typename OutT>
+hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
+                         const void *B, const void *C, G2View G2, const float *DT, const float *D,
+                         const float *H, void *y, hipStream_t stream) {
+    constexpr auto kern = k4_chunk_out_f32<T, P, OutT>;
+    constexpr size_t lds = (size_t)T * (P + 4) * 4 + (size_t)4 * T * 4;
+    static_assert(lds <= kLdsBytes, "stage-4 LDS budget exceeded");
+    if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream,
+                       static_cast<const float *>(x), static_cast<const float *>(B),
+                       static_cast<const float *>(C), G2.hi, G2.lo, DT, D, H,
+                       static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.dstate,
+                       (int)p.ngroups, (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB,
+                       nhb);
+    return hipGetLastError();
+}
+
+template <typename InT, typename OutT, int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
-                     const float *G2, const float *DT, const float *D, const float *H, void *y,
+                     G2View G2, const float *DT, const float *D, const float *H, void *y,
                      hipStream_t stream) {
     const int HB = plan.k4_heads_per_block;
     const int nhb = (int)((p.heads_per_group + HB - 1) / HB);
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
     if (blocks == 0) return hipSuccess;
-    if (p.bf16) {
-        const hipError_t e = (p.dstate <= 128) ? launch_bf16<T, P, 4>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream)
-                                               : launch_bf16<T, P, 8>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
-        if (e != hipSuccess) return e;
+    if constexpr (sizeof(InT) == 2) {
+        if (p.dstate <= 128)
+            return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
+        return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
     } else {
-        const size_t lds = (size_t)T * (P + 4) * 4 + (size_t)3 * T * 4;
-        if (allow_lds<k4_chunk_out_f32<T, P>>(lds) != hipSuccess) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k4_chunk_out_f32<T, P>), dim3((unsigned)blocks), dim3(2 * T), lds, stream,
-                           static_cast<const float *>(x), static_cast<const float *>(B),
-                           static_cast<const float *>(C), G2, DT, D, H, static_cast<float *>(y),
-                           p.seqlen, (int)p.nheads, (int)p.dstate, (int)p.ngroups, (int)p.nchunks,
-                           p.padded_len, (int)p.heads_per_group, HB, nhb);
-    }
-    return hipGetLastError();
-}
-
-template <int T>
-hipError_t launch_t(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
-                    const float *G2, const float *DT, const float *D, const float *H, void *y,
-                    hipStream_t stream) {
-    switch (p.headdim) {
-        case 32: return launch_tp<T, 32>(p, plan, x, B, C, G2, DT, D, H, y, stream);
-        case 64: return launch_tp<T, 64>(p, plan, x, B, C, G2, DT, D, H, y, stream);
-        case 128: return launch_tp<T, 128>(p, plan, x, B, C, G2, DT, D, H, y, stream);
-        default: return hipErrorInvalidValue;
+        return launch_f32_in<T, P, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
     }
 }
 
-}  // namespace
-
-hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                            const void *C, const float *G2, const float *DT, const float *D,
-                            const float *H, void *y, hipStream_t stream) {
+template <typename InT, typename OutT>
+hipError_t launch(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
+                  G2View G2, const float *DT, const float *D, const float *H, void *y,
+                  hipStream_t stream) {
+#define SSD_K4_P(T)                                                                              \
+    switch (p.headdim) {                                                                         \
+        case 32: return launch_tp<InT, OutT, T, 32>(p, plan, x, B, C, G2, DT, D, H, y, stream);  \
+        case 64: return launch_tp<InT, OutT, T, 64>(p, plan, x, B, C, G2, DT, D, H, y, stream);  \
+        case 128: return launch_tp<InT, OutT, T, 128>(p, plan, x, B, C, G2, DT, D, H, y, stream); \
+        default: return hipErrorInvalidValue;                                                    \
+    }
     switch (p.chunk) {
-        case 64: return launch_t<64>(p, plan, x, B, C, G2, DT, D, H, y, stream);
-        case 128: return launch_t<128>(p, plan, x, B, C, G2, DT, D, H, y, stream);
-        case 256: return launch_t<256>(p, plan, x, B, C, G2, DT, D, H, y, stream);
+        case 64: SSD_K4_P(64)
+        case 128: SSD_K4_P(128)
+        case 256: SSD_K4_P(256)
         default: return hipErrorInvalidValue;
     }
+#undef SSD_K4_P
 }
 
+// One explicit instantiation per translation unit (compiled in parallel).
+hipError_t launch_bf16_in_f32_out(const Problem &p, const Plan &plan, const void *x, const void *B,
+                                  const void *C, G2View G2, const float *DT, const float *D,
+                                  const float *H, void *y, hipStream_t stream);
+hipError_t launch_bf16_in_bf16_out(const Problem &p, const Plan &plan, const void *x, const void *B,
+                                   const void *C, G2View G2, const float *DT, const float *D,
+                                   const float *H, void *y, hipStream_t stream);
+
+}  // namespace k4
 }  // namespace ssd

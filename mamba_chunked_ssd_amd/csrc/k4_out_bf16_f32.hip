@@ -1,0 +1,15 @@
+// k4_out_bf16_f32.hip -- stage 4 (chunk output) instantiated for bf16 inputs and an fp32 y.
+// The kernels and their documentation are in k4_chunk_out.h.
+#include "k4_chunk_out.h"
+
+namespace ssd {
+namespace k4 {
+
+hipError_t launch_bf16_in_f32_out(const Problem &p, const Plan &plan, const void *x, const void *B,
+                                  const void *C, G2View G2, const float *DT, const float *D,
+                                  const float *H, void *y, hipStream_t stream) {
+    return launch<uint16_t, float>(p, plan, x, B, C, G2, DT, D, H, y, stream);
+}
+
+}  // namespace k4
+}  // namespace ssd

@@ -1,0 +1,15 @@
+// k4_out_f32.hip -- stage 4 (chunk output) instantiated for fp32 inputs and an fp32 y, plus the stage-4 dispatch.
+// The kernels and their documentation are in k4_chunk_out.h.
+#include "k4_chunk_out.h"
+
+namespace ssd {
+
+hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
+                            const void *C, G2View G2, const float *DT, const float *D,
+                            const float *H, void *y, hipStream_t stream) {
+    if (!p.bf16) return k4::launch<float, float>(p, plan, x, B, C, G2, DT, D, H, y, stream);
+    if (p.y_bf16) return k4::launch_bf16_in_bf16_out(p, plan, x, B, C, G2, DT, D, H, y, stream);
+    return k4::launch_bf16_in_f32_out(p, plan, x, B, C, G2, DT, D, H, y, stream);
+}
+
+}  // namespace ssd

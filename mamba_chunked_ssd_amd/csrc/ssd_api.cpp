@@ -44,6 +44,8 @@ ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
         return SSD_ERROR_INVALID_VALUE;
     if (s->nheads % s->ngroups != 0) return SSD_ERROR_INVALID_VALUE;
     if (s->dtype != SSD_DTYPE_F32 && s->dtype != SSD_DTYPE_BF16) return SSD_ERROR_INVALID_VALUE;
+    if (s->y_dtype != SSD_DTYPE_F32 && s->y_dtype != s->dtype) return SSD_ERROR_INVALID_VALUE;
+    if (s->reserved != 0) return SSD_ERROR_INVALID_VALUE;
     if ((s->flags & ~(uint32_t)SSD_FLAG_KEEP_INTERMEDIATES) != 0) return SSD_ERROR_INVALID_VALUE;
     if (!chunk_supported(chunk) || !headdim_supported(s->headdim) || !dstate_supported(s->dstate))
         return SSD_ERROR_UNSUPPORTED;
@@ -60,6 +62,7 @@ ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
     q.padded_len = q.nchunks * chunk;
     q.heads_per_group = s->nheads / s->ngroups;
     q.bf16 = s->dtype == SSD_DTYPE_BF16;
+    q.y_bf16 = s->y_dtype == SSD_DTYPE_BF16;
 
     // Every element count must fit int64; kernel-side scalar parameters fit int32.
     int64_t t, e;
@@ -88,7 +91,9 @@ ssd_workspace_layout layout_for(const Problem &p, bool keep) {
     const size_t seq = (size_t)p.batch * p.nheads * p.padded_len * sizeof(float);
     const size_t states = (size_t)p.batch * p.nheads * p.nchunks * p.headdim * p.dstate * sizeof(float);
     size_t off = 0;
-    l.g2 = off;
+    l.g2_hi = off;
+    off = align_up(off + seq);
+    l.g2_lo = off;
     off = align_up(off + seq);
     l.dt = off;
     off = align_up(off + seq);
@@ -182,6 +187,7 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     const bool keep = (shape->flags & SSD_FLAG_KEEP_INTERMEDIATES) != 0;
     const ssd_workspace_layout lay = layout_for(p, keep);
     const size_t esz = p.bf16 ? 2 : 4;
+    const size_t ysz = p.y_bf16 ? 2 : 4;
 
     const size_t tok = (size_t)(p.batch * p.seqlen);
     const size_t x_bytes = tok * p.nheads * p.headdim * esz;
@@ -209,7 +215,7 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
 
     // aliasing: outputs must not overlap inputs or each other; final_states may
     // be the very same buffer as initial_states.
-    const Range ry = range_of(y, x_bytes);
+    const Range ry = range_of(y, x_bytes / esz * ysz);
     const Range rws = range_of(workspace, lay.total);
     const Range rfin = range_of(final_states, final_states ? st_bytes : 0);
     const Range rinit = range_of(init, init ? st_bytes : 0);
@@ -227,7 +233,8 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
 
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
-    float *G2 = reinterpret_cast<float *>(ws + lay.g2);
+    const G2Pair G2{reinterpret_cast<float *>(ws + lay.g2_hi), reinterpret_cast<float *>(ws + lay.g2_lo)};
+    const G2View G2v{G2.hi, G2.lo};
     float *DTf = reinterpret_cast<float *>(ws + lay.dt);
     float *S = reinterpret_cast<float *>(ws + lay.s);
     float *Hs = reinterpret_cast<float *>(ws + lay.h);
@@ -243,13 +250,13 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     }
     if (!record(1)) return SSD_ERROR_LAUNCH;
     if (p.nchunks > 0) {
-        if (launch_chunk_state(p, plan, x, B, G2, DTf, S, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
+        if (launch_chunk_state(p, plan, x, B, G2v, DTf, S, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
     }
     if (!record(2)) return SSD_ERROR_LAUNCH;
-    if (launch_state_pass(p, S, Hs, G2, init, final_states, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
+    if (launch_state_pass(p, S, Hs, G2v, init, final_states, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
     if (!record(3)) return SSD_ERROR_LAUNCH;
     if (p.nchunks > 0) {
-        if (launch_chunk_out(p, plan, x, B, C, G2, DTf, D, Hs, y, stream) != hipSuccess)
+        if (launch_chunk_out(p, plan, x, B, C, G2v, DTf, D, Hs, y, stream) != hipSuccess)
             return SSD_ERROR_LAUNCH;
     }
     if (!record(4)) return SSD_ERROR_LAUNCH;

@@ -14,7 +14,8 @@ struct Problem {
     int64_t nchunks;          // ceil(seqlen / chunk)
     int64_t padded_len;       // nchunks * chunk
     int64_t heads_per_group;  // nheads / ngroups
-    bool bf16;                // element type of x, dt, B, C, y
+    bool bf16;                // element type of x, dt, B, C
+    bool y_bf16;              // element type of y
 };
 
 // Launch configuration chosen on the host per problem.
@@ -28,25 +29,36 @@ Plan make_plan(const Problem &p);
 // Each launcher enqueues one kernel on `stream` and returns hipSuccess or the
 // launch error.  Buffers follow the layouts documented in include/ssd.h.
 
-// Stage 1: per-chunk inclusive cumsum of log2(e) * A * dt -> G2, and dt
-// widened to fp32 -> DT; both head-major (batch, nheads, padded_len).
-hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A,
-                               float *G2, float *DT, hipStream_t stream);
+// Decay sums G2 = log2(e) * per-chunk inclusive cumsum of A dt, summed in fp64
+// and stored as a pair of floats (G2 = hi + lo), head-major
+// (batch, nheads, padded_len).
+struct G2Pair {
+    float *hi;
+    float *lo;
+};
+struct G2View {
+    const float *hi;
+    const float *lo;
+};
+
+// Stage 1: G2 (hi/lo) and dt widened to fp32 -> DT, all head-major.
+hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
+                               float *DT, hipStream_t stream);
 
 // Stage 2: per-chunk input state s_c = sum_t exp2(G2_last - G2_t) DT_t x_t B_t^T,
 // written as (batch, nheads, nchunks, headdim, dstate) fp32.
 hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
-                              const float *G2, const float *DT, float *S, hipStream_t stream);
+                              G2View G2, const float *DT, float *S, hipStream_t stream);
 
 // Stage 3: h_0 = init (or 0); for each chunk store h_c then
 // h_{c+1} = exp2(G2_last,c) h_c + s_c; final = h_nchunks.  H may equal S.
-hipError_t launch_state_pass(const Problem &p, const float *S, float *H, const float *G2,
+hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View G2,
                              const float *init, float *final_states, hipStream_t stream);
 
 // Stage 4: chunk output
 // y_i = exp2(G2_i) C_i h_c + sum_{j<=i} exp2(G2_i - G2_j) (C_i . B_j) DT_j x_j + D x_i.
 hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                            const void *C, const float *G2, const float *DT, const float *D,
+                            const void *C, G2View G2, const float *DT, const float *D,
                             const float *H, void *y, hipStream_t stream);
 
 // Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per

@@ -37,20 +37,23 @@ def to_device(inp: dict, dtype: str, dev="cuda"):
     return out
 
 
-def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = True):
-    """Forward pass; returns numpy fp64 dict with y, final and (keep) G2/DT/S/H."""
+def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = True,
+        y_dtype: str = "f32"):
+    """Forward pass; returns numpy fp64 dict with y, final and (keep) G2/DT/S/H
+    (G2 = the stored hi + lo pair, summed in fp64)."""
     t = to_device(inp, dtype)
     b, L, nh, p = t["x"].shape
     g, n = t["B"].shape[2], t["B"].shape[3]
     ws = None
     lay = None
     if keep:
-        shape = ssd.make_shape(b, L, nh, p, n, g, dtype, keep=True)
+        shape = ssd.make_shape(b, L, nh, p, n, g, dtype, keep=True, y_dtype=y_dtype)
         lay = ssd.workspace_layout(shape, chunk)
         ws = torch.empty(max(lay.total, 1), dtype=torch.uint8, device="cuda")
     res = ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=chunk,
                              initial_states=t["h0"], return_final_states=final, workspace=ws,
-                             keep_intermediates=keep)
+                             keep_intermediates=keep,
+                             y_dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32)
     torch.cuda.synchronize()
     if final:
         y, fin = res
@@ -64,7 +67,7 @@ def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = Tru
             cnt = int(np.prod(shape))
             return ws[off: off + 4 * cnt].view(torch.float32).reshape(shape).double().cpu().numpy()
 
-        out["G2"] = view(lay.g2, (b, nh, Lp))
+        out["G2"] = view(lay.g2_hi, (b, nh, Lp)) + view(lay.g2_lo, (b, nh, Lp))
         out["DT"] = view(lay.dt, (b, nh, Lp))
         out["S"] = view(lay.s, (b, nh, nc, p, n))
         out["H"] = view(lay.h, (b, nh, nc, p, n))

@@ -58,11 +58,12 @@ def test_status_strings(lib):
 
 
 def shape(**kw):
-    d = dict(batch=2, seqlen=1000, nheads=8, headdim=64, dstate=128, ngroups=2, dtype="bf16")
+    d = dict(batch=2, seqlen=1000, nheads=8, headdim=64, dstate=128, ngroups=2, dtype="bf16",
+             y_dtype="f32")
     d.update(kw)
     keep = d.pop("keep", False)
     return ssd.make_shape(d["batch"], d["seqlen"], d["nheads"], d["headdim"], d["dstate"],
-                          d["ngroups"], d["dtype"], keep)
+                          d["ngroups"], d["dtype"], keep, d["y_dtype"])
 
 
 def test_workspace_size_formula(lib):
@@ -73,13 +74,14 @@ def test_workspace_size_formula(lib):
             seq = 4 * 2 * 8 * nc * T
             st = 4 * 2 * 8 * nc * 64 * 128
             up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-            want = up(seq) * 2 + up(st) * (2 if keep else 1)
+            want = up(seq) * 3 + up(st) * (2 if keep else 1)
             assert ssd.workspace_size(s, T) == want
             lay = ssd.workspace_layout(s, T)
             assert lay.total == want and lay.nchunks == nc and lay.padded_len == nc * T
-            offs = [lay.g2, lay.dt, lay.s, lay.h]
+            offs = [lay.g2_hi, lay.g2_lo, lay.dt, lay.s, lay.h]
             assert all(o % 256 == 0 for o in offs)
-            assert lay.g2 == 0 and lay.dt == up(seq) and lay.s == 2 * up(seq)
+            assert lay.g2_hi == 0 and lay.g2_lo == up(seq) and lay.dt == 2 * up(seq)
+            assert lay.s == 3 * up(seq)
             assert (lay.h == lay.s) != keep
 
 
@@ -89,6 +91,16 @@ def test_workspace_size_formula(lib):
 ])
 def test_workspace_size_invalid_is_zero(lib, bad):
     assert ssd.workspace_size(shape(**bad), 256) == 0
+
+
+def test_y_dtype_rules(lib):
+    # y is fp32 or the input type; reserved must be 0
+    assert ssd.workspace_size(shape(dtype="bf16", y_dtype="bf16"), 256) > 0
+    assert ssd.workspace_size(shape(dtype="bf16", y_dtype="f32"), 256) > 0
+    assert ssd.workspace_size(shape(dtype="f32", y_dtype="bf16"), 256) == 0
+    s = shape()
+    s.reserved = 1
+    assert ssd.workspace_size(s, 256) == 0
 
 
 @pytest.mark.parametrize("bad", [dict(headdim=48), dict(dstate=24), dict(dstate=272), dict(headdim=256)])
