@@ -23,20 +23,33 @@
 // row i: an A-operand fragment of the next product, up to a fixed relabelling
 // of the contraction index that the X operand reads mirror.
 //  * bf16 inputs: v_mfma_f32_16x16x32_bf16.  X is staged per head in LDS
-//    transposed ([headdim][token], 8-byte units XOR-swizzled by
-//    (row ^ row >> 3) & 15: conflict-free for the transposing writes and the
-//    operand reads).  The fp32-valued operands -- the decay-masked tile and the
-//    carried state h_c -- are split into hi + lo bf16 halves and multiplied by
-//    the exact bf16 inputs, so the result keeps fp32-accumulation accuracy.
+//    transposed ([headdim][token]); h_c is staged as hi/lo bf16.  The
+//    fp32-valued operands -- the decay-masked tile and h_c -- are split into
+//    hi + lo bf16 halves and multiplied by the exact bf16 inputs, so the
+//    result keeps fp32-accumulation accuracy.
 //  * fp32 inputs: v_mfma_f32_16x16x4_f32 on the fp32 values directly; X is
 //    staged in its natural layout, h_c and C fragments are read from global
 //    memory (L2) as 16-byte vectors.
-// Off-diagonal tiles (J < I) use exp2(G2_i - G2_j) = exp2(G2_i - G2_e) *
-// exp2(G2_e - G2_j) with e the last token of tile J: both exponents are <= 0,
-// and the second factor (times dt_j) is tabulated once per head and token, so
-// a lane needs one exp2 per tile instead of four.  The next head's x, h_c and
+// Per head, the block tabulates in LDS what every lane would otherwise
+// recompute: exp2(G2_i) (row decay of the carried-state term), the column
+// factor exp2(G2_e - G2_j) dt_j with e the last token of j's 16-token tile,
+// and the row factor exp2(G2_i - G2_e(J)) for every row i and earlier tile J.
+// An off-diagonal tile (J < I) then takes exp2(G2_i - G2_j) dt_j as
+// rowfactor(i, J) * colfactor(j): both factors have exponents <= 0, so neither
+// can overflow.  Only the diagonal tile evaluates per-element exponentials.
+// All G2 differences are formed from the fp64-derived hi/lo pair.
+//
+// LDS layouts (bank-conflict free on gfx950, measured with
+// SQ_LDS_BANK_CONFLICT): the transposed x tile uses rows of 2T + 16 bytes
+// (64-bit operand reads by 32 lanes hit 32 distinct 8-byte bank groups); the
+// h tile uses rows of 2 NPAD + 32 bytes (128-bit reads).  Both are read at a
+// per-lane base plus compile-time immediates.  When it fits, each wave parks
+// its C fragments in an unpadded C tile whose 16-byte chunks are XOR-swizzled
+// by (row & 15) instead of holding them in registers for the whole block.  The next head's x, h_c and
 // decay data are loaded into registers while the current head computes.
 #pragma once
+
+#include <utility>
 
 #include "ssd_device.h"
 #include "ssd_internal.h"
@@ -44,40 +57,64 @@
 namespace ssd {
 namespace k4 {
 
+// gfx950 LDS per CU (and the most one block may use)
+constexpr size_t kLdsBytes = 160 * 1024;
+
 // Wave w owns row tiles I0 = w and I1 = T/16 - 1 - w.  Its S slots are laid
 // out as [I0: J = 0..I0][pad to even][I1: J = 0..I1][pad to even]; the total
 // is always T/16 + 2 and a pair (2q, 2q + 1) never straddles the two tiles.
 __device__ __forceinline__ int slot_base1(int I0) { return (I0 + 2) & ~1; }
 
-// Per-head decay tables (T floats each, in LDS) for the tokens of the chunk:
-//   gh[t] + gl[t] = G2_t (the hi/lo pair),  dts[t] = dt_t,
-//   cfs[t] = exp2(G2_e(t) - G2_t) dt_t with e(t) the last token of t's 16-tile.
-// Every exponent below is a difference formed as (hi_i - hi_j) + (lo_i - lo_j).
+// Per-head tables in LDS (T floats each, and T/16 x T for the row factors):
+//   gh[t] + gl[t] = G2_t (hi/lo),  dt[t],  e2[t] = exp2(G2_t),
+//   cf[t] = exp2(G2_e(t) - G2_t) dt_t,  e(t) = last token of t's 16-tile,
+//   rf[J * T + i] = exp2(G2_i - G2_e(J)) for i > e(J) (else 0).
+template <int T>
 struct Tables {
-    float *gh, *gl, *cfs, *dts;
+    float *gh, *gl, *dt, *e2, *cf, *rf;
+    static constexpr size_t bytes = (size_t)5 * T * 4 + (size_t)(T / 16) * T * 4;
+    __device__ Tables(float *base)
+        : gh(base), gl(base + T), dt(base + 2 * T), e2(base + 3 * T), cf(base + 4 * T),
+          rf(base + 5 * T) {}
 };
 
-__device__ __forceinline__ void head_tables(const Tables &tb, int t, float gh, float gl, float geh,
-                                            float gel, float d) {
+// Per-token part of the tables (thread t < T), from its G2 pair, the pair at
+// its tile end, and dt.
+template <int T>
+__device__ __forceinline__ void token_tables(const Tables<T> &tb, int t, float gh, float gl,
+                                             float geh, float gel, float d) {
     tb.gh[t] = gh;
     tb.gl[t] = gl;
-    tb.cfs[t] = fast_exp2((geh - gh) + (gel - gl)) * d;
-    tb.dts[t] = d;
+    tb.dt[t] = d;
+    tb.e2[t] = fast_exp2(gh + gl);
+    tb.cf[t] = fast_exp2((geh - gh) + (gel - gl)) * d;
+}
+
+// Row-factor part (after token_tables is visible): thread tid of nthr covers
+// rows i = tid % T and tiles J = (tid / T), (tid / T) + nthr / T, ...
+template <int T>
+__device__ __forceinline__ void row_factor_table(const Tables<T> &tb, int tid, int nthr) {
+    const int i = tid % T;
+    const float ih = tb.gh[i], il = tb.gl[i];
+    for (int J = tid / T; J < T / 16; J += nthr / T) {
+        const int e = 16 * J + 15;
+        tb.rf[J * T + i] = (i > e) ? fast_exp2((ih - tb.gh[e]) + (il - tb.gl[e])) : 0.f;
+    }
 }
 
 // Decay-and-dt weighted values of one S tile slot for this lane: row
-// i = 16 I + l16 (G2_i = gih + gil), columns j = 16 J + 4 g4 + r.  On the
-// diagonal tile the exponent is the exact difference G2_i - G2_j (0 for j = i)
-// and the mask is a select taken before exp2; off the diagonal both factors of
-// exp2(G2_i - G2_e) exp2(G2_e - G2_j) have exponents <= 0.
-__device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, float gih, float gil,
-                                            const Tables &tb, int l16, int g4, float (&v)[4]) {
+// i = 16 I + l16, columns j = 16 J + 4 g4 + r.  On the diagonal tile the
+// exponent is the exact difference G2_i - G2_j (0 for j = i) and the mask is
+// a select taken before exp2.
+template <int T>
+__device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, int l16, int g4,
+                                            float gih, float gil, const Tables<T> &tb,
+                                            float (&v)[4]) {
     if (J > I) {
         v[0] = v[1] = v[2] = v[3] = 0.f;
     } else if (J < I) {
-        const int e = 16 * J + 15;
-        const float rf = fast_exp2((gih - tb.gh[e]) + (gil - tb.gl[e]));
-        const float4 cf = *reinterpret_cast<const float4 *>(tb.cfs + 16 * J + 4 * g4);
+        const float rf = tb.rf[J * T + 16 * I + l16];
+        const float4 cf = *reinterpret_cast<const float4 *>(tb.cf + 16 * J + 4 * g4);
         v[0] = s[0] * (rf * cf.x);
         v[1] = s[1] * (rf * cf.y);
         v[2] = s[2] * (rf * cf.z);
@@ -85,7 +122,7 @@ __device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, floa
     } else {
         const float4 jh = *reinterpret_cast<const float4 *>(tb.gh + 16 * J + 4 * g4);
         const float4 jl = *reinterpret_cast<const float4 *>(tb.gl + 16 * J + 4 * g4);
-        const float4 dj = *reinterpret_cast<const float4 *>(tb.dts + 16 * J + 4 * g4);
+        const float4 dj = *reinterpret_cast<const float4 *>(tb.dt + 16 * J + 4 * g4);
         const float hv[4] = {jh.x, jh.y, jh.z, jh.w};
         const float lv[4] = {jl.x, jl.y, jl.z, jl.w};
         const float dv[4] = {dj.x, dj.y, dj.z, dj.w};
@@ -98,16 +135,6 @@ __device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, floa
     }
 }
 
-// exp2(G2) of the four accumulator rows 16 I + 4 g4 + r
-__device__ __forceinline__ void row_decay(const Tables &tb, int I, int g4, float (&e)[4]) {
-    const float4 h = *reinterpret_cast<const float4 *>(tb.gh + 16 * I + 4 * g4);
-    const float4 l = *reinterpret_cast<const float4 *>(tb.gl + 16 * I + 4 * g4);
-    e[0] = fast_exp2(h.x + l.x);
-    e[1] = fast_exp2(h.y + l.y);
-    e[2] = fast_exp2(h.z + l.z);
-    e[3] = fast_exp2(h.w + l.w);
-}
-
 template <typename OutT>
 __device__ __forceinline__ void store_out(OutT *p, float v);
 template <>
@@ -117,68 +144,298 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
     *p = (uint16_t)(pack_bf16(v, 0.f) & 0xffffu);
 }
 
+__device__ __forceinline__ uint32_t sel_half(int q) { return (q & 1) ? 0x07060302u : 0x05040100u; }
+
+// Lane coordinates re-derived from an opaque copy of the thread index inside
+// a loop, so the compiler recomputes the cheap per-lane offsets instead of
+// hoisting every one of them out of the head loop into registers.
+struct LaneIds {
+    int l16, g4, w;
+};
+__device__ __forceinline__ LaneIds opaque_lane_ids(int tid) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    LaneIds r;
+    r.l16 = t & 15;
+    r.g4 = (t >> 4) & 3;
+    r.w = __builtin_amdgcn_readfirstlane(t >> 6);
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 path
 // ---------------------------------------------------------------------------
-// 8-byte-unit swizzle of the transposed x tile ([P][T] bf16).
-__device__ __forceinline__ int swz16(int row) { return (row ^ (row >> 3)) & 15; }
-template <int T>
-__device__ __forceinline__ int xt_off(int row, int unit) {  // unit = token / 4
-    return row * (T * 2) + ((unit ^ swz16(row)) << 3);
-}
-// 16-byte-chunk swizzle of the h tile ([P][NPAD] bf16).
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
-template <int NPAD>
-__device__ __forceinline__ int h_off(int row, int chunk) {  // chunk = n / 8
-    return row * (NPAD * 2) + ((chunk ^ swz8(row)) << 4);
-}
-
-__device__ __forceinline__ uint32_t sel_half(int q) { return (q & 1) ? 0x07060302u : 0x05040100u; }
-
-// gfx950 LDS per CU (and the most one block may use)
-constexpr size_t kLdsBytes = 160 * 1024;
-
-// LDS of the bf16 kernel: x^T tile, the h hi/lo tiles when they fit, decay tables.
+// LDS of the bf16 kernel: x^T tile, the h hi/lo tiles when they fit, tables.
 template <int T, int P, int NKMAX>
 struct Bf16Lds {
-    static constexpr size_t x = (size_t)P * T * 2;
-    static constexpr size_t h = (size_t)2 * P * (NKMAX * 32) * 2;
-    static constexpr size_t tables = (size_t)4 * T * 4;
+    static constexpr int XRS = 2 * T + 16;           // x^T row stride (bytes)
+    static constexpr int HRS = 2 * NKMAX * 32 + 32;  // h / C row stride (bytes)
+    static constexpr size_t x = (size_t)P * XRS;
+    static constexpr size_t h = (size_t)2 * P * HRS;
+    static constexpr int CRS = 2 * NKMAX * 32;       // C row stride (bytes), XOR-swizzled
+    static constexpr size_t c = (size_t)T * CRS;     // the chunk's C rows
+    static constexpr size_t tables = Tables<T>::bytes;
     // h is staged in LDS when everything fits; otherwise its fragments are read
     // from global memory (L2) and split into hi/lo in registers.
     static constexpr bool h_in_lds = x + h + tables <= kLdsBytes;
-    static constexpr size_t total = x + (h_in_lds ? h : 0) + tables;
+    // The C fragments of a wave's row tiles live in LDS (rather than in 8 NKMAX
+    // registers per lane for the whole block) when that still fits.
+    static constexpr bool c_in_lds = h_in_lds && x + h + c + tables <= kLdsBytes;
+    static constexpr size_t total = x + (h_in_lds ? h : 0) + (c_in_lds ? c : 0) + tables;
     static_assert(total <= kLdsBytes, "stage-4 LDS budget exceeded");
 };
+
+// Compile-time loops and the wave-index dispatch: every wave runs straight-line
+// code specialised for its own pair of row tiles, so no tile-pair step sits
+// behind a runtime branch and the compiler can schedule across steps.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int NW, typename F>
+__device__ __forceinline__ void dispatch_wave(int w, F &&f) {
+    static_for<NW>([&](auto wc) {
+        if (w == decltype(wc)::value) f(wc);
+    });
+}
+
+// Slot layout of wave W (see slot_base1) as compile-time functions.
+template <int T, int W>
+struct WaveTiles {
+    static constexpr int NT16 = T / 16;
+    static constexpr int NSLOT = NT16 + 2;
+    static constexpr int I0 = W, I1 = NT16 - 1 - W;
+    static constexpr int base1 = (I0 + 2) & ~1;
+    static constexpr int ii_of(int k) { return k < base1 ? 0 : 1; }
+    static constexpr int I_of(int k) { return k < base1 ? I0 : I1; }
+    static constexpr int J_of(int k) { return k < base1 ? k : k - base1; }
+};
+
+// tile_values with the tile relation known at compile time
+template <int T, int J, int I>
+__device__ __forceinline__ void tile_values_ct(const floatx4 &s, int l16, int g4, float gih, float gil,
+                                               const Tables<T> &tb, float (&v)[4]) {
+    if constexpr (J > I) {
+        v[0] = v[1] = v[2] = v[3] = 0.f;
+    } else if constexpr (J < I) {
+        const float rf = tb.rf[J * T + 16 * I + l16];
+        const float4 cf = *reinterpret_cast<const float4 *>(tb.cf + 16 * J + 4 * g4);
+        v[0] = s[0] * (rf * cf.x);
+        v[1] = s[1] * (rf * cf.y);
+        v[2] = s[2] * (rf * cf.z);
+        v[3] = s[3] * (rf * cf.w);
+    } else {
+        const float4 jh = *reinterpret_cast<const float4 *>(tb.gh + 16 * J + 4 * g4);
+        const float4 jl = *reinterpret_cast<const float4 *>(tb.gl + 16 * J + 4 * g4);
+        const float4 dj = *reinterpret_cast<const float4 *>(tb.dt + 16 * J + 4 * g4);
+        const float hv[4] = {jh.x, jh.y, jh.z, jh.w};
+        const float lv[4] = {jl.x, jl.y, jl.z, jl.w};
+        const float dv[4] = {dj.x, dj.y, dj.z, dj.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool keep = (4 * g4 + r) <= l16;  // j <= i (diagonal kept)
+            const float arg = keep ? ((gih - hv[r]) + (gil - lv[r])) : -INFINITY;
+            v[r] = keep ? s[r] * (fast_exp2(arg) * dv[r]) : 0.f;
+        }
+    }
+}
+
+// C B^T tiles of wave W (transposed: lane holds S[i = 16 I + l16][j = 16 J + 4 g4 + r]).
+// Bc points at B[b, t0, g, 0]; rows past `rows` (the chunk's valid tokens) and
+// columns past N read as zero.
+template <int T, int NKMAX, int W>
+__device__ __forceinline__ void cbt_tiles(floatx4 (&S)[T / 16 + 2], const u32x4 (&cfr)[2][NKMAX],
+                                          const uint16_t *Bc, int rows, int GN, int N, int l16,
+                                          int g4) {
+    using WT = WaveTiles<T, W>;
+    static_for<WT::NSLOT>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int I = WT::I_of(k), J = WT::J_of(k), ii = WT::ii_of(k);
+        S[k] = zero4();
+        if constexpr (J <= I) {
+            const int row = 16 * J + l16;
+#pragma unroll
+            for (int ks = 0; ks < NKMAX; ++ks) {
+                const int n0 = 32 * ks + 8 * g4;
+                u32x4 bfr = u32x4{0u, 0u, 0u, 0u};
+                if (row < rows && n0 < N)
+                    bfr = *reinterpret_cast<const u32x4 *>(Bc + (int64_t)row * GN + n0);
+                S[k] = mfma_bf16(bfr, cfr[ii][ks], S[k]);
+            }
+        }
+    });
+}
+
+// Everything one wave computes for one head.
+template <int T, int P, int NKMAX, typename OutT>
+struct HeadCtx {
+    const unsigned char *xl;  // x^T + l16 * XRS + 8 g4
+    const unsigned char *hl;  // h hi tile + l16 * HRS + 16 g4 (when staged in LDS)
+    const unsigned char *cl;  // C tile + l16 * CRS (when staged in LDS)
+    const float *hp;          // h_c in global memory (when not staged)
+    Tables<T> tb;
+    OutT *yh;                 // y[b, t0, h, 0]
+    int64_t NHP;              // nheads * headdim (row stride of y)
+    int rows;                 // valid tokens in the chunk
+    int N;
+    float Dh;
+    int l16, g4;
+};
+
+template <int T, int P, int NKMAX, bool HLDS, bool CLDS, typename OutT, int W>
+__device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
+                                          const u32x4 (&cfr)[2][NKMAX],
+                                          const HeadCtx<T, P, NKMAX, OutT> &cx) {
+    using Lds = Bf16Lds<T, P, NKMAX>;
+    using WT = WaveTiles<T, W>;
+    constexpr int XRS = Lds::XRS, HRS = Lds::HRS;
+    constexpr int PT = P / 16;
+    constexpr int NT16 = T / 16;
+    constexpr int I0 = WT::I0, I1 = WT::I1;
+    const int l16 = cx.l16, g4 = cx.g4;
+
+    floatx4 acc[2][PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
+
+    // inter-chunk term C_i h_c (h split into hi + lo); fragments past dstate are 0
+#pragma unroll
+    for (int ks = 0; ks < NKMAX; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 cf[2];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            if constexpr (CLDS)  // 16-byte chunk (4 ks + g4) of row 16 I + l16, swizzled by l16
+                cf[ii] = *reinterpret_cast<const u32x4 *>(
+                    cx.cl + (16 * (ii ? I1 : I0)) * Lds::CRS + (((4 * ks + g4) ^ l16) << 4));
+            else
+                cf[ii] = cfr[ii][ks];
+        }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            u32x4 hh, hlv;
+            if constexpr (HLDS) {
+                hh = *reinterpret_cast<const u32x4 *>(cx.hl + pt * 16 * HRS + 64 * ks);
+                hlv = *reinterpret_cast<const u32x4 *>(cx.hl + Lds::h / 2 + pt * 16 * HRS + 64 * ks);
+            } else {
+                floatx4 v0 = zero4(), v1 = zero4();
+                const int n0 = 32 * ks + 8 * g4;
+                if (n0 < cx.N) {
+                    const float *src = cx.hp + (16 * pt + l16) * cx.N + n0;
+                    v0 = *reinterpret_cast<const floatx4 *>(src);
+                    v1 = *reinterpret_cast<const floatx4 *>(src + 4);
+                }
+                const HiLo a = split_bf16(v0[0], v0[1]), bq = split_bf16(v0[2], v0[3]);
+                const HiLo cq = split_bf16(v1[0], v1[1]), dq = split_bf16(v1[2], v1[3]);
+                hh = u32x4{a.hi, bq.hi, cq.hi, dq.hi};
+                hlv = u32x4{a.lo, bq.lo, cq.lo, dq.lo};
+            }
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                acc[ii][pt] = mfma_bf16(cf[ii], hh, acc[ii][pt]);
+                acc[ii][pt] = mfma_bf16(cf[ii], hlv, acc[ii][pt]);
+            }
+        }
+    }
+    // rows i = 16 I + 4 g4 + r take exp2(G2_i)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        const float4 e = *reinterpret_cast<const float4 *>(cx.tb.e2 + 16 * (ii ? I1 : I0) + 4 * g4);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            acc[ii][pt][0] *= e.x;
+            acc[ii][pt][1] *= e.y;
+            acc[ii][pt][2] *= e.z;
+            acc[ii][pt][3] *= e.w;
+        }
+    }
+    // intra-chunk term: slot pairs (J, J + 1) of one row tile, K = 32
+    static_for<2>([&](auto iic) {
+        constexpr int ii = decltype(iic)::value;
+        constexpr int I = ii ? I1 : I0;
+        constexpr int kb = ii ? WT::base1 : 0, kend = ii ? WT::NSLOT : WT::base1;
+        const float gih = cx.tb.gh[16 * I + l16], gil = cx.tb.gl[16 * I + l16];
+        static_for<WT::NSLOT / 2>([&](auto qc) {
+            constexpr int k0 = 2 * decltype(qc)::value;
+            if constexpr (k0 >= kb && k0 < kend) {
+                // keep the scheduler from hoisting later pairs' loads into this
+                // one (register pressure at two waves per SIMD)
+                __builtin_amdgcn_sched_barrier(0);
+                constexpr int Ja = k0 - kb, Jb = Ja + 1;
+                constexpr int JbR = Jb < NT16 ? Jb : NT16 - 1;  // padded tile: weights are 0
+                float va[4], vb[4];
+                tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, cx.tb, va);
+                tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, cx.tb, vb);
+                const HiLo p0 = split_bf16(va[0], va[1]), p1 = split_bf16(va[2], va[3]);
+                const HiLo p2 = split_bf16(vb[0], vb[1]), p3 = split_bf16(vb[2], vb[3]);
+                const u32x4 ahi = {p0.hi, p1.hi, p2.hi, p3.hi};
+                const u32x4 alo = {p0.lo, p1.lo, p2.lo, p3.lo};
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    u32x4 bop;
+                    bop.xy = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * Ja);
+                    bop.zw = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * JbR);
+                    acc[ii][pt] = mfma_bf16(ahi, bop, acc[ii][pt]);
+                    acc[ii][pt] = mfma_bf16(alo, bop, acc[ii][pt]);
+                }
+            }
+        });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    // skip term and store: lane holds rows 16 I + 4 g4 + r, column 16 pt + l16
+    const int64_t lane_off = (int64_t)(4 * g4) * cx.NHP + l16;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        const int I = ii ? I1 : I0;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const u32x2 xv2 = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * I);
+            const float xv[4] = {bf16lo(xv2[0]), bf16hi(xv2[0]), bf16lo(xv2[1]), bf16hi(xv2[1])};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                OutT *yr = cx.yh + (int64_t)(16 * I + r) * cx.NHP;
+                if (16 * I + 4 * g4 + r < cx.rows)
+                    store_out(yr + lane_off + 16 * pt, acc[ii][pt][r] + cx.Dh * xv[r]);
+            }
+        }
+    }
+}
 
 template <int T, int P, int NKMAX, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ G2hi, const float *__restrict__ G2lo,
     const float *__restrict__ DT, const float *__restrict__ Dv, const float *__restrict__ H,
-    OutT *__restrict__ y,
-    int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
-    constexpr int NT16 = T / 16;
-    constexpr int NSLOT = NT16 + 2;
-    constexpr int PT = P / 16;
-    constexpr int NPAD = NKMAX * 32;
-    constexpr int NTHR = 2 * T;
-    constexpr int PO = P / 8;
-    constexpr int XUNITS = (T / 4) * PO;              // 4-token x 8-column units of x
-    constexpr int XPASS = (XUNITS + NTHR - 1) / NTHR;
-    constexpr int HCH = NPAD / 8;                     // 8-element chunks per h row
-    constexpr int HUNITS = P * HCH;
-    constexpr int HPASS = (HUNITS + NTHR - 1) / NTHR;
-    constexpr int HREG = Bf16Lds<T, P, NKMAX>::h_in_lds ? HPASS : 1;
-
+    OutT *__restrict__ y, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
+    int nhb) {
     using Lds = Bf16Lds<T, P, NKMAX>;
     constexpr bool kHinLds = Lds::h_in_lds;
+    constexpr int XRS = Lds::XRS, HRS = Lds::HRS;
+    constexpr int NT16 = T / 16;
+    constexpr int NSLOT = NT16 + 2;
+    constexpr int NW = T / 32;
+    constexpr int NTHR = 2 * T;
+    // x staging unit: 4 tokens x 8 headdim columns; within a wave 16 token
+    // quads x 4 column octets (conflict-free transposing LDS writes)
+    constexpr int XUNITS = (T / 4) * (P / 8);
+    constexpr int XPASS = (XUNITS + NTHR - 1) / NTHR;
+    constexpr int TQH = T / 64;                       // token-quad groups of 16
+    constexpr int HCH = NKMAX * 4;                    // 8-element chunks per h row
+    constexpr int HUNITS = P * HCH;
+    constexpr int HPASS = (HUNITS + NTHR - 1) / NTHR;
+    constexpr int HREG = kHinLds ? HPASS : 1;
+
     extern __shared__ __align__(16) unsigned char lds[];
-    unsigned char *xt = lds;                          // [P][T] bf16
-    unsigned char *hhi = xt + Lds::x;                 // [P][NPAD] bf16 (if kHinLds)
-    unsigned char *hlo = hhi + Lds::h / 2;            // [P][NPAD] bf16 (if kHinLds)
-    float *tbase = reinterpret_cast<float *>(xt + Lds::x + (kHinLds ? Lds::h : 0));
-    const Tables tb{tbase, tbase + T, tbase + 2 * T, tbase + 3 * T};
+    unsigned char *xt = lds;                               // [P][XRS]
+    unsigned char *hhi = xt + Lds::x;                      // [P][HRS] (if kHinLds)
+    unsigned char *hlo = hhi + Lds::h / 2;                 // [P][HRS] (if kHinLds)
+    constexpr bool kCinLds = Lds::c_in_lds;
+    unsigned char *ct = xt + Lds::x + (kHinLds ? Lds::h : 0);  // [T][HRS] (if kCinLds)
+    const Tables<T> tb(reinterpret_cast<float *>(ct + (kCinLds ? Lds::c : 0)));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -194,30 +451,36 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     const int h_begin = gi * HPG + hb * HB;
     const int h_end = min(h_begin + HB, (gi + 1) * HPG);
     const int64_t t0 = (int64_t)c * T;
-    const int nk = (N + 31) / 32;
-
-    const int I0 = w, I1 = NT16 - 1 - w;
-    const int base1 = slot_base1(I0);
+    const int rows = (int)min<int64_t>(T, L - t0);  // valid tokens in this chunk
+    const bool full = rows == T;
 
     // ---------------- per-head data, loaded one head ahead ----------------
-    u32x4 xr[XPASS][4];   // unit: 4 tokens x 8 headdim columns
-    floatx4 hr[HREG][2];  // unit: 8 consecutive fp32 of one h row
+    u32x4 xr[XPASS][4];
+    floatx4 hr[HREG][2];
     float sgh = 0.f, sgl = 0.f, seh = 0.f, sel = 0.f, sdt = 0.f;
+    auto xunit = [&](int ps, int &tq, int &po) {
+        const int u = tid + ps * NTHR;
+        const int wv = u >> 6, ln = u & 63;
+        tq = 16 * (wv % TQH) + (ln & 15);
+        po = 4 * (wv / TQH) + (ln >> 4);
+        return u < XUNITS;
+    };
     auto load_head = [&](int h) {
+        const uint16_t *xh = x + ((b * L + t0) * NH + h) * P;
 #pragma unroll
         for (int ps = 0; ps < XPASS; ++ps) {
-            const int u = tid + ps * NTHR;
-            const int po = u % PO, tq = u / PO;
+            int tq, po;
+            const bool ok = xunit(ps, tq, po);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t tok = t0 + 4 * tq + r;
+                const int t = 4 * tq + r;
                 xr[ps][r] = u32x4{0u, 0u, 0u, 0u};
-                if (u < XUNITS && tok < L)
-                    xr[ps][r] = *reinterpret_cast<const u32x4 *>(x + ((b * L + tok) * NH + h) * P + po * 8);
+                if (ok && (full || t < rows))
+                    xr[ps][r] = *reinterpret_cast<const u32x4 *>(xh + (int64_t)t * NH * P + po * 8);
             }
         }
-        const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
         if constexpr (kHinLds) {
+            const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
 #pragma unroll
             for (int ps = 0; ps < HPASS; ++ps) {
                 const int u = tid + ps * NTHR;
@@ -241,189 +504,92 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     auto stage_head = [&]() {
 #pragma unroll
         for (int ps = 0; ps < XPASS; ++ps) {
-            const int u = tid + ps * NTHR;
-            if (u < XUNITS) {
-                const int po = u % PO, tq = u / PO;
+            int tq, po;
+            if (xunit(ps, tq, po)) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const uint32_t s = sel_half(q);
                     const u32x2 v = {__builtin_amdgcn_perm(xr[ps][1][q >> 1], xr[ps][0][q >> 1], s),
                                      __builtin_amdgcn_perm(xr[ps][3][q >> 1], xr[ps][2][q >> 1], s)};
-                    *reinterpret_cast<u32x2 *>(xt + xt_off<T>(8 * po + q, tq)) = v;
+                    *reinterpret_cast<u32x2 *>(xt + (8 * po + q) * XRS + 8 * tq) = v;
                 }
             }
         }
+        if constexpr (kHinLds) {
 #pragma unroll
-        for (int ps = 0; ps < HPASS; ++ps) {
-            const int u = tid + ps * NTHR;
-            if (kHinLds && u < HUNITS) {
-                const int ch = u % HCH, p = u / HCH;
-                u32x4 hi, lo;
-                { const HiLo s2 = split_bf16(hr[ps][0][0], hr[ps][0][1]); hi[0] = s2.hi; lo[0] = s2.lo; }
-                { const HiLo s2 = split_bf16(hr[ps][0][2], hr[ps][0][3]); hi[1] = s2.hi; lo[1] = s2.lo; }
-                { const HiLo s2 = split_bf16(hr[ps][1][0], hr[ps][1][1]); hi[2] = s2.hi; lo[2] = s2.lo; }
-                { const HiLo s2 = split_bf16(hr[ps][1][2], hr[ps][1][3]); hi[3] = s2.hi; lo[3] = s2.lo; }
-                *reinterpret_cast<u32x4 *>(hhi + h_off<NPAD>(p, ch)) = hi;
-                *reinterpret_cast<u32x4 *>(hlo + h_off<NPAD>(p, ch)) = lo;
+            for (int ps = 0; ps < HPASS; ++ps) {
+                const int u = tid + ps * NTHR;
+                if (u < HUNITS) {
+                    const int ch = u % HCH, p = u / HCH;
+                    const HiLo a = split_bf16(hr[ps][0][0], hr[ps][0][1]);
+                    const HiLo bq = split_bf16(hr[ps][0][2], hr[ps][0][3]);
+                    const HiLo cq = split_bf16(hr[ps][1][0], hr[ps][1][1]);
+                    const HiLo dq = split_bf16(hr[ps][1][2], hr[ps][1][3]);
+                    *reinterpret_cast<u32x4 *>(hhi + p * HRS + 16 * ch) = u32x4{a.hi, bq.hi, cq.hi, dq.hi};
+                    *reinterpret_cast<u32x4 *>(hlo + p * HRS + 16 * ch) = u32x4{a.lo, bq.lo, cq.lo, dq.lo};
+                }
             }
         }
-        if (tid < T) head_tables(tb, tid, sgh, sgl, seh, sel, sdt);
+        if (tid < T) token_tables(tb, tid, sgh, sgl, seh, sel, sdt);
     };
 
     if (h_begin < h_end) load_head(h_begin);
 
     // ---------------- C fragments of the wave's two row tiles -------------
-    // lane holds C[t0 + 16 I + l16][32 ks + 8 g4 .. +7]
+    // lane holds C[t0 + 16 I + l16][32 ks + 8 g4 .. +7]; zero past the chunk / dstate
+    const int I0 = w, I1 = NT16 - 1 - w;
     u32x4 cfr[2][NKMAX];
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-        const int64_t row = t0 + 16 * (ii ? I1 : I0) + l16;
+        const int row = 16 * (ii ? I1 : I0) + l16;
 #pragma unroll
         for (int ks = 0; ks < NKMAX; ++ks) {
             const int n0 = 32 * ks + 8 * g4;
             cfr[ii][ks] = u32x4{0u, 0u, 0u, 0u};
-            if (ks < nk && row < L && n0 < N)
-                cfr[ii][ks] = *reinterpret_cast<const u32x4 *>(Cm + ((b * L + row) * G + gi) * N + n0);
+            if (row < rows && n0 < N)
+                cfr[ii][ks] = *reinterpret_cast<const u32x4 *>(Cm + ((b * L + t0 + row) * G + gi) * N + n0);
         }
     }
 
     // ---------------- C B^T tiles (transposed), once per block -------------
     floatx4 S[NSLOT];
+    const uint16_t *Bc = Bm + ((b * L + t0) * G + gi) * N;
+    dispatch_wave<NW>(w, [&](auto wc) {
+        cbt_tiles<T, NKMAX, decltype(wc)::value>(S, cfr, Bc, rows, G * N, N, l16, g4);
+    });
+    if constexpr (kCinLds) {
+        // each wave parks its own C fragments in LDS (read back per head)
 #pragma unroll
-    for (int k = 0; k < NSLOT; ++k) S[k] = zero4();
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const int I = ii ? I1 : I0;
-        const int kb = ii ? base1 : 0, kend = ii ? NSLOT : base1;
-#pragma unroll
-        for (int k = 0; k < NSLOT; ++k) {
-            const int J = k - kb;
-            if (k < kb || k >= kend || J > I) continue;  // wave-uniform
-            const int64_t row = t0 + 16 * J + l16;
-#pragma unroll
-            for (int ks = 0; ks < NKMAX; ++ks) {
-                if (ks >= nk) continue;
-                const int n0 = 32 * ks + 8 * g4;
-                u32x4 bfr = u32x4{0u, 0u, 0u, 0u};
-                if (row < L && n0 < N)
-                    bfr = *reinterpret_cast<const u32x4 *>(Bm + ((b * L + row) * G + gi) * N + n0);
-                S[k] = mfma_bf16(bfr, cfr[ii][ks], S[k]);
-            }
-        }
+            for (int ks = 0; ks < NKMAX; ++ks)
+                *reinterpret_cast<u32x4 *>(ct + (16 * (ii ? I1 : I0) + l16) * Lds::CRS +
+                                           (((4 * ks + g4) ^ l16) << 4)) = cfr[ii][ks];
     }
 
     // ---------------- heads -------------------------------------------------
     for (int h = h_begin; h < h_end; ++h) {
         stage_head();
         __syncthreads();
+        row_factor_table(tb, tid, NTHR);
         if (h + 1 < h_end) load_head(h + 1);
-        const float Dh = (Dv != nullptr) ? Dv[h] : 0.f;
-        // Re-derive the lane coordinates from an opaque copy each head, so the
-        // compiler recomputes the (cheap) swizzled LDS offsets instead of
-        // hoisting all of them out of the head loop into registers.
-        int tid_o = tid;
-        asm volatile("" : "+v"(tid_o));
-        const int l16 = tid_o & 15, g4 = (tid_o >> 4) & 3;
-        const int w_o = __builtin_amdgcn_readfirstlane(tid_o >> 6);
-        const int I0 = w_o, I1 = NT16 - 1 - w_o;
-        const int base1 = slot_base1(I0);
-
-        floatx4 acc[2][PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
-
-        // inter-chunk term C_i h_c (h split into hi + lo)
-        const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
-#pragma unroll
-        for (int ks = 0; ks < NKMAX; ++ks) {
-            if (ks >= nk) continue;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                u32x4 hh, hl;
-                if constexpr (kHinLds) {
-                    const int off = h_off<NPAD>(16 * pt + l16, 4 * ks + g4);
-                    hh = *reinterpret_cast<const u32x4 *>(hhi + off);
-                    hl = *reinterpret_cast<const u32x4 *>(hlo + off);
-                } else {
-                    // lane reads h[p][32 ks + 8 g4 .. +7]; columns past dstate are 0
-                    floatx4 v0 = zero4(), v1 = zero4();
-                    const int n0 = 32 * ks + 8 * g4;
-                    if (n0 < N) {
-                        const float *src = hp + (16 * pt + l16) * N + n0;
-                        v0 = *reinterpret_cast<const floatx4 *>(src);
-                        v1 = *reinterpret_cast<const floatx4 *>(src + 4);
-                    }
-                    const HiLo a = split_bf16(v0[0], v0[1]), bq = split_bf16(v0[2], v0[3]);
-                    const HiLo cq = split_bf16(v1[0], v1[1]), dq = split_bf16(v1[2], v1[3]);
-                    hh = u32x4{a.hi, bq.hi, cq.hi, dq.hi};
-                    hl = u32x4{a.lo, bq.lo, cq.lo, dq.lo};
-                }
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    acc[ii][pt] = mfma_bf16(cfr[ii][ks], hh, acc[ii][pt]);
-                    acc[ii][pt] = mfma_bf16(cfr[ii][ks], hl, acc[ii][pt]);
-                }
-            }
-        }
-        // rows i = 16 I + 4 g4 + r take exp2(G2_i)
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            float e[4];
-            row_decay(tb, ii ? I1 : I0, g4, e);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[ii][pt][r] *= e[r];
-        }
-        // intra-chunk term: slot pairs (J, J + 1) of one row tile, K = 32
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int I = ii ? I1 : I0;
-            const int kb = ii ? base1 : 0, kend = ii ? NSLOT : base1;
-            const float gih = tb.gh[16 * I + l16], gil = tb.gl[16 * I + l16];
-#pragma unroll
-            for (int q = 0; q < NSLOT / 2; ++q) {
-                const int k0 = 2 * q;
-                if (k0 < kb || k0 >= kend) continue;  // wave-uniform
-                const int Ja = k0 - kb, Jb = Ja + 1;
-                float va[4], vb[4];
-                tile_values(S[k0], Ja, I, gih, gil, tb, l16, g4, va);
-                tile_values(S[k0 + 1], Jb, I, gih, gil, tb, l16, g4, vb);
-                u32x4 ahi, alo;
-                { const HiLo s2 = split_bf16(va[0], va[1]); ahi[0] = s2.hi; alo[0] = s2.lo; }
-                { const HiLo s2 = split_bf16(va[2], va[3]); ahi[1] = s2.hi; alo[1] = s2.lo; }
-                { const HiLo s2 = split_bf16(vb[0], vb[1]); ahi[2] = s2.hi; alo[2] = s2.lo; }
-                { const HiLo s2 = split_bf16(vb[2], vb[3]); ahi[3] = s2.hi; alo[3] = s2.lo; }
-                const int JbR = Jb < NT16 ? Jb : NT16 - 1;  // padded tile: weights are 0
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const int p = 16 * pt + l16;
-                    const u32x2 xa = *reinterpret_cast<const u32x2 *>(xt + xt_off<T>(p, 4 * Ja + g4));
-                    const u32x2 xb = *reinterpret_cast<const u32x2 *>(xt + xt_off<T>(p, 4 * JbR + g4));
-                    const u32x4 bop = {xa[0], xa[1], xb[0], xb[1]};
-                    acc[ii][pt] = mfma_bf16(ahi, bop, acc[ii][pt]);
-                    acc[ii][pt] = mfma_bf16(alo, bop, acc[ii][pt]);
-                }
-            }
-        }
-        // skip term and store: lane holds rows 16 I + 4 g4 + r, column 16 pt + l16
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int I = ii ? I1 : I0;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int p = 16 * pt + l16;
-                const u32x2 xi = *reinterpret_cast<const u32x2 *>(xt + xt_off<T>(p, 4 * I + g4));
-                const float xv[4] = {bf16lo(xi[0]), bf16hi(xi[0]), bf16lo(xi[1]), bf16hi(xi[1])};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t row = t0 + 16 * I + 4 * g4 + r;
-                    if (row < L) {
-                        store_out(&y[((b * L + row) * NH + h) * P + p], acc[ii][pt][r] + Dh * xv[r]);
-                    }
-                }
-            }
-        }
+        __syncthreads();
+        const LaneIds id = opaque_lane_ids(tid);
+        HeadCtx<T, P, NKMAX, OutT> cx{xt + id.l16 * XRS + 8 * id.g4,
+                                      hhi + id.l16 * HRS + 16 * id.g4,
+                                      ct + id.l16 * Lds::CRS,
+                                      H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N,
+                                      tb,
+                                      y + ((b * L + t0) * NH + h) * P,
+                                      (int64_t)NH * P,
+                                      rows,
+                                      N,
+                                      (Dv != nullptr) ? Dv[h] : 0.f,
+                                      id.l16,
+                                      id.g4};
+        dispatch_wave<NW>(id.w, [&](auto wc) {
+            head_wave<T, P, NKMAX, kHinLds, kCinLds, OutT, decltype(wc)::value>(S, cfr, cx);
+        });
         __syncthreads();
     }
 }
@@ -431,24 +597,32 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
 // ---------------------------------------------------------------------------
 // fp32 path
 // ---------------------------------------------------------------------------
+template <int T, int P>
+struct F32Lds {
+    static constexpr int LDP = P + 4;                 // padded row of the x tile (floats)
+    static constexpr size_t x = (size_t)T * LDP * 4;
+    static constexpr size_t total = x + Tables<T>::bytes;
+    static_assert(total <= kLdsBytes, "stage-4 LDS budget exceeded");
+};
+
 template <int T, int P, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ Cm,
     const float *__restrict__ G2hi, const float *__restrict__ G2lo, const float *__restrict__ DT,
     const float *__restrict__ Dv, const float *__restrict__ H, OutT *__restrict__ y, int64_t L,
-    int NH, int N, int G, int NC,
-    int64_t Lp, int HPG, int HB, int nhb) {
+    int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
+    using Lds = F32Lds<T, P>;
     constexpr int NT16 = T / 16;
     constexpr int NSLOT = NT16 + 2;
     constexpr int PT = P / 16;
     constexpr int NTHR = 2 * T;
-    constexpr int LDP = P + 4;                       // padded LDS row (floats)
+    constexpr int LDP = Lds::LDP;
     constexpr int XV = T * (P / 4);                  // float4 units of the x tile
     constexpr int XPASS = (XV + NTHR - 1) / NTHR;
 
     extern __shared__ __align__(16) unsigned char lds[];
     float *xs = reinterpret_cast<float *>(lds);       // [T][LDP]
-    const Tables tb{xs + T * LDP, xs + T * LDP + T, xs + T * LDP + 2 * T, xs + T * LDP + 3 * T};
+    const Tables<T> tb(reinterpret_cast<float *>(lds + Lds::x));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -465,11 +639,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     const int h_end = min(h_begin + HB, (gi + 1) * HPG);
     const int64_t t0 = (int64_t)c * T;
     const int ns = N / 16;
-
-    const int I0 = w, I1 = NT16 - 1 - w;
-    const int base1 = slot_base1(I0);
-    const int64_t rowC[2] = {t0 + 16 * I0 + l16, t0 + 16 * I1 + l16};
-    const float *crow[2] = {Cm + ((b * L + rowC[0]) * G + gi) * N, Cm + ((b * L + rowC[1]) * G + gi) * N};
+    const bool full = t0 + T <= L;
 
     floatx4 xr[XPASS];
     float sgh = 0.f, sgl = 0.f, seh = 0.f, sel = 0.f, sdt = 0.f;
@@ -479,7 +649,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
             const int v = tid + ps * NTHR;
             const int t = v / (P / 4), p4 = v % (P / 4);
             xr[ps] = zero4();
-            if (v < XV && t0 + t < L)
+            if (v < XV && (full || t0 + t < L))
                 xr[ps] = *reinterpret_cast<const floatx4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
         }
         if (tid < T) {
@@ -500,10 +670,14 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 *reinterpret_cast<floatx4 *>(xs + t * LDP + 4 * p4) = xr[ps];
             }
         }
-        if (tid < T) head_tables(tb, tid, sgh, sgl, seh, sel, sdt);
+        if (tid < T) token_tables(tb, tid, sgh, sgl, seh, sel, sdt);
     };
 
     if (h_begin < h_end) load_head(h_begin);
+
+    const int I0 = w, I1 = NT16 - 1 - w;
+    const int base1 = slot_base1(I0);
+    const int64_t rowC[2] = {t0 + 16 * I0 + l16, t0 + 16 * I1 + l16};
 
     // C B^T tiles (transposed), once per block.  K = 4 per MFMA: instruction q
     // of a 16-wide dstate step s contracts n = 16 s + 4 g4 + q.
@@ -514,17 +688,19 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     for (int ii = 0; ii < 2; ++ii) {
         const int I = ii ? I1 : I0;
         const int kb = ii ? base1 : 0, kend = ii ? NSLOT : base1;
-        const bool crow_ok = rowC[ii] < L;
+        const bool crow_ok = full || rowC[ii] < L;
+        const float *crow = Cm + ((b * L + (crow_ok ? rowC[ii] : 0)) * G + gi) * N;
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) {
             const int J = k - kb;
             if (k < kb || k >= kend || J > I) continue;  // wave-uniform
             const int64_t row = t0 + 16 * J + l16;
-            const float *brow = Bm + ((b * L + row) * G + gi) * N;
+            const bool brow_ok = full || row < L;
+            const float *brow = Bm + ((b * L + (brow_ok ? row : 0)) * G + gi) * N;
             for (int s = 0; s < ns; ++s) {
                 floatx4 bv = zero4(), cv = zero4();
-                if (row < L) bv = *reinterpret_cast<const floatx4 *>(brow + 16 * s + 4 * g4);
-                if (crow_ok) cv = *reinterpret_cast<const floatx4 *>(crow[ii] + 16 * s + 4 * g4);
+                if (brow_ok) bv = *reinterpret_cast<const floatx4 *>(brow + 16 * s + 4 * g4);
+                if (crow_ok) cv = *reinterpret_cast<const floatx4 *>(crow + 16 * s + 4 * g4);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) S[k] = mfma_f32(bv[q], cv[q], S[k]);
             }
@@ -534,15 +710,15 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     for (int h = h_begin; h < h_end; ++h) {
         stage_head();
         __syncthreads();
+        row_factor_table(tb, tid, NTHR);
         if (h + 1 < h_end) load_head(h + 1);
+        __syncthreads();
         const float Dh = (Dv != nullptr) ? Dv[h] : 0.f;
         const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
-        int tid_o = tid;  // opaque lane coordinates: see the bf16 kernel
-        asm volatile("" : "+v"(tid_o));
-        const int l16 = tid_o & 15, g4 = (tid_o >> 4) & 3;
-        const int w_o = __builtin_amdgcn_readfirstlane(tid_o >> 6);
-        const int I0 = w_o, I1 = NT16 - 1 - w_o;
-        const int base1 = slot_base1(I0);
+        const LaneIds id = opaque_lane_ids(tid);
+        const int I0h = id.w, I1h = NT16 - 1 - id.w;
+        const int base1h = slot_base1(I0h);
+        const int64_t rc[2] = {t0 + 16 * I0h + id.l16, t0 + 16 * I1h + id.l16};
 
         floatx4 acc[2][PT];
 #pragma unroll
@@ -554,11 +730,12 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) {
                 cv[ii] = zero4();
-                if (rowC[ii] < L) cv[ii] = *reinterpret_cast<const floatx4 *>(crow[ii] + 16 * s + 4 * g4);
+                if (full || rc[ii] < L)
+                    cv[ii] = *reinterpret_cast<const floatx4 *>(Cm + ((b * L + rc[ii]) * G + gi) * N + 16 * s + 4 * id.g4);
             }
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const floatx4 hv = *reinterpret_cast<const floatx4 *>(hp + (16 * pt + l16) * N + 16 * s + 4 * g4);
+                const floatx4 hv = *reinterpret_cast<const floatx4 *>(hp + (16 * pt + id.l16) * N + 16 * s + 4 * id.g4);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     acc[0][pt] = mfma_f32(cv[0][q], hv[q], acc[0][pt]);
@@ -568,28 +745,30 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
         }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            float e[4];
-            row_decay(tb, ii ? I1 : I0, g4, e);
+            const float4 e = *reinterpret_cast<const float4 *>(tb.e2 + 16 * (ii ? I1h : I0h) + 4 * id.g4);
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[ii][pt][r] *= e[r];
+            for (int pt = 0; pt < PT; ++pt) {
+                acc[ii][pt][0] *= e.x;
+                acc[ii][pt][1] *= e.y;
+                acc[ii][pt][2] *= e.z;
+                acc[ii][pt][3] *= e.w;
+            }
         }
         // intra-chunk term: instruction r of a slot contracts j = 16 J + 4 g4 + r
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            const int I = ii ? I1 : I0;
-            const int kb = ii ? base1 : 0, kend = ii ? NSLOT : base1;
-            const float gih = tb.gh[16 * I + l16], gil = tb.gl[16 * I + l16];
+            const int I = ii ? I1h : I0h;
+            const int kb = ii ? base1h : 0, kend = ii ? NSLOT : base1h;
+            const float gih = tb.gh[16 * I + id.l16], gil = tb.gl[16 * I + id.l16];
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
                 const int J = k - kb;
                 if (k < kb || k >= kend || J > I) continue;  // wave-uniform
                 float v[4];
-                tile_values(S[k], J, I, gih, gil, tb, l16, g4, v);
+                tile_values<T>(S[k], J, I, id.l16, id.g4, gih, gil, tb, v);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float *xrow = xs + (16 * J + 4 * g4 + r) * LDP + l16;
+                    const float *xrow = xs + (16 * J + 4 * id.g4 + r) * LDP + id.l16;
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt)
                         acc[ii][pt] = mfma_f32(v[r], xrow[16 * pt], acc[ii][pt]);
@@ -598,15 +777,15 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
         }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            const int I = ii ? I1 : I0;
+            const int I = ii ? I1h : I0h;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const int p = 16 * pt + l16;
+                const int p = 16 * pt + id.l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * g4 + r;
+                    const int i = 16 * I + 4 * id.g4 + r;
                     const int64_t row = t0 + i;
-                    if (row < L)
+                    if (full || row < L)
                         store_out(&y[((b * L + row) * NH + h) * P + p], acc[ii][pt][r] + Dh * xs[i * LDP + p]);
                 }
             }
@@ -623,7 +802,7 @@ hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, con
                           const void *B, const void *C, G2View G2, const float *DT, const float *D,
                           const float *H, void *y, hipStream_t stream) {
     constexpr auto kern = k4_chunk_out_bf16<T, P, NKMAX, OutT>;
-    const size_t lds = Bf16Lds<T, P, NKMAX>::total;
+    constexpr size_t lds = Bf16Lds<T, P, NKMAX>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
@@ -639,8 +818,7 @@ hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, cons
                          const void *B, const void *C, G2View G2, const float *DT, const float *D,
                          const float *H, void *y, hipStream_t stream) {
     constexpr auto kern = k4_chunk_out_f32<T, P, OutT>;
-    constexpr size_t lds = (size_t)T * (P + 4) * 4 + (size_t)4 * T * 4;
-    static_assert(lds <= kLdsBytes, "stage-4 LDS budget exceeded");
+    constexpr size_t lds = F32Lds<T, P>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream,
                        static_cast<const float *>(x), static_cast<const float *>(B),
