@@ -135,13 +135,22 @@ __device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, int 
     }
 }
 
+// y is written with raw buffer stores: the resource covers a chunk's rows of
+// one head up to the last valid row, so the hardware drops the stores of rows
+// past the sequence end, and the row offsets stay 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
 template <typename OutT>
-__device__ __forceinline__ void store_out(OutT *p, float v);
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off, float v);
 template <>
-__device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_out<float>(__amdgpu_buffer_rsrc_t r, int off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
-    *p = (uint16_t)(pack_bf16(v, 0.f) & 0xffffu);
+__device__ __forceinline__ void store_out<uint16_t>(__amdgpu_buffer_rsrc_t r, int off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(v, 0.f) & 0xffffu), r, off, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t sel_half(int q) { return (q & 1) ? 0x07060302u : 0x05040100u; }
@@ -181,8 +190,21 @@ struct Bf16Lds {
     // The C fragments of a wave's row tiles live in LDS (rather than in 8 NKMAX
     // registers per lane for the whole block) when that still fits.
     static constexpr bool c_in_lds = h_in_lds && x + h + c + tables <= kLdsBytes;
-    static constexpr size_t total = x + (h_in_lds ? h : 0) + (c_in_lds ? c : 0) + tables;
-    static_assert(total <= kLdsBytes, "stage-4 LDS budget exceeded");
+    static constexpr size_t heads_total = x + (h_in_lds ? h : 0) + (c_in_lds ? c : 0) + tables;
+    static_assert(heads_total <= kLdsBytes, "stage-4 LDS budget exceeded");
+    // Before the first head the x / h / table space is free: B rows are staged
+    // there (from offset 0) in pieces of KSP dstate slices of 32, as many as fit
+    // below the C tile, or else in max(heads_total, half the LDS).
+    static constexpr size_t b_avail =
+        c_in_lds ? x + h : (heads_total > kLdsBytes / 2 ? heads_total : kLdsBytes / 2);
+    static constexpr int KSP = (size_t)T * 64 * NKMAX <= b_avail       ? NKMAX
+                               : (size_t)T * 64 * (NKMAX / 2) <= b_avail ? NKMAX / 2
+                                                                         : NKMAX / 4;
+    static constexpr int NPIECE = NKMAX / KSP;
+    static constexpr size_t b_bytes = (size_t)T * 64 * KSP;
+    static_assert(KSP >= 1 && b_bytes <= b_avail, "stage-4 B staging does not fit");
+    // what the block allocates
+    static constexpr size_t total = heads_total > b_bytes ? heads_total : b_bytes;
 };
 
 // Compile-time loops and the wave-index dispatch: every wave runs straight-line
@@ -244,29 +266,37 @@ __device__ __forceinline__ void tile_values_ct(const floatx4 &s, int l16, int g4
     }
 }
 
-// C B^T tiles of wave W (transposed: lane holds S[i = 16 I + l16][j = 16 J + 4 g4 + r]).
-// Bc points at B[b, t0, g, 0]; rows past `rows` (the chunk's valid tokens) and
-// columns past N read as zero.
-template <int T, int NKMAX, int W>
-__device__ __forceinline__ void cbt_tiles(floatx4 (&S)[T / 16 + 2], const u32x4 (&cfr)[2][NKMAX],
-                                          const uint16_t *Bc, int rows, int GN, int N, int l16,
+// C B^T tiles of wave W (transposed: lane holds S[i = 16 I + l16][j = 16 J + 4 g4 + r]),
+// contribution of the dstate slices ks = KSP * PC .. KSP * PC + KSP - 1.  The
+// slices' B rows are staged in LDS (row stride 64 KSP bytes, 16-byte chunk c
+// of row t stored at chunk c ^ (t & SWM)); bl = that tile + l16 * row stride.
+// C fragments come from the swizzled C tile (CLDS, cl = tile + l16 * CRS) or
+// from registers.
+template <int T, int NKMAX, int KSP, int PC, bool CLDS, int CRS, int W>
+__device__ __forceinline__ void cbt_piece(floatx4 (&S)[T / 16 + 2], const u32x4 (&cfr)[2][NKMAX],
+                                          const unsigned char *bl, const unsigned char *cl, int l16,
                                           int g4) {
     using WT = WaveTiles<T, W>;
-    static_for<WT::NSLOT>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        constexpr int I = WT::I_of(k), J = WT::J_of(k), ii = WT::ii_of(k);
-        S[k] = zero4();
-        if constexpr (J <= I) {
-            const int row = 16 * J + l16;
-#pragma unroll
-            for (int ks = 0; ks < NKMAX; ++ks) {
-                const int n0 = 32 * ks + 8 * g4;
-                u32x4 bfr = u32x4{0u, 0u, 0u, 0u};
-                if (row < rows && n0 < N)
-                    bfr = *reinterpret_cast<const u32x4 *>(Bc + (int64_t)row * GN + n0);
-                S[k] = mfma_bf16(bfr, cfr[ii][ks], S[k]);
-            }
+    constexpr int BROW = 64 * KSP;
+    constexpr int SWM = (4 * KSP >= 16 ? 16 : 4 * KSP) - 1;
+    static_for<KSP>([&](auto kc) {
+        constexpr int ksl = decltype(kc)::value;
+        constexpr int ks = KSP * PC + ksl;
+        u32x4 c0, c1;
+        if constexpr (CLDS) {
+            c0 = *reinterpret_cast<const u32x4 *>(cl + 16 * WT::I0 * CRS + (((4 * ks + g4) ^ l16) << 4));
+            c1 = *reinterpret_cast<const u32x4 *>(cl + 16 * WT::I1 * CRS + (((4 * ks + g4) ^ l16) << 4));
+        } else {
+            c0 = cfr[0][ks];
+            c1 = cfr[1][ks];
         }
+        const unsigned char *bk = bl + (((4 * ksl + g4) ^ (l16 & SWM)) << 4);
+        static_for<WT::I1 + 1>([&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            const u32x4 bf = *reinterpret_cast<const u32x4 *>(bk + 16 * J * BROW);
+            if constexpr (J <= WT::I0) S[J] = mfma_bf16(bf, c0, S[J]);
+            S[WT::base1 + J] = mfma_bf16(bf, c1, S[WT::base1 + J]);
+        });
     });
 }
 
@@ -278,9 +308,8 @@ struct HeadCtx {
     const unsigned char *cl;  // C tile + l16 * CRS (when staged in LDS)
     const float *hp;          // h_c in global memory (when not staged)
     Tables<T> tb;
-    OutT *yh;                 // y[b, t0, h, 0]
-    int64_t NHP;              // nheads * headdim (row stride of y)
-    int rows;                 // valid tokens in the chunk
+    __amdgpu_buffer_rsrc_t yr;  // y[b, t0 .., h, :] through the chunk's last valid row
+    int NHP;                  // nheads * headdim (row stride of y)
     int N;
     float Dh;
     int l16, g4;
@@ -387,7 +416,8 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
     });
     __builtin_amdgcn_sched_barrier(0);
     // skip term and store: lane holds rows 16 I + 4 g4 + r, column 16 pt + l16
-    const int64_t lane_off = (int64_t)(4 * g4) * cx.NHP + l16;
+    constexpr int ES = (int)sizeof(OutT);
+    const int lane_off = ((4 * g4) * cx.NHP + l16) * ES;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
         const int I = ii ? I1 : I0;
@@ -396,11 +426,9 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
             const u32x2 xv2 = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * I);
             const float xv[4] = {bf16lo(xv2[0]), bf16hi(xv2[0]), bf16lo(xv2[1]), bf16hi(xv2[1])};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                OutT *yr = cx.yh + (int64_t)(16 * I + r) * cx.NHP;
-                if (16 * I + 4 * g4 + r < cx.rows)
-                    store_out(yr + lane_off + 16 * pt, acc[ii][pt][r] + cx.Dh * xv[r]);
-            }
+            for (int r = 0; r < 4; ++r)
+                store_out<OutT>(cx.yr, lane_off + (16 * I + r) * cx.NHP * ES + 16 * pt * ES,
+                                acc[ii][pt][r] + cx.Dh * xv[r]);
         }
     }
 }
@@ -535,37 +563,74 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
 
     if (h_begin < h_end) load_head(h_begin);
 
-    // ---------------- C fragments of the wave's two row tiles -------------
-    // lane holds C[t0 + 16 I + l16][32 ks + 8 g4 .. +7]; zero past the chunk / dstate
-    const int I0 = w, I1 = NT16 - 1 - w;
-    u32x4 cfr[2][NKMAX];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const int row = 16 * (ii ? I1 : I0) + l16;
-#pragma unroll
-        for (int ks = 0; ks < NKMAX; ++ks) {
-            const int n0 = 32 * ks + 8 * g4;
-            cfr[ii][ks] = u32x4{0u, 0u, 0u, 0u};
-            if (row < rows && n0 < N)
-                cfr[ii][ks] = *reinterpret_cast<const u32x4 *>(Cm + ((b * L + t0 + row) * G + gi) * N + n0);
-        }
-    }
-
     // ---------------- C B^T tiles (transposed), once per block -------------
-    floatx4 S[NSLOT];
+    // All threads stage the chunk's C rows (into the C tile, when it lives in
+    // LDS) and its B rows (piece by piece) with coalesced 16-byte loads at
+    // clamped addresses; chunks past the chunk's rows or past dstate are zero.
+    // Each wave then reads its fragments from LDS.
+    const int I0 = w, I1 = NT16 - 1 - w;
     const uint16_t *Bc = Bm + ((b * L + t0) * G + gi) * N;
-    dispatch_wave<NW>(w, [&](auto wc) {
-        cbt_tiles<T, NKMAX, decltype(wc)::value>(S, cfr, Bc, rows, G * N, N, l16, g4);
-    });
+    const uint16_t *Cc = Cm + ((b * L + t0) * G + gi) * N;
+    const int64_t GN = (int64_t)G * N;
+    auto chunk16 = [&](const uint16_t *base, int row, int n0) {
+        const bool ok = row < rows && n0 < N;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + (int64_t)min(row, rows - 1) * GN +
+                                                          min(n0, N - 8));
+        return ok ? v : u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 cfr[2][NKMAX];
     if constexpr (kCinLds) {
-        // each wave parks its own C fragments in LDS (read back per head)
+        constexpr int CCH = 4 * NKMAX;                   // 16-byte chunks per C row
+        constexpr int CPT = T * CCH / NTHR;              // per thread
+        u32x4 cv[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int u = tid + k * NTHR;
+            cv[k] = chunk16(Cc, u / CCH, 8 * (u % CCH));
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int u = tid + k * NTHR;
+            const int row = u / CCH, ch = u % CCH;
+            *reinterpret_cast<u32x4 *>(ct + row * Lds::CRS + ((ch ^ (row & 15)) << 4)) = cv[k];
+        }
+    } else {
+        // lane holds C[t0 + 16 I + l16][32 ks + 8 g4 .. +7]
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
             for (int ks = 0; ks < NKMAX; ++ks)
-                *reinterpret_cast<u32x4 *>(ct + (16 * (ii ? I1 : I0) + l16) * Lds::CRS +
-                                           (((4 * ks + g4) ^ l16) << 4)) = cfr[ii][ks];
+                cfr[ii][ks] = chunk16(Cc, 16 * (ii ? I1 : I0) + l16, 32 * ks + 8 * g4);
     }
+    floatx4 S[NSLOT];
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k) S[k] = zero4();
+    static_for<Lds::NPIECE>([&](auto pcc) {
+        constexpr int PC = decltype(pcc)::value;
+        constexpr int KSP = Lds::KSP;
+        constexpr int BCH = 4 * KSP;                     // 16-byte chunks per staged B row
+        constexpr int BPT = T * BCH / NTHR;              // per thread
+        constexpr int SWM = (BCH >= 16 ? 16 : BCH) - 1;
+        if constexpr (PC > 0) __syncthreads();           // previous piece consumed
+        u32x4 bv[BPT];
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int u = tid + k * NTHR;
+            bv[k] = chunk16(Bc, u / BCH, 8 * (BCH * PC + u % BCH));
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int u = tid + k * NTHR;
+            const int row = u / BCH, ch = u % BCH;
+            *reinterpret_cast<u32x4 *>(lds + row * (16 * BCH) + ((ch ^ (row & SWM)) << 4)) = bv[k];
+        }
+        __syncthreads();
+        dispatch_wave<NW>(w, [&](auto wc) {
+            cbt_piece<T, NKMAX, KSP, PC, kCinLds, Lds::CRS, decltype(wc)::value>(
+                S, cfr, lds + l16 * (16 * BCH), ct + l16 * Lds::CRS, l16, g4);
+        });
+    });
+    __syncthreads();  // the B rows are overwritten by the first head's staging
 
     // ---------------- heads -------------------------------------------------
     for (int h = h_begin; h < h_end; ++h) {
@@ -580,9 +645,9 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                                       ct + id.l16 * Lds::CRS,
                                       H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N,
                                       tb,
-                                      y + ((b * L + t0) * NH + h) * P,
-                                      (int64_t)NH * P,
-                                      rows,
+                                      buffer_rsrc(y + ((b * L + t0) * NH + h) * P,
+                                                  (uint32_t)(((rows - 1) * NH * P + P) * sizeof(OutT))),
+                                      NH * P,
                                       N,
                                       (Dv != nullptr) ? Dv[h] : 0.f,
                                       id.l16,
@@ -775,6 +840,9 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 }
             }
         }
+        const int rows = (int)min<int64_t>(T, L - t0);
+        const __amdgpu_buffer_rsrc_t yr = buffer_rsrc(
+            y + ((b * L + t0) * NH + h) * P, (uint32_t)(((rows - 1) * NH * P + P) * sizeof(OutT)));
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             const int I = ii ? I1h : I0h;
@@ -784,9 +852,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * I + 4 * id.g4 + r;
-                    const int64_t row = t0 + i;
-                    if (full || row < L)
-                        store_out(&y[((b * L + row) * NH + h) * P + p], acc[ii][pt][r] + Dh * xs[i * LDP + p]);
+                    store_out<OutT>(yr, (i * NH * P + p) * (int)sizeof(OutT),
+                                    acc[ii][pt][r] + Dh * xs[i * LDP + p]);
                 }
             }
         }

@@ -75,6 +75,8 @@ ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
         return SSD_ERROR_UNSUPPORTED;
     if (q.nheads > kMaxI32 || q.nchunks > kMaxI32 || q.ngroups > kMaxI32 || q.batch > 65535)
         return SSD_ERROR_UNSUPPORTED;
+    // The chunk output stage addresses one chunk's y rows with 32-bit byte offsets.
+    if (q.chunk * q.nheads * q.headdim * 4 > kMaxI32) return SSD_ERROR_UNSUPPORTED;
     // Launch geometry limits (work-items per grid dimension < 2^32).
     const int64_t tiles = q.batch * q.nchunks * q.ngroups * q.heads_per_group;  // upper bound on blocks
     if (tiles > ((int64_t)1 << 31) / 512) return SSD_ERROR_UNSUPPORTED;

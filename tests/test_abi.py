@@ -110,6 +110,14 @@ def test_unsupported_sizes(lib, bad):
     assert lib.ssd_chunk_scan_fwd_workspace_layout(ctypes.byref(shape(**bad)), 256, ctypes.byref(lay)) == 2
 
 
+def test_y_chunk_offsets_must_fit_32_bits(lib):
+    # one chunk's y rows of a head are addressed with 32-bit byte offsets
+    # 256 x 16384 x 128 x 4 bytes = 2^31: one past the limit; half the chunk fits
+    assert ssd.workspace_size(shape(nheads=8192, ngroups=1, headdim=128, seqlen=300), 256) > 0
+    assert ssd.workspace_size(shape(nheads=16384, ngroups=1, headdim=128, seqlen=300), 256) == 0
+    assert ssd.workspace_size(shape(nheads=16384, ngroups=1, headdim=128, seqlen=300), 128) > 0
+
+
 def test_unsupported_chunk(lib):
     for T in (0, 32, 100, 512):
         assert ssd.workspace_size(shape(), T) == 0
