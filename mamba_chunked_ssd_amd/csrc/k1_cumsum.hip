@@ -7,26 +7,26 @@
 // and stored.  It is kept in base-2 units (G2 = log2(e) G) so that the later
 // stages use the native exp2.
 //
-// Design for gfx950: one block per (chunk, 16-head tile, batch).  The block
-// stages the chunk's dt tile [T tokens x 16 heads] in LDS (the token-major
-// input makes a per-head read strided), then each wave scans one head's chunk:
-// every lane sums T/64 consecutive tokens serially, the 64 lane totals are
-// scanned with wave shuffles, and each lane adds its exclusive prefix.  The
-// sum runs in fp64 and is stored as two floats, G2 = hi + lo: within a chunk
-// |G2| can reach thousands while the later stages exponentiate differences
-// G2_i - G2_j of nearby tokens, and (hi_i - hi_j) + (lo_i - lo_j) keeps those
-// differences accurate to fp32 relative precision instead of to ulp(|G2|).
-// Outputs are head-major (batch, nheads, padded_len), so each (head, chunk)
-// is one contiguous run of T floats for the later stages; dt is also written
-// there widened to fp32.  Tokens past seqlen are treated as dt = 0: G2 stays
-// flat and DT is 0.
+// Design for gfx950: one wave per (batch, chunk, head), four heads per block,
+// so a layer launches batch x nchunks x nheads / 4 blocks (hundreds) rather
+// than one block per 16 heads.  Every lane sums T/64 consecutive tokens
+// serially, the 64 lane totals are scanned with wave shuffles, and each lane
+// adds its exclusive prefix.  The sum runs in fp64 and is stored as two
+// floats, G2 = hi + lo: within a chunk |G2| can reach thousands while the
+// later stages exponentiate differences G2_i - G2_j of nearby tokens, and
+// (hi_i - hi_j) + (lo_i - lo_j) keeps those differences accurate to fp32
+// relative precision instead of to ulp(|G2|).  Outputs are head-major
+// (batch, nheads, padded_len), so each (head, chunk) is one contiguous run of
+// T floats for the later stages, written by each lane as one vector of its
+// T/64 tokens; dt is also written there widened to fp32.  Tokens past seqlen
+// are treated as dt = 0: G2 stays flat and DT is 0.
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
 namespace ssd {
 namespace {
 
-constexpr int kHeadTile = 16;
+constexpr int kHeadsPerBlock = 4;
 
 template <typename Tin>
 __device__ __forceinline__ float load_dt(const Tin *p);
@@ -35,72 +35,79 @@ __device__ __forceinline__ float load_dt<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load_dt<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
+template <int E>
+struct VecF;
+template <>
+struct VecF<1> { typedef float type; };
+template <>
+struct VecF<2> { typedef floatx2 type; };
+template <>
+struct VecF<4> { typedef floatx4 type; };
+
+template <int E>
+__device__ __forceinline__ void store_vec(float *p, const float (&v)[E]) {
+    typename VecF<E>::type t;
+    if constexpr (E == 1) {
+        t = v[0];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) t[e] = v[e];
+    }
+    *reinterpret_cast<typename VecF<E>::type *>(p) = t;
+}
+
 template <typename Tin, int T>
-__global__ __launch_bounds__(256) void k1_cumsum(const Tin *__restrict__ dt,
-                                                 const float *__restrict__ A,
-                                                 float *__restrict__ G2hi, float *__restrict__ G2lo,
-                                                 float *__restrict__ DT, int64_t seqlen, int nheads,
-                                                 int64_t Lp) {
+__global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
+    const Tin *__restrict__ dt, const float *__restrict__ A, float *__restrict__ G2hi,
+    float *__restrict__ G2lo, float *__restrict__ DT, int64_t seqlen, int nheads, int64_t Lp) {
     constexpr int E = T / 64;  // tokens per lane
-    __shared__ float s_dt[kHeadTile][T + 1];
-
     const int c = blockIdx.x;
-    const int h0 = blockIdx.y * kHeadTile;
+    const int h = blockIdx.y * kHeadsPerBlock + (threadIdx.x >> 6);
     const int64_t b = blockIdx.z;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    if (h >= nheads) return;  // wave-uniform; no barrier follows
 
-    // Stage dt[b, cT + t, h0 + j] -> s_dt[j][t]; consecutive threads read
-    // consecutive heads of one token.
-    for (int idx = tid; idx < T * kHeadTile; idx += 256) {
-        const int t = idx / kHeadTile, j = idx % kHeadTile;
-        const int64_t tok = (int64_t)c * T + t;
-        float v = 0.f;
-        if (tok < seqlen && h0 + j < nheads) v = load_dt(dt + (b * seqlen + tok) * nheads + h0 + j);
-        s_dt[j][t] = v;
+    const double a2 = (double)A[h] * 1.4426950408889634;  // log2(e)
+    const int64_t t0 = (int64_t)c * T + lane * E;
+    float d[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        d[e] = (t0 + e < seqlen) ? load_dt(dt + (b * seqlen + t0 + e) * nheads + h) : 0.f;
+    double run[E];
+    double tot = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        tot += a2 * (double)d[e];
+        run[e] = tot;
     }
-    __syncthreads();
-
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int j = wave; j < kHeadTile; j += 4) {
-        const int h = h0 + j;
-        if (h >= nheads) break;  // wave-uniform
-        const double a2 = (double)A[h] * 1.4426950408889634;  // log2(e)
-        float d[E];
-        double run[E];
-        double tot = 0.0;
+    // Inclusive scan of the lane totals across the wave.
+    double inc = tot;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            d[e] = s_dt[j][lane * E + e];
-            tot += a2 * (double)d[e];
-            run[e] = tot;
-        }
-        // Inclusive scan of the lane totals across the wave.
-        double inc = tot;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double up = __shfl_up(inc, off, 64);
-            if (lane >= off) inc += up;
-        }
-        const double excl = inc - tot;
-        const int64_t base = (b * nheads + h) * Lp + (int64_t)c * T + lane * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const double g = excl + run[e];
-            const float hi = (float)g;
-            G2hi[base + e] = hi;
-            G2lo[base + e] = (float)(g - (double)hi);
-            DT[base + e] = d[e];
-        }
+    for (int off = 1; off < 64; off <<= 1) {
+        const double up = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += up;
     }
+    const double excl = inc - tot;
+    float hi[E], lo[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const double g = excl + run[e];
+        hi[e] = (float)g;
+        lo[e] = (float)(g - (double)hi[e]);
+    }
+    const int64_t base = (b * nheads + h) * Lp + t0;
+    store_vec<E>(G2hi + base, hi);
+    store_vec<E>(G2lo + base, lo);
+    store_vec<E>(DT + base, d);
 }
 
 template <typename Tin, int T>
 hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
                     hipStream_t stream) {
-    dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadTile - 1) / kHeadTile),
+    dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadsPerBlock - 1) / kHeadsPerBlock),
               (unsigned)p.batch);
-    hipLaunchKernelGGL((k1_cumsum<Tin, T>), grid, dim3(256), 0, stream, dt, A, G2.hi, G2.lo, DT,
-                       p.seqlen, (int)p.nheads, p.padded_len);
+    hipLaunchKernelGGL((k1_cumsum<Tin, T>), grid, dim3(64 * kHeadsPerBlock), 0, stream, dt, A,
+                       G2.hi, G2.lo, DT, p.seqlen, (int)p.nheads, p.padded_len);
     return hipGetLastError();
 }
 

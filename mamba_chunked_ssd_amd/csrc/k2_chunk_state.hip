@@ -20,8 +20,9 @@
 //    through LDS: each thread loads an 8-token x 8-column tile with 16-byte
 //    global loads, transposes it in registers and writes 16-byte rows of the
 //    transposed tile.  The 16-byte chunks of each LDS row are XOR-swizzled by
-//    (row ^ row >> 3) & 7, which makes both those writes and the MFMA operand
-//    reads (8 rows x 16 B per LDS pass) bank-conflict free.  B^T is staged once
+//    (row ^ row >> 3) & 15 (& 7 when a row has only 8 chunks), which makes
+//    both those writes and the MFMA operand reads bank-conflict free (measured
+//    with the LDS bank-conflict counter on gfx950).  B^T is staged once
 //    per block and each wave keeps its B fragments in registers for all of
 //    the block's heads.  w_t x_t is fp32-valued; it is split into a hi and a lo
 //    bf16 (hi + lo keeps ~16 significant bits) and both halves are multiplied
@@ -41,13 +42,12 @@
 namespace ssd {
 namespace {
 
-// 16-byte-chunk swizzle of a transposed bf16 tile row.
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
-
-// byte offset of 16-byte chunk `ch` of row `row` in a [rows][T] bf16 tile
+// byte offset of 16-byte chunk `ch` of row `row` in a [rows][T] bf16 tile;
+// chunks are XOR-swizzled within each row
 template <int T>
 __device__ __forceinline__ int tr_off(int row, int ch) {
-    return row * (T * 2) + ((ch ^ swz8(row)) << 4);
+    constexpr int M = (T / 8 >= 16) ? 15 : 7;  // T / 8 chunks per row
+    return row * (T * 2) + ((ch ^ ((row ^ (row >> 3)) & M)) << 4);
 }
 
 // Transpose an 8x8 tile of bf16 held as 8 rows of 4 dwords (row r holds
@@ -145,35 +145,47 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
     const int po = u % PO, to = u / PO;
     const bool has_unit = u < units;
     const bool wave_busy = 32 * w < N;  // waves past dstate only stage x
-    auto load_x = [&](int h, u32x4 (&rows)[8]) {
+    // The unit's x rows and its 8 tokens' cumsum / dt values, loaded one head
+    // ahead through per-head buffer resources (rows past seqlen read as 0).
+    struct Pre {
+        u32x4 rows[8];
+        floatx4 gh[2], gl[2], dd[2];
+        float lh, ll;
+    };
+    const int64_t rows_valid = min<int64_t>(T, L - t0);
+    const uint32_t x_bytes = (uint32_t)(((rows_valid - 1) * NH * P + P) * 2);
+    auto load_x = [&](int h, Pre &pre) {
+        const auto xres = buffer_rsrc(x + ((b * L + t0) * NH + h) * P, x_bytes);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int64_t tok = t0 + to * 8 + r;
-            rows[r] = u32x4{0u, 0u, 0u, 0u};
-            if (has_unit && tok < L)
-                rows[r] = *reinterpret_cast<const u32x4 *>(x + ((b * L + tok) * NH + h) * P + po * 8);
+            pre.rows[r] = u32x4{0u, 0u, 0u, 0u};
+            if (has_unit) pre.rows[r] = buffer_load_x4(xres, ((to * 8 + r) * NH * P + po * 8) * 2);
         }
+        const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
+        const auto gh = buffer_rsrc(G2hi + hoff, T * 4), gl = buffer_rsrc(G2lo + hoff, T * 4);
+        const auto dd = buffer_rsrc(DT + hoff, T * 4);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            pre.gh[q] = __builtin_bit_cast(floatx4, buffer_load_x4(gh, (to * 8 + 4 * q) * 4));
+            pre.gl[q] = __builtin_bit_cast(floatx4, buffer_load_x4(gl, (to * 8 + 4 * q) * 4));
+            pre.dd[q] = __builtin_bit_cast(floatx4, buffer_load_x4(dd, (to * 8 + 4 * q) * 4));
+        }
+        pre.lh = buffer_load_f32(gh, (T - 1) * 4);
+        pre.ll = buffer_load_f32(gl, (T - 1) * 4);
     };
     // Scale by w_t = exp2(G2_last - G2_t) dt_t (G2 differences formed from the
     // hi/lo pair), split into hi/lo bf16 and
     // write the unit transposed into xhi / xlo.
-    auto store_x = [&](int h, const u32x4 (&rows)[8]) {
+    auto store_x = [&](const Pre &pre) {
         if (!has_unit) return;
-        const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
-        const float *gh = G2hi + hoff;
-        const float *gl = G2lo + hoff;
-        const float *dd = DT + hoff;
-        const float lh = gh[T - 1], ll = gl[T - 1];
+        const u32x4 (&rows)[8] = pre.rows;
+        const float lh = pre.lh, ll = pre.ll;
         float wt[8];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const float4 a = *reinterpret_cast<const float4 *>(gh + to * 8 + 4 * q);
-            const float4 l = *reinterpret_cast<const float4 *>(gl + to * 8 + 4 * q);
-            const float4 d = *reinterpret_cast<const float4 *>(dd + to * 8 + 4 * q);
-            wt[4 * q + 0] = fast_exp2((lh - a.x) + (ll - l.x)) * d.x;
-            wt[4 * q + 1] = fast_exp2((lh - a.y) + (ll - l.y)) * d.y;
-            wt[4 * q + 2] = fast_exp2((lh - a.z) + (ll - l.z)) * d.z;
-            wt[4 * q + 3] = fast_exp2((lh - a.w) + (ll - l.w)) * d.w;
+            const floatx4 a = pre.gh[q], l = pre.gl[q], d = pre.dd[q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wt[4 * q + i] = fast_exp2((lh - a[i]) + (ll - l[i])) * d[i];
         }
         u32x4 hi[8], lo[8];
 #pragma unroll
@@ -194,11 +206,11 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
         for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4 *>(xlo + tr_off<T>(po * 8 + q, to)) = t8[q];
     };
 
-    u32x4 pre[8];
+    Pre pre;
     if (h_begin < h_end) load_x(h_begin, pre);
 
     for (int h = h_begin; h < h_end; ++h) {
-        store_x(h, pre);
+        store_x(pre);
         __syncthreads();
         if (h + 1 < h_end) load_x(h + 1, pre);
         if (!wave_busy) {

@@ -65,17 +65,18 @@ constexpr size_t kLdsBytes = 160 * 1024;
 // is always T/16 + 2 and a pair (2q, 2q + 1) never straddles the two tiles.
 __device__ __forceinline__ int slot_base1(int I0) { return (I0 + 2) & ~1; }
 
-// Per-head tables in LDS (T floats each, and T/16 x T for the row factors):
+// Per-head tables in LDS (T floats each):
 //   gh[t] + gl[t] = G2_t (hi/lo),  dt[t],  e2[t] = exp2(G2_t),
-//   cf[t] = exp2(G2_e(t) - G2_t) dt_t,  e(t) = last token of t's 16-tile,
-//   rf[J * T + i] = exp2(G2_i - G2_e(J)) for i > e(J) (else 0).
+//   cf[t] = exp2(G2_e(t) - G2_t) dt_t,  e(t) = last token of t's 16-tile.
 template <int T>
 struct Tables {
-    float *gh, *gl, *dt, *e2, *cf, *rf;
-    static constexpr size_t bytes = (size_t)5 * T * 4 + (size_t)(T / 16) * T * 4;
+    float *gh, *gl, *dt, *e2, *cf;
+    static constexpr size_t bytes = (size_t)5 * T * 4;
     __device__ Tables(float *base)
-        : gh(base), gl(base + T), dt(base + 2 * T), e2(base + 3 * T), cf(base + 4 * T),
-          rf(base + 5 * T) {}
+        : gh(base), gl(base + T), dt(base + 2 * T), e2(base + 3 * T), cf(base + 4 * T) {}
+    // G2 at the last token before row tile I (G2 before the chunk is 0)
+    __device__ float before_hi(int I) const { return I > 0 ? gh[16 * I - 1] : 0.f; }
+    __device__ float before_lo(int I) const { return I > 0 ? gl[16 * I - 1] : 0.f; }
 };
 
 // Per-token part of the tables (thread t < T), from its G2 pair, the pair at
@@ -90,35 +91,38 @@ __device__ __forceinline__ void token_tables(const Tables<T> &tb, int t, float g
     tb.cf[t] = fast_exp2((geh - gh) + (gel - gl)) * d;
 }
 
-// Row-factor part (after token_tables is visible): thread tid of nthr covers
-// rows i = tid % T and tiles J = (tid / T), (tid / T) + nthr / T, ...
+// Off-diagonal decay weights.  For row i in tile I and column j in tile J < I,
+//     exp2(G2_i - G2_j) dt_j = rs(i) * m(I, J) * cf(j),
+//     rs(i)   = exp2(G2_i - G2_{16 I - 1})        (per row, one per lane and row tile)
+//     m(I, J) = exp2(G2_{16 I - 1} - G2_{16 J + 15})  (per tile pair, wave-uniform)
+//     cf(j)   = exp2(G2_{16 J + 15} - G2_j) dt_j     (per column, tabulated)
+// Every exponent is <= 0 (G2 never increases), so no factor can overflow, and
+// a factor that underflows bounds a product that is at least as small.
 template <int T>
-__device__ __forceinline__ void row_factor_table(const Tables<T> &tb, int tid, int nthr) {
-    const int i = tid % T;
-    const float ih = tb.gh[i], il = tb.gl[i];
-    for (int J = tid / T; J < T / 16; J += nthr / T) {
-        const int e = 16 * J + 15;
-        tb.rf[J * T + i] = (i > e) ? fast_exp2((ih - tb.gh[e]) + (il - tb.gl[e])) : 0.f;
-    }
+__device__ __forceinline__ float tile_pair_factor(const Tables<T> &tb, int I, int J) {
+    return fast_exp2((tb.before_hi(I) - tb.gh[16 * J + 15]) + (tb.before_lo(I) - tb.gl[16 * J + 15]));
+}
+template <int T>
+__device__ __forceinline__ float row_factor(const Tables<T> &tb, int I, float gih, float gil) {
+    return fast_exp2((gih - tb.before_hi(I)) + (gil - tb.before_lo(I)));
 }
 
 // Decay-and-dt weighted values of one S tile slot for this lane: row
-// i = 16 I + l16, columns j = 16 J + 4 g4 + r.  On the diagonal tile the
-// exponent is the exact difference G2_i - G2_j (0 for j = i) and the mask is
-// a select taken before exp2.
+// i = 16 I + l16, columns j = 16 J + 4 g4 + r; rm = rs(i) m(I, J) when J < I.
+// On the diagonal tile the exponent is the exact difference G2_i - G2_j (0
+// for j = i) and the mask is a select taken before exp2.
 template <int T>
 __device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, int l16, int g4,
-                                            float gih, float gil, const Tables<T> &tb,
+                                            float gih, float gil, float rm, const Tables<T> &tb,
                                             float (&v)[4]) {
     if (J > I) {
         v[0] = v[1] = v[2] = v[3] = 0.f;
     } else if (J < I) {
-        const float rf = tb.rf[J * T + 16 * I + l16];
         const float4 cf = *reinterpret_cast<const float4 *>(tb.cf + 16 * J + 4 * g4);
-        v[0] = s[0] * (rf * cf.x);
-        v[1] = s[1] * (rf * cf.y);
-        v[2] = s[2] * (rf * cf.z);
-        v[3] = s[3] * (rf * cf.w);
+        v[0] = s[0] * (rm * cf.x);
+        v[1] = s[1] * (rm * cf.y);
+        v[2] = s[2] * (rm * cf.z);
+        v[3] = s[3] * (rm * cf.w);
     } else {
         const float4 jh = *reinterpret_cast<const float4 *>(tb.gh + 16 * J + 4 * g4);
         const float4 jl = *reinterpret_cast<const float4 *>(tb.gl + 16 * J + 4 * g4);
@@ -138,10 +142,6 @@ __device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, int 
 // y is written with raw buffer stores: the resource covers a chunk's rows of
 // one head up to the last valid row, so the hardware drops the stores of rows
 // past the sequence end, and the row offsets stay 32-bit.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 template <typename OutT>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off, float v);
 template <>
@@ -177,7 +177,7 @@ __device__ __forceinline__ LaneIds opaque_lane_ids(int tid) {
 // LDS of the bf16 kernel: x^T tile, the h hi/lo tiles when they fit, tables.
 template <int T, int P, int NKMAX>
 struct Bf16Lds {
-    static constexpr int XRS = 2 * T + 16;           // x^T row stride (bytes)
+    static constexpr int XRS = 2 * T + 32;           // x^T row stride (bytes)
     static constexpr int HRS = 2 * NKMAX * 32 + 32;  // h / C row stride (bytes)
     static constexpr size_t x = (size_t)P * XRS;
     static constexpr size_t h = (size_t)2 * P * HRS;
@@ -240,16 +240,15 @@ struct WaveTiles {
 // tile_values with the tile relation known at compile time
 template <int T, int J, int I>
 __device__ __forceinline__ void tile_values_ct(const floatx4 &s, int l16, int g4, float gih, float gil,
-                                               const Tables<T> &tb, float (&v)[4]) {
+                                               float rm, const Tables<T> &tb, float (&v)[4]) {
     if constexpr (J > I) {
         v[0] = v[1] = v[2] = v[3] = 0.f;
     } else if constexpr (J < I) {
-        const float rf = tb.rf[J * T + 16 * I + l16];
         const float4 cf = *reinterpret_cast<const float4 *>(tb.cf + 16 * J + 4 * g4);
-        v[0] = s[0] * (rf * cf.x);
-        v[1] = s[1] * (rf * cf.y);
-        v[2] = s[2] * (rf * cf.z);
-        v[3] = s[3] * (rf * cf.w);
+        v[0] = s[0] * (rm * cf.x);
+        v[1] = s[1] * (rm * cf.y);
+        v[2] = s[2] * (rm * cf.z);
+        v[3] = s[3] * (rm * cf.w);
     } else {
         const float4 jh = *reinterpret_cast<const float4 *>(tb.gh + 16 * J + 4 * g4);
         const float4 jl = *reinterpret_cast<const float4 *>(tb.gl + 16 * J + 4 * g4);
@@ -303,7 +302,7 @@ __device__ __forceinline__ void cbt_piece(floatx4 (&S)[T / 16 + 2], const u32x4 
 // Everything one wave computes for one head.
 template <int T, int P, int NKMAX, typename OutT>
 struct HeadCtx {
-    const unsigned char *xl;  // x^T + l16 * XRS + 8 g4
+    const unsigned char *xl;  // x^T + l16 * XRS + 16 g4
     const unsigned char *hl;  // h hi tile + l16 * HRS + 16 g4 (when staged in LDS)
     const unsigned char *cl;  // C tile + l16 * CRS (when staged in LDS)
     const float *hp;          // h_c in global memory (when not staged)
@@ -382,12 +381,24 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
             acc[ii][pt][3] *= e.w;
         }
     }
+    // tile-pair factors m(I, J): lane k evaluates the one of slot k, which is
+    // then read back as a wave-uniform value
+    float mk;
+    {
+        const int k = l16 + 16 * g4;
+        const int Ik = k < WT::base1 ? I0 : I1;
+        const int Jk = k < WT::base1 ? k : k - WT::base1;
+        const bool off = k < WT::NSLOT && Jk < Ik;
+        const float m = tile_pair_factor(cx.tb, off ? Ik : 1, off ? Jk : 0);  // in-range reads
+        mk = off ? m : 0.f;
+    }
     // intra-chunk term: slot pairs (J, J + 1) of one row tile, K = 32
     static_for<2>([&](auto iic) {
         constexpr int ii = decltype(iic)::value;
         constexpr int I = ii ? I1 : I0;
         constexpr int kb = ii ? WT::base1 : 0, kend = ii ? WT::NSLOT : WT::base1;
         const float gih = cx.tb.gh[16 * I + l16], gil = cx.tb.gl[16 * I + l16];
+        const float rs = row_factor(cx.tb, I, gih, gil);
         static_for<WT::NSLOT / 2>([&](auto qc) {
             constexpr int k0 = 2 * decltype(qc)::value;
             if constexpr (k0 >= kb && k0 < kend) {
@@ -395,19 +406,19 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
                 // one (register pressure at two waves per SIMD)
                 __builtin_amdgcn_sched_barrier(0);
                 constexpr int Ja = k0 - kb, Jb = Ja + 1;
-                constexpr int JbR = Jb < NT16 ? Jb : NT16 - 1;  // padded tile: weights are 0
+                const float rma = rs * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0));
+                const float rmb = rs * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0 + 1));
                 float va[4], vb[4];
-                tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, cx.tb, va);
-                tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, cx.tb, vb);
+                tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, rma, cx.tb, va);
+                tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, rmb, cx.tb, vb);
                 const HiLo p0 = split_bf16(va[0], va[1]), p1 = split_bf16(va[2], va[3]);
                 const HiLo p2 = split_bf16(vb[0], vb[1]), p3 = split_bf16(vb[2], vb[3]);
                 const u32x4 ahi = {p0.hi, p1.hi, p2.hi, p3.hi};
                 const u32x4 alo = {p0.lo, p1.lo, p2.lo, p3.lo};
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    u32x4 bop;
-                    bop.xy = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * Ja);
-                    bop.zw = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * JbR);
+                    // 16-byte chunk (Ja / 2, g4): tokens 16 Ja + 4 g4 .. +3, then 16 Jb + 4 g4 .. +3
+                    const u32x4 bop = *reinterpret_cast<const u32x4 *>(cx.xl + pt * 16 * XRS + 32 * Ja);
                     acc[ii][pt] = mfma_bf16(ahi, bop, acc[ii][pt]);
                     acc[ii][pt] = mfma_bf16(alo, bop, acc[ii][pt]);
                 }
@@ -423,7 +434,7 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
         const int I = ii ? I1 : I0;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const u32x2 xv2 = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * I);
+            const u32x2 xv2 = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * (I & ~1) + 8 * (I & 1));
             const float xv[4] = {bf16lo(xv2[0]), bf16hi(xv2[0]), bf16lo(xv2[1]), bf16hi(xv2[1])};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -539,7 +550,9 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                     const uint32_t s = sel_half(q);
                     const u32x2 v = {__builtin_amdgcn_perm(xr[ps][1][q >> 1], xr[ps][0][q >> 1], s),
                                      __builtin_amdgcn_perm(xr[ps][3][q >> 1], xr[ps][2][q >> 1], s)};
-                    *reinterpret_cast<u32x2 *>(xt + (8 * po + q) * XRS + 8 * tq) = v;
+                    // tokens 4 tq .. +3 (tile J = tq / 4, quad tq % 4) of column 8 po + q
+                    *reinterpret_cast<u32x2 *>(xt + (8 * po + q) * XRS + 32 * ((tq >> 2) & ~1) +
+                                               16 * (tq & 3) + 8 * ((tq >> 2) & 1)) = v;
                 }
             }
         }
@@ -636,11 +649,9 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     for (int h = h_begin; h < h_end; ++h) {
         stage_head();
         __syncthreads();
-        row_factor_table(tb, tid, NTHR);
         if (h + 1 < h_end) load_head(h + 1);
-        __syncthreads();
         const LaneIds id = opaque_lane_ids(tid);
-        HeadCtx<T, P, NKMAX, OutT> cx{xt + id.l16 * XRS + 8 * id.g4,
+        HeadCtx<T, P, NKMAX, OutT> cx{xt + id.l16 * XRS + 16 * id.g4,
                                       hhi + id.l16 * HRS + 16 * id.g4,
                                       ct + id.l16 * Lds::CRS,
                                       H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N,
@@ -775,9 +786,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     for (int h = h_begin; h < h_end; ++h) {
         stage_head();
         __syncthreads();
-        row_factor_table(tb, tid, NTHR);
         if (h + 1 < h_end) load_head(h + 1);
-        __syncthreads();
         const float Dh = (Dv != nullptr) ? Dv[h] : 0.f;
         const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
         const LaneIds id = opaque_lane_ids(tid);
@@ -825,12 +834,14 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
             const int I = ii ? I1h : I0h;
             const int kb = ii ? base1h : 0, kend = ii ? NSLOT : base1h;
             const float gih = tb.gh[16 * I + id.l16], gil = tb.gl[16 * I + id.l16];
+            const float rs = row_factor(tb, I, gih, gil);
 #pragma unroll
             for (int k = 0; k < NSLOT; ++k) {
                 const int J = k - kb;
                 if (k < kb || k >= kend || J > I) continue;  // wave-uniform
+                const float rm = J < I ? rs * tile_pair_factor(tb, I, J) : 0.f;
                 float v[4];
-                tile_values<T>(S[k], J, I, id.l16, id.g4, gih, gil, tb, v);
+                tile_values<T>(S[k], J, I, id.l16, id.g4, gih, gil, rm, tb, v);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float *xrow = xs + (16 * J + 4 * id.g4 + r) * LDP + id.l16;

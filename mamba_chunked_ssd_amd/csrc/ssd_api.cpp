@@ -82,7 +82,7 @@ ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
     if (tiles > ((int64_t)1 << 31) / 512) return SSD_ERROR_UNSUPPORTED;
     const int64_t k3_threads = q.batch * q.nheads * q.headdim * q.dstate / 4;
     if (k3_threads > ((int64_t)1 << 31)) return SSD_ERROR_UNSUPPORTED;
-    if ((q.nheads + 15) / 16 > 65535) return SSD_ERROR_UNSUPPORTED;
+    if ((q.nheads + 3) / 4 > 65535) return SSD_ERROR_UNSUPPORTED;  // cumsum grid.y
     *p = q;
     return SSD_OK;
 }

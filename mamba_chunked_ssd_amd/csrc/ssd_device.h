@@ -67,4 +67,18 @@ __device__ __forceinline__ floatx4 mfma_f32(float a, float b, const floatx4 &c) 
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Raw buffer access (gfx9 resource word 3 = 0x00020000: 32-bit data format,
+// no swizzle, byte-granular range).  Loads past `bytes` read 0 and stores past
+// it are dropped; offsets are 32-bit byte offsets from `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load_x4(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 }  // namespace ssd
