@@ -208,15 +208,16 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps; 5 events per step around the stages
-    evs = [[hip.event() for _ in range(5)] for _ in range(a.steps)]
+    # timed region: K back-to-back steps; a (start, stop) event pair per stage,
+    # recorded by each kernel's own dispatch
+    evs = [[hip.event() for _ in range(8)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per_stage = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(4)] for e in evs])
+    per_stage = np.array([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(4)] for e in evs])
     for e in evs:
         for ev in e:
             hip.destroy(ev)
@@ -282,10 +283,10 @@ def main(argv=None):
         cold = []
         for _ in range(min(a.steps, 20)):
             flush.fill_(1.0)
-            e = [hip.event() for _ in range(5)]
+            e = [hip.event() for _ in range(8)]
             step(e)
             torch.cuda.synchronize()
-            cold.append([hip.elapsed_ms(e[j], e[j + 1]) for j in range(4)])
+            cold.append([hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(4)])
             for ev in e:
                 hip.destroy(ev)
         cold = np.array(cold).mean(axis=0)

@@ -91,13 +91,16 @@ typedef struct {
  *       sum grows within a chunk; positions past seqlen are padded with dt = 0
  *       and so stay flat.
  *   DT  fp32 (batch, nheads, Lp): dt widened to fp32, head-major, zero padded.
+ *   W   fp32 (batch, nheads, Lp): exp(G_last - G_t) dt_t, the weight with which
+ *       token t enters its chunk's state (G_last: G at the chunk's last
+ *       token; the exponent is formed in fp64); 0 past seqlen.
  *   S   fp32 (batch, nheads, nchunks, headdim, dstate): after the call, the
  *       chunk-start states h_c (the state before the chunk's first token);
  *       with SSD_FLAG_KEEP_INTERMEDIATES, the per-chunk input states s_c
  *       (what a chunk alone adds to a zero state).
  *   H   (only with SSD_FLAG_KEEP_INTERMEDIATES) same shape as S: h_c. */
 typedef struct {
-    size_t g2_hi, g2_lo, dt, s, h, total;
+    size_t g2_hi, g2_lo, dt, w, s, h, total;
     int64_t nchunks, padded_len;
 } ssd_workspace_layout;
 
@@ -133,10 +136,12 @@ ssd_status ssd_chunk_scan_fwd(const ssd_shape *shape,
                               void *y, float *final_states,
                               void *workspace, size_t workspace_bytes, void *stream);
 
-/* Same as ssd_chunk_scan_fwd; in addition records the five hipEvent_t in
- * stage_events[0..4] on `stream` before the first kernel, between the kernels
- * and after the last, so a caller can time each stage.  stage_events must
- * point to 5 valid events. */
+/* Same as ssd_chunk_scan_fwd; in addition times every kernel: stage_events
+ * holds 8 valid hipEvent_t, a (start, stop) pair per stage in stream order
+ * (chunk cumsum, chunk state, state passing, chunk output).  Each pair is
+ * recorded by the kernel's own dispatch (hipExtLaunchKernel), so the elapsed
+ * time between them is that kernel alone.  A stage that has nothing to do
+ * (no chunks) records both of its events back to back. */
 ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape,
                                        const void *x, const void *dt, const float *A,
                                        const void *B, const void *C, const float *D,

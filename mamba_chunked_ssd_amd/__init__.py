@@ -75,6 +75,7 @@ class WorkspaceLayout(ctypes.Structure):
         ("g2_hi", ctypes.c_size_t),
         ("g2_lo", ctypes.c_size_t),
         ("dt", ctypes.c_size_t),
+        ("w", ctypes.c_size_t),
         ("s", ctypes.c_size_t),
         ("h", ctypes.c_size_t),
         ("total", ctypes.c_size_t),
@@ -188,8 +189,9 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
     default) or the input dtype.  Returns y, or (y, final_states).
     ``workspace`` (uint8 device tensor) may be passed to reuse an allocation;
     with ``keep_intermediates`` its layout is :func:`workspace_layout` of the
-    shape with the keep flag.  ``events``: 5 raw hipEvent_t handles (ints) to
-    record around the four stages (``ssd_chunk_scan_fwd_profiled``).
+    shape with the keep flag.  ``events``: 8 raw hipEvent_t handles (ints), a
+    (start, stop) pair per stage recorded by each kernel's own dispatch
+    (``ssd_chunk_scan_fwd_profiled``).
     """
     torch = _torch()
     lib = load_library()
@@ -238,7 +240,9 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
         st = lib.ssd_chunk_scan_fwd(*args)
         where = "ssd_chunk_scan_fwd"
     else:
-        ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) for e in events])
+        if len(events) != 8:
+            raise ValueError("events: a (start, stop) pair for each of the 4 stages")
+        ev = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e) for e in events])
         st = lib.ssd_chunk_scan_fwd_profiled(*args, ev)
         where = "ssd_chunk_scan_fwd_profiled"
     if st != 0:

@@ -18,8 +18,12 @@
 // relative precision instead of to ulp(|G2|).  Outputs are head-major
 // (batch, nheads, padded_len), so each (head, chunk) is one contiguous run of
 // T floats for the later stages, written by each lane as one vector of its
-// T/64 tokens; dt is also written there widened to fp32.  Tokens past seqlen
-// are treated as dt = 0: G2 stays flat and DT is 0.
+// T/64 tokens; dt is also written there widened to fp32, and so is the weight
+// with which each token enters its chunk's state (the log-space state jump of
+// the same page's section "Mamba-2 architecture"),
+//     W_t = exp2(G2_last - G2_t) dt_t ,
+// whose exponent is formed exactly in fp64 before the fp32 exp2.  Tokens past
+// seqlen are treated as dt = 0: G2 stays flat and DT, W are 0.
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
@@ -59,7 +63,8 @@ __device__ __forceinline__ void store_vec(float *p, const float (&v)[E]) {
 template <typename Tin, int T>
 __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
     const Tin *__restrict__ dt, const float *__restrict__ A, float *__restrict__ G2hi,
-    float *__restrict__ G2lo, float *__restrict__ DT, int64_t seqlen, int nheads, int64_t Lp) {
+    float *__restrict__ G2lo, float *__restrict__ DT, float *__restrict__ W, int64_t seqlen,
+    int nheads, int64_t Lp) {
     constexpr int E = T / 64;  // tokens per lane
     const int c = blockIdx.x;
     const int h = blockIdx.y * kHeadsPerBlock + (threadIdx.x >> 6);
@@ -88,36 +93,39 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
         if (lane >= off) inc += up;
     }
     const double excl = inc - tot;
-    float hi[E], lo[E];
+    const double last = __shfl(inc, 63, 64);  // G2 at the chunk's last token
+    float hi[E], lo[E], wt[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const double g = excl + run[e];
         hi[e] = (float)g;
         lo[e] = (float)(g - (double)hi[e]);
+        wt[e] = fast_exp2((float)(last - g)) * d[e];
     }
     const int64_t base = (b * nheads + h) * Lp + t0;
     store_vec<E>(G2hi + base, hi);
     store_vec<E>(G2lo + base, lo);
     store_vec<E>(DT + base, d);
+    store_vec<E>(W + base, wt);
 }
 
 template <typename Tin, int T>
 hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
-                    hipStream_t stream) {
+                    float *W, hipStream_t stream, const LaunchEvents &ev) {
     dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadsPerBlock - 1) / kHeadsPerBlock),
               (unsigned)p.batch);
-    hipLaunchKernelGGL((k1_cumsum<Tin, T>), grid, dim3(64 * kHeadsPerBlock), 0, stream, dt, A,
-                       G2.hi, G2.lo, DT, p.seqlen, (int)p.nheads, p.padded_len);
+    launch_kernel((k1_cumsum<Tin, T>), grid, dim3(64 * kHeadsPerBlock), 0, stream, ev, dt, A,
+                       G2.hi, G2.lo, DT, W, p.seqlen, (int)p.nheads, p.padded_len);
     return hipGetLastError();
 }
 
 template <typename Tin>
 hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
-                        hipStream_t stream) {
+                        float *W, hipStream_t stream, const LaunchEvents &ev) {
     switch (p.chunk) {
-        case 64: return launch_t<Tin, 64>(p, dt, A, G2, DT, stream);
-        case 128: return launch_t<Tin, 128>(p, dt, A, G2, DT, stream);
-        case 256: return launch_t<Tin, 256>(p, dt, A, G2, DT, stream);
+        case 64: return launch_t<Tin, 64>(p, dt, A, G2, DT, W, stream, ev);
+        case 128: return launch_t<Tin, 128>(p, dt, A, G2, DT, W, stream, ev);
+        case 256: return launch_t<Tin, 256>(p, dt, A, G2, DT, W, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
@@ -125,9 +133,9 @@ hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, G2Pair 
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
-                               float *DT, hipStream_t stream) {
-    if (p.bf16) return launch_dtype(p, static_cast<const uint16_t *>(dt), A, G2, DT, stream);
-    return launch_dtype(p, static_cast<const float *>(dt), A, G2, DT, stream);
+                               float *DT, float *W, hipStream_t stream, const LaunchEvents &ev) {
+    if (p.bf16) return launch_dtype(p, static_cast<const uint16_t *>(dt), A, G2, DT, W, stream, ev);
+    return launch_dtype(p, static_cast<const float *>(dt), A, G2, DT, W, stream, ev);
 }
 
 }  // namespace ssd

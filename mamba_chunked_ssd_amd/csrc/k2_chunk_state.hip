@@ -35,6 +35,8 @@
 // The next head's x tile is loaded into registers while the current head's
 // MFMAs run.  Tokens past seqlen are zero-filled (the chunk is padded).
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "ssd_device.h"
 #include "ssd_internal.h"
@@ -64,14 +66,23 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
+// compile-time loop
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---------------------------------------------------------------------------
 // bf16 path
 // ---------------------------------------------------------------------------
 template <int T, int P>
 __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const float *__restrict__ G2hi, const float *__restrict__ G2lo, const float *__restrict__ DT,
-    float *__restrict__ S, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
+    const float *__restrict__ W, float *__restrict__ S, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
     int nhb) {
     constexpr int KS = T / 32;   // k-steps of the contraction over tokens
     constexpr int PT = P / 16;   // 16-row tiles of headdim
@@ -95,6 +106,74 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
     const int h_begin = gi * HPG + hb * HB;
     const int h_end = min(h_begin + HB, (gi + 1) * HPG);
     const int64_t t0 = (int64_t)c * T;
+
+    // ---- per head: x tile -> registers (prefetched one head ahead).  The
+    //      launch gives every 8x8 (token, headdim) unit of the tile its own
+    //      thread, so one pass covers the tile.
+    const int units = TO * PO;
+    const int u = tid;
+    const int po = u % PO, to = u / PO;
+    const bool has_unit = u < units;
+    const bool wave_busy = 32 * w < N;  // waves past dstate only stage x
+    // The unit's x rows and its 8 tokens' weights, loaded one head ahead
+    // through per-head buffer resources (rows past seqlen read as 0).
+    struct Pre {
+        u32x4 rows[8];
+        floatx4 wv[2];
+    };
+    const int64_t rows_valid = min<int64_t>(T, L - t0);
+    const uint32_t x_bytes = (uint32_t)(((rows_valid - 1) * NH * P + P) * 2);
+    auto load_x = [&](int h, Pre &pre) {
+        const auto xres = buffer_rsrc(x + ((b * L + t0) * NH + h) * P, x_bytes);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            pre.rows[r] = u32x4{0u, 0u, 0u, 0u};
+            if (has_unit) pre.rows[r] = buffer_load_x4(xres, ((to * 8 + r) * NH * P + po * 8) * 2);
+        }
+        const auto wr = buffer_rsrc(W + ((int64_t)b * NH + h) * Lp + t0, T * 4);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            pre.wv[q] = __builtin_bit_cast(floatx4, buffer_load_x4(wr, (to * 8 + 4 * q) * 4));
+    };
+    // Scale by w_t, split into hi/lo bf16 and write the unit transposed into
+    // xhi / xlo.
+    auto store_x = [&](const Pre &pre) {
+        if (!has_unit) return;
+        const u32x4 (&rows)[8] = pre.rows;
+        float wt[8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wt[4 * q + i] = pre.wv[q][i];
+        // one pair of columns (dword i of every row) at a time: split, then
+        // transpose into LDS rows 8 po + 2i and 8 po + 2i + 1 of both tiles
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const HiLo s2 = split_bf16(bf16lo(rows[r][i]) * wt[r], bf16hi(rows[r][i]) * wt[r]);
+                hi[r] = s2.hi;
+                lo[r] = s2.lo;
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t sel = half ? 0x07060302u : 0x05040100u;
+                const int row = po * 8 + 2 * i + half;
+                u32x4 th, tl;
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) {
+                    th[r2] = __builtin_amdgcn_perm(hi[2 * r2 + 1], hi[2 * r2], sel);
+                    tl[r2] = __builtin_amdgcn_perm(lo[2 * r2 + 1], lo[2 * r2], sel);
+                }
+                *reinterpret_cast<u32x4 *>(xhi + tr_off<T>(row, to)) = th;
+                *reinterpret_cast<u32x4 *>(xlo + tr_off<T>(row, to)) = tl;
+            }
+        }
+    };
+
+    Pre pre;
+    if (h_begin < h_end) load_x(h_begin, pre);  // in flight during the B^T staging
 
     // ---- stage B^T for this chunk in pieces that fit the x buffers; each wave
     //      keeps its own B fragments (32 columns, all tokens) in registers.
@@ -137,80 +216,31 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
         }
     }
 
-    // ---- per head: x tile -> registers (prefetched one head ahead).  The
-    //      launch gives every 8x8 (token, headdim) unit of the tile its own
-    //      thread, so one pass covers the tile.
-    const int units = TO * PO;
-    const int u = tid;
-    const int po = u % PO, to = u / PO;
-    const bool has_unit = u < units;
-    const bool wave_busy = 32 * w < N;  // waves past dstate only stage x
-    // The unit's x rows and its 8 tokens' cumsum / dt values, loaded one head
-    // ahead through per-head buffer resources (rows past seqlen read as 0).
-    struct Pre {
-        u32x4 rows[8];
-        floatx4 gh[2], gl[2], dd[2];
-        float lh, ll;
-    };
-    const int64_t rows_valid = min<int64_t>(T, L - t0);
-    const uint32_t x_bytes = (uint32_t)(((rows_valid - 1) * NH * P + P) * 2);
-    auto load_x = [&](int h, Pre &pre) {
-        const auto xres = buffer_rsrc(x + ((b * L + t0) * NH + h) * P, x_bytes);
+
+    // A head's states are stored after the next head's staging: on this
+    // architecture one counter tracks both loads and stores, so the wait for
+    // the prefetched loads would otherwise also wait for the stores to land.
+    floatx4 accd[PT][2];  // the previous head's states
+    auto store_states = [&](int h, const auto &acc) {
+        // lane coordinates from an opaque copy of the thread index, so the
+        // store addresses are formed here rather than hoisted out of the loop
+        int tid_o = tid;
+        asm volatile("" : "+v"(tid_o));
+        const int l16 = tid_o & 15, g4 = (tid_o >> 4) & 3;
+        float *out = S + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            pre.rows[r] = u32x4{0u, 0u, 0u, 0u};
-            if (has_unit) pre.rows[r] = buffer_load_x4(xres, ((to * 8 + r) * NH * P + po * 8) * 2);
-        }
-        const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
-        const auto gh = buffer_rsrc(G2hi + hoff, T * 4), gl = buffer_rsrc(G2lo + hoff, T * 4);
-        const auto dd = buffer_rsrc(DT + hoff, T * 4);
+        for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            pre.gh[q] = __builtin_bit_cast(floatx4, buffer_load_x4(gh, (to * 8 + 4 * q) * 4));
-            pre.gl[q] = __builtin_bit_cast(floatx4, buffer_load_x4(gl, (to * 8 + 4 * q) * 4));
-            pre.dd[q] = __builtin_bit_cast(floatx4, buffer_load_x4(dd, (to * 8 + 4 * q) * 4));
-        }
-        pre.lh = buffer_load_f32(gh, (T - 1) * 4);
-        pre.ll = buffer_load_f32(gl, (T - 1) * 4);
-    };
-    // Scale by w_t = exp2(G2_last - G2_t) dt_t (G2 differences formed from the
-    // hi/lo pair), split into hi/lo bf16 and
-    // write the unit transposed into xhi / xlo.
-    auto store_x = [&](const Pre &pre) {
-        if (!has_unit) return;
-        const u32x4 (&rows)[8] = pre.rows;
-        const float lh = pre.lh, ll = pre.ll;
-        float wt[8];
+            for (int nt = 0; nt < 2; ++nt) {
+                const int n = 32 * w + 16 * nt + l16;
+                if (n < N)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const floatx4 a = pre.gh[q], l = pre.gl[q], d = pre.dd[q];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wt[4 * q + i] = fast_exp2((lh - a[i]) + (ll - l[i])) * d[i];
-        }
-        u32x4 hi[8], lo[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-            {
-                const HiLo s2 = split_bf16(bf16lo(rows[r][i]) * wt[r], bf16hi(rows[r][i]) * wt[r]);
-                hi[r][i] = s2.hi;
-                lo[r][i] = s2.lo;
+                    for (int r = 0; r < 4; ++r) out[(16 * pt + 4 * g4 + r) * N + n] = acc[pt][nt][r];
             }
-        u32x4 t8[8];
-        transpose8x8(hi, t8);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4 *>(xhi + tr_off<T>(po * 8 + q, to)) = t8[q];
-        transpose8x8(lo, t8);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4 *>(xlo + tr_off<T>(po * 8 + q, to)) = t8[q];
     };
-
-    Pre pre;
-    if (h_begin < h_end) load_x(h_begin, pre);
-
     for (int h = h_begin; h < h_end; ++h) {
         store_x(pre);
+        if (h > h_begin && wave_busy) store_states(h - 1, accd);
         __syncthreads();
         if (h + 1 < h_end) load_x(h + 1, pre);
         if (!wave_busy) {
@@ -240,16 +270,251 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
                 }
             }
         }
-        float *out = S + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
+        for (int pt = 0; pt < PT; ++pt) accd[pt][0] = acc[pt][0], accd[pt][1] = acc[pt][1];
+        __syncthreads();
+    }
+    if (h_begin < h_end && wave_busy) store_states(h_end - 1, accd);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path with producer and consumer waves
+// ---------------------------------------------------------------------------
+// When two x^T hi/lo tile pairs fit in LDS (8 P T bytes) and dstate <= 128
+// (at most 4 consumer waves, so 8 waves hold the B fragments without
+// spilling), kProducers waves
+// stage head k + 1 (x and weights loaded one head further ahead; scale, split,
+// transpose) into one buffer while ceil(N / 32) consumer waves run head k's
+// MFMAs from the other and store its states: one block barrier per head, and
+// the staging (VALU) of one head overlaps the MFMAs of the previous one on
+// every SIMD.  Consumers keep their B fragments in registers for the block's
+// heads; they never load from global memory in the head loop, and producers
+// never store to it, so neither role waits on the other's memory traffic.
+constexpr int kProducers = 4;
+
+template <int T, int P>
+struct K2WsLds {
+    static constexpr size_t buf = (size_t)2 * P * T * 2;  // hi + lo tiles of one head
+    static constexpr size_t total = 2 * buf;
+    static constexpr bool fits = total <= 160 * 1024;
+};
+
+template <int T, int P, int NCW>
+__global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_ws(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, const float *__restrict__ W,
+    float *__restrict__ S, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
+    int nhb) {
+    constexpr int KS = T / 32;   // k-steps of the contraction over tokens
+    constexpr int PT = P / 16;   // 16-row tiles of headdim
+    constexpr int TO = T / 8;    // token octets
+    constexpr int PO = P / 8;    // headdim octets
+    constexpr int NTHR = 64 * (kProducers + NCW);
+    constexpr int PTHR = 64 * kProducers;
+    constexpr size_t BUF = K2WsLds<T, P>::buf;
+    constexpr int XU = TO * PO;  // x units of 8 tokens x 8 columns
+    constexpr int XPASS = (XU + PTHR - 1) / PTHR;
+    static_assert(K2WsLds<T, P>::fits, "two x^T buffers must fit in LDS");
+    extern __shared__ __align__(16) unsigned char lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const bool producer = w < kProducers;
+    const int cw = w - kProducers;  // consumer wave: dstate columns [32 cw, 32 cw + 32)
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int hb = bid % nhb;
+    const int bcg = bid / nhb;
+    const int gi = bcg % G;
+    const int bc = bcg / G;
+    const int c = bc % NC;
+    const int64_t b = bc / NC;
+    const int h_begin = gi * HPG + hb * HB;
+    const int h_end = min(h_begin + HB, (gi + 1) * HPG);
+    const int64_t t0 = (int64_t)c * T;
+
+    // ---- producer side: x rows and weights of XPASS units, one head ahead,
+    //      through per-head buffer resources (rows past seqlen read as 0)
+    struct Pre {
+        u32x4 rows[8];
+        floatx4 wv[2];
+    };
+    Pre pre[XPASS];
+    const int64_t rows_valid = min<int64_t>(T, L - t0);
+    const uint32_t x_bytes = (uint32_t)(((rows_valid - 1) * NH * P + P) * 2);
+    auto unit = [&](int ps, int &po, int &to) __attribute__((always_inline)) {
+        const int u = tid + ps * PTHR;
+        po = u % PO;
+        to = u / PO;
+        return u < XU;
+    };
+    auto load_x = [&](int h) __attribute__((always_inline)) {
+        const auto xres = buffer_rsrc(x + ((b * L + t0) * NH + h) * P, x_bytes);
+        const auto wr = buffer_rsrc(W + ((int64_t)b * NH + h) * Lp + t0, T * 4);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int n = 32 * w + 16 * nt + l16;
-                if (n < N)
+        for (int ps = 0; ps < XPASS; ++ps) {
+            int po, to;
+            if (!unit(ps, po, to)) continue;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) out[(16 * pt + 4 * g4 + r) * N + n] = acc[pt][nt][r];
+            for (int r = 0; r < 8; ++r)
+                pre[ps].rows[r] = buffer_load_x4(xres, ((to * 8 + r) * NH * P + po * 8) * 2);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                pre[ps].wv[q] = __builtin_bit_cast(floatx4, buffer_load_x4(wr, (to * 8 + 4 * q) * 4));
+        }
+    };
+    // scale by w_t, split into hi/lo bf16, write transposed into buffer `bf`
+    auto store_x = [&](int bf) __attribute__((always_inline)) {
+        unsigned char *xhi = lds + bf * BUF;
+        unsigned char *xlo = xhi + P * T * 2;
+#pragma unroll
+        for (int ps = 0; ps < XPASS; ++ps) {
+            int po, to;
+            if (!unit(ps, po, to)) continue;
+            float wt[8];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wt[4 * q + i] = pre[ps].wv[q][i];
+            // one pair of columns (dword i of every row) at a time
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hi[8], lo[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const uint32_t v = pre[ps].rows[r][i];
+                    const HiLo s2 = split_bf16(bf16lo(v) * wt[r], bf16hi(v) * wt[r]);
+                    hi[r] = s2.hi;
+                    lo[r] = s2.lo;
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t sel = half ? 0x07060302u : 0x05040100u;
+                    const int row = po * 8 + 2 * i + half;
+                    u32x4 th, tl;
+#pragma unroll
+                    for (int r2 = 0; r2 < 4; ++r2) {
+                        th[r2] = __builtin_amdgcn_perm(hi[2 * r2 + 1], hi[2 * r2], sel);
+                        tl[r2] = __builtin_amdgcn_perm(lo[2 * r2 + 1], lo[2 * r2], sel);
+                    }
+                    *reinterpret_cast<u32x4 *>(xhi + tr_off<T>(row, to)) = th;
+                    *reinterpret_cast<u32x4 *>(xlo + tr_off<T>(row, to)) = tl;
+                }
             }
+        }
+    };
+    if (producer && h_begin < h_end) load_x(h_begin);  // in flight during the B^T staging
+
+    // ---- B^T for this chunk, staged by all threads in pieces of dstate
+    //      columns; each consumer wave keeps its fragments in registers.
+    u32x4 bfrag[KS][2];
+    {
+        constexpr int PIECE = (int)(2 * BUF / (T * 2)) < 256 ? (int)(2 * BUF / (T * 2)) : 256;
+        for (int n_base = 0; n_base < N; n_base += PIECE) {
+            const int ncols = min(PIECE, N - n_base);
+            const int units = TO * (ncols / 8);
+            for (int u = tid; u < units; u += NTHR) {
+                const int no = u % (ncols / 8), to = u / (ncols / 8);
+                u32x4 rows[8], cols[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int64_t tok = t0 + to * 8 + r;
+                    rows[r] = u32x4{0u, 0u, 0u, 0u};
+                    if (tok < L)
+                        rows[r] = *reinterpret_cast<const u32x4 *>(
+                            Bm + ((b * L + tok) * G + gi) * N + n_base + no * 8);
+                }
+                transpose8x8(rows, cols);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    *reinterpret_cast<u32x4 *>(lds + tr_off<T>(no * 8 + q, to)) = cols[q];
+            }
+            __syncthreads();
+            if (!producer) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int n = 32 * cw + 16 * nt + l16;
+                    const bool mine = (n - n_base) >= 0 && (n - n_base) < ncols;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        if (mine)
+                            bfrag[ks][nt] = *reinterpret_cast<const u32x4 *>(
+                                lds + tr_off<T>(n - n_base, 4 * ks + g4));
+                        else if (n_base == 0)
+                            bfrag[ks][nt] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- heads: producers stage head i + 1 while consumers compute head i
+    if (producer && h_begin < h_end) {
+        store_x(0);
+        if (h_begin + 1 < h_end) load_x(h_begin + 1);
+    }
+    __syncthreads();
+    for (int i = 0; h_begin + i < h_end; ++i) {
+        const int h = h_begin + i;
+        if (producer) {
+            if (h + 1 < h_end) {
+                store_x((i + 1) & 1);
+                if (h + 2 < h_end) load_x(h + 2);
+            }
+        } else if (32 * cw < N) {
+            // opaque lane coordinates: keeps the LDS and store offsets from
+            // being hoisted out of the head loop into registers
+            int tid_o = tid;
+            asm volatile("" : "+v"(tid_o));
+            const int ol16 = tid_o & 15, og4 = (tid_o >> 4) & 3;
+            const unsigned char *xhi = lds + (i & 1) * BUF;
+            const unsigned char *xlo = xhi + P * T * 2;
+            floatx4 acc[PT][2];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt][0] = acc[pt][1] = zero4();
+            // x^T fragments of one k-step, read one step ahead of their MFMAs
+            struct Frags {
+                u32x4 h[PT], l[PT];
+            };
+            auto read = [&](int ks) {
+                Frags f;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int off = tr_off<T>(16 * pt + ol16, 4 * ks + og4);
+                    f.h[pt] = *reinterpret_cast<const u32x4 *>(xhi + off);
+                    f.l[pt] = *reinterpret_cast<const u32x4 *>(xlo + off);
+                }
+                return f;
+            };
+            Frags cur = read(0);
+            static_for<KS>([&](auto kc) {
+                constexpr int ks = decltype(kc)::value;
+                Frags nxt;
+                if constexpr (ks + 1 < KS) nxt = read(ks + 1);
+                // hi products of every tile first, then lo: dependent MFMAs
+                // (same accumulator) are never adjacent
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) acc[pt][nt] = mfma_bf16(cur.h[pt], bfrag[ks][nt], acc[pt][nt]);
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) acc[pt][nt] = mfma_bf16(cur.l[pt], bfrag[ks][nt], acc[pt][nt]);
+                if constexpr (ks + 1 < KS) cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            float *out = S + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int n = 32 * cw + 16 * nt + ol16;
+                    if (n < N)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) out[(16 * pt + 4 * og4 + r) * N + n] = acc[pt][nt][r];
+                }
+        }
         __syncthreads();
     }
 }
@@ -261,8 +526,8 @@ constexpr int kSlab = 64;  // tokens of w*x staged in LDS at a time
 
 template <int T, int P>
 __global__ __launch_bounds__(512) void k2_chunk_state_f32(
-    const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ G2hi,
-    const float *__restrict__ G2lo, const float *__restrict__ DT, float *__restrict__ S, int64_t L,
+    const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ W,
+    float *__restrict__ S, int64_t L,
     int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
     constexpr int KS = T / 4;        // k-steps (4 tokens each) over the chunk
     constexpr int PT = P / 16;
@@ -297,11 +562,7 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
         }
 
     for (int h = h_begin; h < h_end; ++h) {
-        const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
-        const float *gh = G2hi + hoff;
-        const float *gl = G2lo + hoff;
-        const float *dd = DT + hoff;
-        const float lh = gh[T - 1], ll = gl[T - 1];
+        const float *wh = W + ((int64_t)b * NH + h) * Lp + t0;
         int tid_o = tid;  // opaque lane coordinates, as in the bf16 kernel
         asm volatile("" : "+v"(tid_o));
         const int l16 = tid_o & 15, g4 = (tid_o >> 4) & 3;
@@ -317,7 +578,7 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
                 float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (t0 + t < L) {
                     xv = *reinterpret_cast<const float4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
-                    const float wt = fast_exp2((lh - gh[t]) + (ll - gl[t])) * dd[t];
+                    const float wt = wh[t];
                     xv.x *= wt; xv.y *= wt; xv.z *= wt; xv.w *= wt;
                 }
                 *reinterpret_cast<float4 *>(&xs[tt * LDP + 4 * p4]) = xv;
@@ -350,28 +611,47 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
 
 template <int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B,
-                     G2View G2, const float *DT, float *S, hipStream_t stream) {
+                     const float *W, float *S, hipStream_t stream, const LaunchEvents &ev) {
     const int HB = plan.k2_heads_per_block;
     const int nhb = (int)((p.heads_per_group + HB - 1) / HB);
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
     if (blocks == 0) return hipSuccess;
-    if (p.bf16) {
+    if (p.bf16 && p.dstate <= 128 && K2WsLds<T, P>::fits) {
+        if constexpr (K2WsLds<T, P>::fits) {
+            constexpr size_t lds = K2WsLds<T, P>::total;
+            auto go = [&](auto kern, int ncw) -> hipError_t {
+                if (allow_lds<decltype(kern)::value>(lds) != hipSuccess) return hipErrorInvalidValue;
+                launch_kernel(decltype(kern)::value, dim3((unsigned)blocks),
+                                   dim3(64 * (kProducers + ncw)), lds, stream, ev,
+                                   static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
+                                   W, S, p.seqlen, (int)p.nheads, (int)p.dstate, (int)p.ngroups,
+                                   (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB, nhb);
+                return hipSuccess;
+            };
+            const hipError_t e =
+                p.dstate <= 64
+                    ? go(std::integral_constant<decltype(&k2_chunk_state_bf16_ws<T, P, 2>),
+                                                &k2_chunk_state_bf16_ws<T, P, 2>>{}, 2)
+                    : go(std::integral_constant<decltype(&k2_chunk_state_bf16_ws<T, P, 4>),
+                                                &k2_chunk_state_bf16_ws<T, P, 4>>{}, 4);
+            if (e != hipSuccess) return e;
+        }
+    } else if (p.bf16) {
         // one 8x8 (token, headdim) unit of the x tile per thread
         const int waves = (int)std::max<int64_t>((p.dstate + 31) / 32, (T / 8) * (P / 8) / 64);
         constexpr size_t lds = (size_t)2 * P * T * 2;
         static_assert(lds <= 160 * 1024, "stage-2 LDS budget exceeded");
         if (allow_lds<k2_chunk_state_bf16<T, P>>(lds) != hipSuccess) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k2_chunk_state_bf16<T, P>), dim3((unsigned)blocks), dim3(64 * waves),
-                           lds, stream, static_cast<const uint16_t *>(x),
-                           static_cast<const uint16_t *>(B), G2.hi, G2.lo, DT, S, p.seqlen,
-                           (int)p.nheads,
+        launch_kernel((k2_chunk_state_bf16<T, P>), dim3((unsigned)blocks), dim3(64 * waves),
+                           lds, stream, ev, static_cast<const uint16_t *>(x),
+                           static_cast<const uint16_t *>(B), W, S, p.seqlen, (int)p.nheads,
                            (int)p.dstate, (int)p.ngroups, (int)p.nchunks, p.padded_len,
                            (int)p.heads_per_group, HB, nhb);
     } else {
         const int waves = (int)((p.dstate + 31) / 32);
-        hipLaunchKernelGGL((k2_chunk_state_f32<T, P>), dim3((unsigned)blocks), dim3(64 * waves), 0,
-                           stream, static_cast<const float *>(x), static_cast<const float *>(B),
-                           G2.hi, G2.lo, DT, S, p.seqlen, (int)p.nheads, (int)p.dstate,
+        launch_kernel((k2_chunk_state_f32<T, P>), dim3((unsigned)blocks), dim3(64 * waves), 0,
+                           stream, ev, static_cast<const float *>(x), static_cast<const float *>(B),
+                           W, S, p.seqlen, (int)p.nheads, (int)p.dstate,
                            (int)p.ngroups,
                            (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB, nhb);
     }
@@ -380,23 +660,36 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
 
 template <int T>
 hipError_t launch_t(const Problem &p, const Plan &plan, const void *x, const void *B,
-                    G2View G2, const float *DT, float *S, hipStream_t stream) {
+                    const float *W, float *S, hipStream_t stream, const LaunchEvents &ev) {
     switch (p.headdim) {
-        case 32: return launch_tp<T, 32>(p, plan, x, B, G2, DT, S, stream);
-        case 64: return launch_tp<T, 64>(p, plan, x, B, G2, DT, S, stream);
-        case 128: return launch_tp<T, 128>(p, plan, x, B, G2, DT, S, stream);
+        case 32: return launch_tp<T, 32>(p, plan, x, B, W, S, stream, ev);
+        case 64: return launch_tp<T, 64>(p, plan, x, B, W, S, stream, ev);
+        case 128: return launch_tp<T, 128>(p, plan, x, B, W, S, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+int chunk_state_blocks_per_cu(const Problem &p) {
+    size_t lds = 0;
+    if (p.bf16) {
+        // producer/consumer variant (two x^T hi/lo buffers) when it applies
+        const size_t ws = (size_t)8 * p.headdim * p.chunk;
+        lds = (ws <= 160 * 1024 && p.dstate <= 128) ? ws : (size_t)4 * p.headdim * p.chunk;
+    } else {
+        lds = (size_t)kSlab * (p.headdim + 16) * 4;
+    }
+    const size_t by_lds = (160 * 1024) / std::max<size_t>(lds, 1);
+    return (int)std::max<size_t>(1, std::min<size_t>(2, by_lds));
+}
+
 hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
-                              G2View G2, const float *DT, float *S, hipStream_t stream) {
+                              const float *W, float *S, hipStream_t stream, const LaunchEvents &ev) {
     switch (p.chunk) {
-        case 64: return launch_t<64>(p, plan, x, B, G2, DT, S, stream);
-        case 128: return launch_t<128>(p, plan, x, B, G2, DT, S, stream);
-        case 256: return launch_t<256>(p, plan, x, B, G2, DT, S, stream);
+        case 64: return launch_t<64>(p, plan, x, B, W, S, stream, ev);
+        case 128: return launch_t<128>(p, plan, x, B, W, S, stream, ev);
+        case 256: return launch_t<256>(p, plan, x, B, W, S, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -70,12 +70,12 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
 }  // namespace
 
 hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View G2,
-                             const float *init, float *final_states, hipStream_t stream) {
+                             const float *init, float *final_states, hipStream_t stream, const LaunchEvents &ev) {
     const int64_t pn_vec = p.headdim * p.dstate / 4;
     const int64_t n_vec = p.batch * p.nheads * pn_vec;
     if (n_vec == 0) return hipSuccess;
     const int64_t blocks = (n_vec + 255) / 256;
-    hipLaunchKernelGGL(k3_state_pass, dim3((unsigned)blocks), dim3(256), 0, stream, S, H, G2.hi,
+    launch_kernel(k3_state_pass, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H, G2.hi,
                        G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
                        (int)p.chunk);
     return hipGetLastError();

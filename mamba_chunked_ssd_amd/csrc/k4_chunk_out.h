@@ -878,11 +878,11 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 template <int T, int P, int NKMAX, typename OutT>
 hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
                           const void *B, const void *C, G2View G2, const float *DT, const float *D,
-                          const float *H, void *y, hipStream_t stream) {
+                          const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
     constexpr auto kern = k4_chunk_out_bf16<T, P, NKMAX, OutT>;
     constexpr size_t lds = Bf16Lds<T, P, NKMAX>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream,
+    launch_kernel(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream, ev,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), G2.hi, G2.lo, DT, D, H,
                        static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.dstate,
@@ -894,11 +894,11 @@ hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, con
 template <int T, int P, typename OutT>
 hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
                          const void *B, const void *C, G2View G2, const float *DT, const float *D,
-                         const float *H, void *y, hipStream_t stream) {
+                         const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
     constexpr auto kern = k4_chunk_out_f32<T, P, OutT>;
     constexpr size_t lds = F32Lds<T, P>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream,
+    launch_kernel(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream, ev,
                        static_cast<const float *>(x), static_cast<const float *>(B),
                        static_cast<const float *>(C), G2.hi, G2.lo, DT, D, H,
                        static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.dstate,
@@ -910,29 +910,29 @@ hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, cons
 template <typename InT, typename OutT, int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
                      G2View G2, const float *DT, const float *D, const float *H, void *y,
-                     hipStream_t stream) {
+                     hipStream_t stream, const LaunchEvents &ev) {
     const int HB = plan.k4_heads_per_block;
     const int nhb = (int)((p.heads_per_group + HB - 1) / HB);
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
     if (blocks == 0) return hipSuccess;
     if constexpr (sizeof(InT) == 2) {
         if (p.dstate <= 128)
-            return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
-        return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
+            return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
+        return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
     } else {
-        return launch_f32_in<T, P, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream);
+        return launch_f32_in<T, P, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
     }
 }
 
 template <typename InT, typename OutT>
 hipError_t launch(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
                   G2View G2, const float *DT, const float *D, const float *H, void *y,
-                  hipStream_t stream) {
+                  hipStream_t stream, const LaunchEvents &ev) {
 #define SSD_K4_P(T)                                                                              \
     switch (p.headdim) {                                                                         \
-        case 32: return launch_tp<InT, OutT, T, 32>(p, plan, x, B, C, G2, DT, D, H, y, stream);  \
-        case 64: return launch_tp<InT, OutT, T, 64>(p, plan, x, B, C, G2, DT, D, H, y, stream);  \
-        case 128: return launch_tp<InT, OutT, T, 128>(p, plan, x, B, C, G2, DT, D, H, y, stream); \
+        case 32: return launch_tp<InT, OutT, T, 32>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);  \
+        case 64: return launch_tp<InT, OutT, T, 64>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);  \
+        case 128: return launch_tp<InT, OutT, T, 128>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev); \
         default: return hipErrorInvalidValue;                                                    \
     }
     switch (p.chunk) {
@@ -947,10 +947,10 @@ hipError_t launch(const Problem &p, const Plan &plan, const void *x, const void 
 // One explicit instantiation per translation unit (compiled in parallel).
 hipError_t launch_bf16_in_f32_out(const Problem &p, const Plan &plan, const void *x, const void *B,
                                   const void *C, G2View G2, const float *DT, const float *D,
-                                  const float *H, void *y, hipStream_t stream);
+                                  const float *H, void *y, hipStream_t stream, const LaunchEvents &ev);
 hipError_t launch_bf16_in_bf16_out(const Problem &p, const Plan &plan, const void *x, const void *B,
                                    const void *C, G2View G2, const float *DT, const float *D,
-                                   const float *H, void *y, hipStream_t stream);
+                                   const float *H, void *y, hipStream_t stream, const LaunchEvents &ev);
 
 }  // namespace k4
 }  // namespace ssd

@@ -7,8 +7,8 @@ namespace k4 {
 
 hipError_t launch_bf16_in_f32_out(const Problem &p, const Plan &plan, const void *x, const void *B,
                                   const void *C, G2View G2, const float *DT, const float *D,
-                                  const float *H, void *y, hipStream_t stream) {
-    return launch<uint16_t, float>(p, plan, x, B, C, G2, DT, D, H, y, stream);
+                                  const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
+    return launch<uint16_t, float>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);
 }
 
 }  // namespace k4

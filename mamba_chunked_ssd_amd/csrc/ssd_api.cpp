@@ -99,6 +99,8 @@ ssd_workspace_layout layout_for(const Problem &p, bool keep) {
     off = align_up(off + seq);
     l.dt = off;
     off = align_up(off + seq);
+    l.w = off;
+    off = align_up(off + seq);
     l.s = off;
     off = align_up(off + states);
     l.h = keep ? off : l.s;
@@ -152,7 +154,7 @@ const int kNumCUs = 256;
 
 Plan make_plan(const Problem &p) {
     Plan plan;
-    plan.k2_heads_per_block = pick_heads_per_block(p, 2 * kNumCUs, 1.0);
+    plan.k2_heads_per_block = pick_heads_per_block(p, chunk_state_blocks_per_cu(p) * kNumCUs, 1.0);
     plan.k4_heads_per_block = pick_heads_per_block(p, kNumCUs, 1.0);
     return plan;
 }
@@ -206,7 +208,7 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     if (p.batch > 0 && lay.total > 0 && workspace == nullptr) return SSD_ERROR_WORKSPACE;
     if (workspace_bytes < lay.total) return SSD_ERROR_WORKSPACE;
     if (events != nullptr)
-        for (int i = 0; i < 5; ++i)
+        for (int i = 0; i < 8; ++i)
             if (events[i] == nullptr) return SSD_ERROR_INVALID_VALUE;
 
     // alignment
@@ -238,30 +240,43 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     const G2Pair G2{reinterpret_cast<float *>(ws + lay.g2_hi), reinterpret_cast<float *>(ws + lay.g2_lo)};
     const G2View G2v{G2.hi, G2.lo};
     float *DTf = reinterpret_cast<float *>(ws + lay.dt);
+    float *Wf = reinterpret_cast<float *>(ws + lay.w);
     float *S = reinterpret_cast<float *>(ws + lay.s);
     float *Hs = reinterpret_cast<float *>(ws + lay.h);
     const Plan plan = make_plan(p);
 
-    auto record = [&](int i) -> bool {
-        if (events == nullptr) return true;
-        return hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess;
+    // stage i's (start, stop) events, recorded by its kernel's dispatch; a
+    // stage with nothing to do records both at once
+    auto events_of = [&](int i) {
+        LaunchEvents ev;
+        if (events != nullptr) {
+            ev.start = static_cast<hipEvent_t>(events[2 * i]);
+            ev.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+        }
+        return ev;
     };
-    if (!record(0)) return SSD_ERROR_LAUNCH;
+    auto skip = [&](int i) -> bool {
+        if (events == nullptr) return true;
+        const LaunchEvents ev = events_of(i);
+        return hipEventRecord(ev.start, stream) == hipSuccess &&
+               hipEventRecord(ev.stop, stream) == hipSuccess;
+    };
     if (p.nchunks > 0) {
-        if (launch_chunk_cumsum(p, dt, A, G2, DTf, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
-    }
-    if (!record(1)) return SSD_ERROR_LAUNCH;
-    if (p.nchunks > 0) {
-        if (launch_chunk_state(p, plan, x, B, G2v, DTf, S, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
-    }
-    if (!record(2)) return SSD_ERROR_LAUNCH;
-    if (launch_state_pass(p, S, Hs, G2v, init, final_states, stream) != hipSuccess) return SSD_ERROR_LAUNCH;
-    if (!record(3)) return SSD_ERROR_LAUNCH;
-    if (p.nchunks > 0) {
-        if (launch_chunk_out(p, plan, x, B, C, G2v, DTf, D, Hs, y, stream) != hipSuccess)
+        if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
+        if (launch_chunk_state(p, plan, x, B, Wf, S, stream, events_of(1)) != hipSuccess)
+            return SSD_ERROR_LAUNCH;
+    } else if (!skip(0) || !skip(1)) {
+        return SSD_ERROR_LAUNCH;
     }
-    if (!record(4)) return SSD_ERROR_LAUNCH;
+    if (launch_state_pass(p, S, Hs, G2v, init, final_states, stream, events_of(2)) != hipSuccess)
+        return SSD_ERROR_LAUNCH;
+    if (p.nchunks > 0) {
+        if (launch_chunk_out(p, plan, x, B, C, G2v, DTf, D, Hs, y, stream, events_of(3)) != hipSuccess)
+            return SSD_ERROR_LAUNCH;
+    } else if (!skip(3)) {
+        return SSD_ERROR_LAUNCH;
+    }
     return SSD_OK;
 }
 

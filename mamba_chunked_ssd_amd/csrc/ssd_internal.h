@@ -2,6 +2,7 @@
 // the four kernel translation units.  Not installed; not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,25 +42,42 @@ struct G2View {
     const float *lo;
 };
 
-// Stage 1: G2 (hi/lo) and dt widened to fp32 -> DT, all head-major.
-hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
-                               float *DT, hipStream_t stream);
+// Optional (start, stop) events recorded by a kernel's own dispatch.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
 
-// Stage 2: per-chunk input state s_c = sum_t exp2(G2_last - G2_t) DT_t x_t B_t^T,
+// Launch on `stream`; when `ev` holds events they time this dispatch alone.
+template <typename... Args, typename F>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                const LaunchEvents &ev, Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, ev.start, ev.stop, 0u, args...);
+    return hipGetLastError();
+}
+
+// Stage 1: G2 (hi/lo), dt widened to fp32 -> DT and the chunk-state weights
+// W_t = exp2(G2_last - G2_t) DT_t, all head-major.
+hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
+                               float *DT, float *W, hipStream_t stream, const LaunchEvents &ev);
+
+// Stage 2: per-chunk input state s_c = sum_t W_t x_t B_t^T,
 // written as (batch, nheads, nchunks, headdim, dstate) fp32.
 hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
-                              G2View G2, const float *DT, float *S, hipStream_t stream);
+                              const float *W, float *S, hipStream_t stream, const LaunchEvents &ev);
+// How many stage-2 blocks one CU holds (set by the kernel variant's LDS use).
+int chunk_state_blocks_per_cu(const Problem &p);
 
 // Stage 3: h_0 = init (or 0); for each chunk store h_c then
 // h_{c+1} = exp2(G2_last,c) h_c + s_c; final = h_nchunks.  H may equal S.
 hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View G2,
-                             const float *init, float *final_states, hipStream_t stream);
+                             const float *init, float *final_states, hipStream_t stream,
+                             const LaunchEvents &ev);
 
 // Stage 4: chunk output
 // y_i = exp2(G2_i) C_i h_c + sum_{j<=i} exp2(G2_i - G2_j) (C_i . B_j) DT_j x_j + D x_i.
 hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
                             const void *C, G2View G2, const float *DT, const float *D,
-                            const float *H, void *y, hipStream_t stream);
+                            const float *H, void *y, hipStream_t stream, const LaunchEvents &ev);
 
 // Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
 // CU).  The template parameter is the kernel itself, so each kernel caches

@@ -148,6 +148,22 @@ def chunk_cumsum(dt, A, chunk_size: int):
     return np.ascontiguousarray(g.reshape(bsz, nc * chunk_size, nh).transpose(0, 2, 1))
 
 
+def chunk_state_weights(dt, A, chunk_size: int):
+    """Weight with which each token enters its chunk's state, (b, nh, Lp):
+    exp(G_last - G_t) dt_t with G the per-chunk cumsum and G_last its value at
+    the chunk's last token ("Accelerating Mamba-2 ...", section "Mamba-2
+    architecture": the log-space state jump scales the chunk's B rows by the
+    decay from each token to the chunk end; dt is the discretisation step
+    that multiplies B).  Padding past seqlen has dt = 0, hence weight 0.
+    """
+    G = chunk_cumsum(dt, A, chunk_size)
+    bsz, nh, Lp = G.shape
+    Gc = G.reshape(bsz, nh, Lp // chunk_size, chunk_size)
+    decay = np.exp(Gc[..., -1:] - Gc).reshape(bsz, nh, Lp)
+    dtp = _pad_tokens(_f64(dt), Lp).transpose(0, 2, 1)
+    return decay * dtp
+
+
 def _pad_tokens(v, Lp):
     out = np.zeros((v.shape[0], Lp) + v.shape[2:], np.float64)
     out[:, : v.shape[1]] = v

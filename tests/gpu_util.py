@@ -39,7 +39,7 @@ def to_device(inp: dict, dtype: str, dev="cuda"):
 
 def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = True,
         y_dtype: str = "f32"):
-    """Forward pass; returns numpy fp64 dict with y, final and (keep) G2/DT/S/H
+    """Forward pass; returns numpy fp64 dict with y, final and (keep) G2/DT/W/S/H
     (G2 = the stored hi + lo pair, summed in fp64)."""
     t = to_device(inp, dtype)
     b, L, nh, p = t["x"].shape
@@ -69,6 +69,7 @@ def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = Tru
 
         out["G2"] = view(lay.g2_hi, (b, nh, Lp)) + view(lay.g2_lo, (b, nh, Lp))
         out["DT"] = view(lay.dt, (b, nh, Lp))
+        out["W"] = view(lay.w, (b, nh, Lp))
         out["S"] = view(lay.s, (b, nh, nc, p, n))
         out["H"] = view(lay.h, (b, nh, nc, p, n))
     return out

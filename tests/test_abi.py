@@ -74,14 +74,14 @@ def test_workspace_size_formula(lib):
             seq = 4 * 2 * 8 * nc * T
             st = 4 * 2 * 8 * nc * 64 * 128
             up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-            want = up(seq) * 3 + up(st) * (2 if keep else 1)
+            want = up(seq) * 4 + up(st) * (2 if keep else 1)
             assert ssd.workspace_size(s, T) == want
             lay = ssd.workspace_layout(s, T)
             assert lay.total == want and lay.nchunks == nc and lay.padded_len == nc * T
-            offs = [lay.g2_hi, lay.g2_lo, lay.dt, lay.s, lay.h]
+            offs = [lay.g2_hi, lay.g2_lo, lay.dt, lay.w, lay.s, lay.h]
             assert all(o % 256 == 0 for o in offs)
             assert lay.g2_hi == 0 and lay.g2_lo == up(seq) and lay.dt == 2 * up(seq)
-            assert lay.s == 3 * up(seq)
+            assert lay.w == 3 * up(seq) and lay.s == 4 * up(seq)
             assert (lay.h == lay.s) != keep
 
 

@@ -58,6 +58,9 @@ def test_stage_parity(dtype, shp):
     dtp = np.zeros((b, nc * T, nh))
     dtp[:, :L] = inp["dt"]
     assert np.array_equal(out["DT"], dtp.transpose(0, 2, 1))
+    # chunk-state weights exp(G_last - G_t) dt_t (fp64 exponent, fp32 exp2)
+    Wref = oracle.chunk_state_weights(inp["dt"], inp["A"], T)
+    assert nerr(out["W"], Wref) < 1e-5, ("W", nerr(out["W"], Wref))
     # stage 2: per-chunk input states
     S = oracle.chunk_states(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], T)
     assert nerr(out["S"], S) < tol, ("S", nerr(out["S"], S))

@@ -78,6 +78,31 @@ def test_chunk_states_match_bruteforce():
         assert pins.rel_err(S[:, :, c], fr) < 1e-11
 
 
+def test_chunk_state_weights_reproduce_sequential_chunk_states():
+    # summing every token's outer product x_t B_t^T with its weight must give
+    # the state the sequential scan reaches from zero at the chunk end
+    pr = pins.problem(10, b=2, L=23, nh=4, p=3, n=5, g=2, h0=False)
+    T = 8
+    Wt = oracle.chunk_state_weights(pr["dt"], pr["A"], T)
+    nc = -(-23 // T)
+    assert Wt.shape == (2, 4, nc * T)
+    assert np.all(Wt[:, :, 23:] == 0.0)
+    S = oracle.chunk_states(pr["x"], pr["dt"], pr["A"], pr["B"], pr["C"], T)
+    hpg = 4 // 2
+    for c in range(nc):
+        t1 = min(23, (c + 1) * T)
+        for h in range(4):
+            Bh = pr["B"][:, c * T:t1, h // hpg]                      # (b, t, n)
+            xw = pr["x"][:, c * T:t1, h] * Wt[:, h, c * T:t1, None]   # (b, t, p)
+            ref = np.einsum("btp,btn->bpn", xw, Bh)
+            assert pins.rel_err(S[:, h, c], ref) < 1e-12
+    # the chunk's last token enters with weight dt (no decay left)
+    dtp = np.zeros((2, nc * T, 4))
+    dtp[:, :23] = pr["dt"]
+    for c in range(nc - 1):
+        np.testing.assert_allclose(Wt[:, :, c * T + T - 1], dtp[:, c * T + T - 1], rtol=1e-15)
+
+
 def test_chunk_start_states_match_chunked_reference():
     pr = pins.problem(9, b=1, L=21, nh=2, p=3, n=4, h0=True)
     T = 5
