@@ -7,9 +7,11 @@ synthetic input already resident in HBM.  The default workload is the
 Mamba-2 2.7B-shaped layer (batch 2, seqlen 2048, 80 heads, headdim 64,
 dstate 128, 1 group, chunk 256, bf16 inputs, fp32 accumulation and fp32 y).
 
-Prints ONE JSON line: tokens/s, per-stage times from HIP events recorded on
-the library's stream inside the timed region, the roofline of the dominant
-kernel, and the fp64 CPU oracle timed on this host as a reference baseline.
+Prints ONE JSON line: tokens/s over K back-to-back steps (nothing else on the
+stream), per-stage kernel times from a second run of K steps in which every
+kernel's dispatch records a (start, stop) HIP event pair, the roofline of the
+dominant kernel, and the fp64 CPU oracle timed on this host as a reference
+baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -208,21 +210,28 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps; a (start, stop) event pair per stage,
-    # recorded by each kernel's own dispatch
-    evs = [[hip.event() for _ in range(8)] for _ in range(a.steps)]
+    # timed region: K back-to-back steps, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / a.steps
+
+    # per-stage times: a second run of K steps in which every kernel's own
+    # dispatch records a (start, stop) event pair (these records cost time of
+    # their own, so this run is not the one the throughput comes from)
+    evs = [[hip.event() for _ in range(8)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
     for i in range(a.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     per_stage = np.array([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(4)] for e in evs])
     for e in evs:
         for ev in e:
             hip.destroy(ev)
     stage_ms = per_stage.mean(axis=0)
-    ms_per_step = elapsed * 1e3 / a.steps
 
     model = stage_model(w, 4 if ydt == torch.float32 else (2 if w.dtype == "bf16" else 4))
     peak_tf = PEAK_TFLOPS[w.dtype]

@@ -235,6 +235,14 @@ struct WaveTiles {
     static constexpr int ii_of(int k) { return k < base1 ? 0 : 1; }
     static constexpr int I_of(int k) { return k < base1 ? I0 : I1; }
     static constexpr int J_of(int k) { return k < base1 ? k : k - base1; }
+    // the q-th pair processed: pairs of I0 (0 .. base1/2 - 1) and of I1
+    // (base1/2 .. NSLOT/2 - 1) alternate while both last
+    static constexpr int pair_order(int q) {
+        const int n0 = base1 / 2, n1 = NSLOT / 2 - n0;
+        const int m = n0 < n1 ? n0 : n1;
+        if (q < 2 * m) return (q % 2 == 0) ? q / 2 : n0 + q / 2;
+        return n0 > n1 ? q - m : n0 + (q - m);
+    }
 };
 
 // tile_values with the tile relation known at compile time
@@ -392,38 +400,62 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
         const float m = tile_pair_factor(cx.tb, off ? Ik : 1, off ? Jk : 0);  // in-range reads
         mk = off ? m : 0.f;
     }
-    // intra-chunk term: slot pairs (J, J + 1) of one row tile, K = 32
-    static_for<2>([&](auto iic) {
-        constexpr int ii = decltype(iic)::value;
+    // intra-chunk term: slot pairs (J, J + 1) of one row tile, K = 32.  The
+    // A operand (masked, decay-weighted values, hi/lo) of pair q + 1 is built
+    // while the MFMAs of pair q run; the x fragments are read just before use.
+    const float rs[2] = {row_factor(cx.tb, I0, cx.tb.gh[16 * I0 + l16], cx.tb.gl[16 * I0 + l16]),
+                         row_factor(cx.tb, I1, cx.tb.gh[16 * I1 + l16], cx.tb.gl[16 * I1 + l16])};
+    // G2 of the lane's row, re-read from LDS where a diagonal tile needs it
+    // (an opaque offset keeps the reads from being merged and held in registers)
+    auto row_g2 = [&](int I, float &h, float &lo) {
+        int off = 16 * I + l16;
+        asm volatile("" : "+v"(off));
+        h = cx.tb.gh[off];
+        lo = cx.tb.gl[off];
+    };
+    constexpr int NP = WT::NSLOT / 2;
+    struct AOps {
+        u32x4 hi, lo;
+        u32x4 xb[PT];  // x fragments of the pair, one per 16 headdim columns
+    };
+    auto prep = [&](auto qc) {
+        constexpr int k0 = 2 * decltype(qc)::value;
+        constexpr int ii = k0 < WT::base1 ? 0 : 1;
         constexpr int I = ii ? I1 : I0;
-        constexpr int kb = ii ? WT::base1 : 0, kend = ii ? WT::NSLOT : WT::base1;
-        const float gih = cx.tb.gh[16 * I + l16], gil = cx.tb.gl[16 * I + l16];
-        const float rs = row_factor(cx.tb, I, gih, gil);
-        static_for<WT::NSLOT / 2>([&](auto qc) {
-            constexpr int k0 = 2 * decltype(qc)::value;
-            if constexpr (k0 >= kb && k0 < kend) {
-                // keep the scheduler from hoisting later pairs' loads into this
-                // one (register pressure at two waves per SIMD)
-                __builtin_amdgcn_sched_barrier(0);
-                constexpr int Ja = k0 - kb, Jb = Ja + 1;
-                const float rma = rs * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0));
-                const float rmb = rs * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0 + 1));
-                float va[4], vb[4];
-                tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, rma, cx.tb, va);
-                tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, rmb, cx.tb, vb);
-                const HiLo p0 = split_bf16(va[0], va[1]), p1 = split_bf16(va[2], va[3]);
-                const HiLo p2 = split_bf16(vb[0], vb[1]), p3 = split_bf16(vb[2], vb[3]);
-                const u32x4 ahi = {p0.hi, p1.hi, p2.hi, p3.hi};
-                const u32x4 alo = {p0.lo, p1.lo, p2.lo, p3.lo};
+        constexpr int Ja = k0 - (ii ? WT::base1 : 0), Jb = Ja + 1;
+        const float rma = rs[ii] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0));
+        const float rmb = rs[ii] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0 + 1));
+        float gih = 0.f, gil = 0.f;
+        if constexpr (Ja == I || Jb == I) row_g2(I, gih, gil);
+        float va[4], vb[4];
+        tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, rma, cx.tb, va);
+        tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, rmb, cx.tb, vb);
+        const HiLo p0 = split_bf16(va[0], va[1]), p1 = split_bf16(va[2], va[3]);
+        const HiLo p2 = split_bf16(vb[0], vb[1]), p3 = split_bf16(vb[2], vb[3]);
+        AOps o;
+        o.hi = u32x4{p0.hi, p1.hi, p2.hi, p3.hi};
+        o.lo = u32x4{p0.lo, p1.lo, p2.lo, p3.lo};
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    // 16-byte chunk (Ja / 2, g4): tokens 16 Ja + 4 g4 .. +3, then 16 Jb + 4 g4 .. +3
-                    const u32x4 bop = *reinterpret_cast<const u32x4 *>(cx.xl + pt * 16 * XRS + 32 * Ja);
-                    acc[ii][pt] = mfma_bf16(ahi, bop, acc[ii][pt]);
-                    acc[ii][pt] = mfma_bf16(alo, bop, acc[ii][pt]);
-                }
-            }
-        });
+        for (int pt = 0; pt < PT; ++pt)  // chunk (Ja / 2, g4): tokens 16 Ja + 4 g4 .. +3, 16 Jb + 4 g4 .. +3
+            o.xb[pt] = *reinterpret_cast<const u32x4 *>(cx.xl + pt * 16 * XRS + 32 * Ja);
+        return o;
+    };
+    // pairs of the two row tiles alternate, so consecutive MFMAs go to
+    // different accumulators (8 independent chains instead of 4)
+    AOps cur = prep(std::integral_constant<int, WT::pair_order(0)>{});
+    static_for<NP>([&](auto qc) {
+        constexpr int q = WT::pair_order(decltype(qc)::value);
+        constexpr int k0 = 2 * q;
+        constexpr int ii = k0 < WT::base1 ? 0 : 1;
+        constexpr int qn = decltype(qc)::value + 1;
+        AOps nxt;
+        if constexpr (qn < NP) nxt = prep(std::integral_constant<int, WT::pair_order(qn < NP ? qn : 0)>{});
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.hi, cur.xb[pt], acc[ii][pt]);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.lo, cur.xb[pt], acc[ii][pt]);
+        if constexpr (qn < NP) cur = nxt;
+        __builtin_amdgcn_sched_barrier(0);
     });
     __builtin_amdgcn_sched_barrier(0);
     // skip term and store: lane holds rows 16 I + 4 g4 + r, column 16 pt + l16
