@@ -94,11 +94,15 @@ typedef struct {
  *   W   fp32 (batch, nheads, Lp): exp(G_last - G_t) dt_t, the weight with which
  *       token t enters its chunk's state (G_last: G at the chunk's last
  *       token; the exponent is formed in fp64); 0 past seqlen.
- *   S   fp32 (batch, nheads, nchunks, headdim, dstate): after the call, the
- *       chunk-start states h_c (the state before the chunk's first token);
- *       with SSD_FLAG_KEEP_INTERMEDIATES, the per-chunk input states s_c
- *       (what a chunk alone adds to a zero state).
- *   H   (only with SSD_FLAG_KEEP_INTERMEDIATES) same shape as S: h_c. */
+ *   S   fp32 (batch, nheads, nchunks, headdim, dstate): the per-chunk input
+ *       states s_c (what a chunk alone adds to a zero state), except for fp32
+ *       problems without SSD_FLAG_KEEP_INTERMEDIATES, where H shares this
+ *       region and it holds h_c after the call.
+ *   H   the chunk-start states h_c (the state before the chunk's first
+ *       token), same byte size as S.  fp32 problems: fp32 (batch, nheads,
+ *       nchunks, headdim, dstate).  bf16 problems: per (batch, head, chunk) a
+ *       hi plane then a lo plane of (headdim, dstate) bf16 with hi = bf16(h_c),
+ *       lo = bf16(h_c - hi); always a region of its own. */
 typedef struct {
     size_t g2_hi, g2_lo, dt, w, s, h, total;
     int64_t nchunks, padded_len;

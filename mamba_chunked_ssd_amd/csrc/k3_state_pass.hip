@@ -14,8 +14,12 @@
 // (batch, head) and walks the chunks; loads of up to 8 chunks are issued
 // before the dependent FMA chain so each thread keeps 128 B in flight, and
 // consecutive threads touch consecutive 16-byte words, so every wave access
-// is a fully coalesced 1 KiB.  h may alias s (in-place): each element is read
-// before it is overwritten, by the same thread.
+// is a fully coalesced 1 KiB.  For fp32 problems h is fp32 and may alias s
+// (in place: each element is read before it is overwritten, by the same
+// thread).  For bf16 problems the chunk output multiplies h_c as hi + lo bf16
+// halves, so h is written split: per (batch, head, chunk) a hi plane and a lo
+// plane of (headdim, dstate) bf16 (hi = bf16(h), lo = bf16(h - hi)), in a
+// region of its own; the final state stays fp32.
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
@@ -24,6 +28,7 @@ namespace {
 
 constexpr int kDepth = 8;
 
+template <bool kSplit>
 __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
                                                      const float *__restrict__ G2hi,
                                                      const float *__restrict__ G2lo,
@@ -55,7 +60,15 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
 #pragma unroll
         for (int k = 0; k < kDepth; ++k) {
             if (c0 + k < nchunks) {
-                Hv[((bh * nchunks) + c0 + k) * pn_vec + e] = h;
+                if constexpr (kSplit) {
+                    // planes of 4 pn_vec bf16 each: hi at chunk base, lo after it
+                    uint16_t *hb = reinterpret_cast<uint16_t *>(H) + ((bh * nchunks) + c0 + k) * 8 * pn_vec;
+                    const HiLo a = split_bf16(h.x, h.y), bq = split_bf16(h.z, h.w);
+                    *reinterpret_cast<u32x2 *>(hb + 4 * e) = u32x2{a.hi, bq.hi};
+                    *reinterpret_cast<u32x2 *>(hb + 4 * pn_vec + 4 * e) = u32x2{a.lo, bq.lo};
+                } else {
+                    Hv[((bh * nchunks) + c0 + k) * pn_vec + e] = h;
+                }
                 const float a = fast_exp2(dec[k]);
                 h.x = fmaf(a, h.x, s[k].x);
                 h.y = fmaf(a, h.y, s[k].y);
@@ -75,9 +88,14 @@ hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View 
     const int64_t n_vec = p.batch * p.nheads * pn_vec;
     if (n_vec == 0) return hipSuccess;
     const int64_t blocks = (n_vec + 255) / 256;
-    launch_kernel(k3_state_pass, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H, G2.hi,
-                       G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
-                       (int)p.chunk);
+    if (p.bf16)
+        launch_kernel(k3_state_pass<true>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H,
+                      G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
+                      (int)p.chunk);
+    else
+        launch_kernel(k3_state_pass<false>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H,
+                      G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
+                      (int)p.chunk);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@
 // row i: an A-operand fragment of the next product, up to a fixed relabelling
 // of the contraction index that the X operand reads mirror.
 //  * bf16 inputs: v_mfma_f32_16x16x32_bf16.  X is staged per head in LDS
-//    transposed ([headdim][token]); h_c is staged as hi/lo bf16.  The
+//    transposed ([headdim][token]); h_c arrives from the state-passing stage
+//    as hi/lo bf16 planes and is staged as is.  The
 //    fp32-valued operands -- the decay-masked tile and h_c -- are split into
 //    hi + lo bf16 halves and multiplied by the exact bf16 inputs, so the
 //    result keeps fp32-accumulation accuracy.
@@ -313,7 +314,7 @@ struct HeadCtx {
     const unsigned char *xl;  // x^T + l16 * XRS + 16 g4
     const unsigned char *hl;  // h hi tile + l16 * HRS + 16 g4 (when staged in LDS)
     const unsigned char *cl;  // C tile + l16 * CRS (when staged in LDS)
-    const float *hp;          // h_c in global memory (when not staged)
+    const uint16_t *hp;       // h_c hi plane in global memory (lo plane follows; when not staged)
     Tables<T> tb;
     __amdgpu_buffer_rsrc_t yr;  // y[b, t0 .., h, :] through the chunk's last valid row
     int NHP;                  // nheads * headdim (row stride of y)
@@ -358,17 +359,13 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
                 hh = *reinterpret_cast<const u32x4 *>(cx.hl + pt * 16 * HRS + 64 * ks);
                 hlv = *reinterpret_cast<const u32x4 *>(cx.hl + Lds::h / 2 + pt * 16 * HRS + 64 * ks);
             } else {
-                floatx4 v0 = zero4(), v1 = zero4();
+                hh = hlv = u32x4{0u, 0u, 0u, 0u};
                 const int n0 = 32 * ks + 8 * g4;
                 if (n0 < cx.N) {
-                    const float *src = cx.hp + (16 * pt + l16) * cx.N + n0;
-                    v0 = *reinterpret_cast<const floatx4 *>(src);
-                    v1 = *reinterpret_cast<const floatx4 *>(src + 4);
+                    const uint16_t *src = cx.hp + (16 * pt + l16) * cx.N + n0;
+                    hh = *reinterpret_cast<const u32x4 *>(src);
+                    hlv = *reinterpret_cast<const u32x4 *>(src + P * cx.N);
                 }
-                const HiLo a = split_bf16(v0[0], v0[1]), bq = split_bf16(v0[2], v0[3]);
-                const HiLo cq = split_bf16(v1[0], v1[1]), dq = split_bf16(v1[2], v1[3]);
-                hh = u32x4{a.hi, bq.hi, cq.hi, dq.hi};
-                hlv = u32x4{a.lo, bq.lo, cq.lo, dq.lo};
             }
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) {
@@ -480,7 +477,7 @@ template <int T, int P, int NKMAX, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ G2hi, const float *__restrict__ G2lo,
-    const float *__restrict__ DT, const float *__restrict__ Dv, const float *__restrict__ H,
+    const float *__restrict__ DT, const float *__restrict__ Dv, const uint16_t *__restrict__ H,
     OutT *__restrict__ y, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
     int nhb) {
     using Lds = Bf16Lds<T, P, NKMAX>;
@@ -527,7 +524,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
 
     // ---------------- per-head data, loaded one head ahead ----------------
     u32x4 xr[XPASS][4];
-    floatx4 hr[HREG][2];
+    u32x4 hr[HREG][2];  // hi, lo bf16 of 8 consecutive dstate entries
     float sgh = 0.f, sgl = 0.f, seh = 0.f, sel = 0.f, sdt = 0.f;
     auto xunit = [&](int ps, int &tq, int &po) {
         const int u = tid + ps * NTHR;
@@ -551,15 +548,15 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
             }
         }
         if constexpr (kHinLds) {
-            const float *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N;
+            const uint16_t *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N;
 #pragma unroll
             for (int ps = 0; ps < HPASS; ++ps) {
                 const int u = tid + ps * NTHR;
                 const int ch = u % HCH, p = u / HCH;
-                hr[ps][0] = hr[ps][1] = zero4();
+                hr[ps][0] = hr[ps][1] = u32x4{0u, 0u, 0u, 0u};
                 if (u < HUNITS && 8 * ch < N) {
-                    hr[ps][0] = *reinterpret_cast<const floatx4 *>(hp + p * N + 8 * ch);
-                    hr[ps][1] = *reinterpret_cast<const floatx4 *>(hp + p * N + 8 * ch + 4);
+                    hr[ps][0] = *reinterpret_cast<const u32x4 *>(hp + p * N + 8 * ch);
+                    hr[ps][1] = *reinterpret_cast<const u32x4 *>(hp + P * N + p * N + 8 * ch);
                 }
             }
         }
@@ -594,12 +591,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                 const int u = tid + ps * NTHR;
                 if (u < HUNITS) {
                     const int ch = u % HCH, p = u / HCH;
-                    const HiLo a = split_bf16(hr[ps][0][0], hr[ps][0][1]);
-                    const HiLo bq = split_bf16(hr[ps][0][2], hr[ps][0][3]);
-                    const HiLo cq = split_bf16(hr[ps][1][0], hr[ps][1][1]);
-                    const HiLo dq = split_bf16(hr[ps][1][2], hr[ps][1][3]);
-                    *reinterpret_cast<u32x4 *>(hhi + p * HRS + 16 * ch) = u32x4{a.hi, bq.hi, cq.hi, dq.hi};
-                    *reinterpret_cast<u32x4 *>(hlo + p * HRS + 16 * ch) = u32x4{a.lo, bq.lo, cq.lo, dq.lo};
+                    *reinterpret_cast<u32x4 *>(hhi + p * HRS + 16 * ch) = hr[ps][0];
+                    *reinterpret_cast<u32x4 *>(hlo + p * HRS + 16 * ch) = hr[ps][1];
                 }
             }
         }
@@ -686,7 +679,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         HeadCtx<T, P, NKMAX, OutT> cx{xt + id.l16 * XRS + 16 * id.g4,
                                       hhi + id.l16 * HRS + 16 * id.g4,
                                       ct + id.l16 * Lds::CRS,
-                                      H + (((int64_t)b * NH + h) * NC + c) * (int64_t)P * N,
+                                      H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
                                       tb,
                                       buffer_rsrc(y + ((b * L + t0) * NH + h) * P,
                                                   (uint32_t)(((rows - 1) * NH * P + P) * sizeof(OutT))),
@@ -916,7 +909,8 @@ hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, con
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
     launch_kernel(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream, ev,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
-                       static_cast<const uint16_t *>(C), G2.hi, G2.lo, DT, D, H,
+                       static_cast<const uint16_t *>(C), G2.hi, G2.lo, DT, D,
+                       reinterpret_cast<const uint16_t *>(H),  // hi/lo bf16 planes
                        static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.dstate,
                        (int)p.ngroups, (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB,
                        nhb);

@@ -103,8 +103,11 @@ ssd_workspace_layout layout_for(const Problem &p, bool keep) {
     off = align_up(off + seq);
     l.s = off;
     off = align_up(off + states);
-    l.h = keep ? off : l.s;
-    if (keep) off = align_up(off + states);
+    // bf16 problems store h_c split into bf16 hi/lo planes, which cannot be
+    // written in place over s_c; fp32 problems without the keep flag reuse S
+    const bool own_h = keep || p.bf16;
+    l.h = own_h ? off : l.s;
+    if (own_h) off = align_up(off + states);
     l.total = off;
     l.nchunks = p.nchunks;
     l.padded_len = p.padded_len;

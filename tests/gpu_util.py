@@ -71,5 +71,12 @@ def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = Tru
         out["DT"] = view(lay.dt, (b, nh, Lp))
         out["W"] = view(lay.w, (b, nh, Lp))
         out["S"] = view(lay.s, (b, nh, nc, p, n))
-        out["H"] = view(lay.h, (b, nh, nc, p, n))
+        if dtype == "bf16":
+            # h_c as hi and lo bf16 planes per (batch, head, chunk)
+            cnt = b * nh * nc * 2 * p * n
+            hl = ws[lay.h: lay.h + 2 * cnt].view(torch.bfloat16).reshape(b, nh, nc, 2, p, n)
+            hl = hl.double().cpu().numpy()
+            out["H"] = hl[:, :, :, 0] + hl[:, :, :, 1]
+        else:
+            out["H"] = view(lay.h, (b, nh, nc, p, n))
     return out

@@ -67,14 +67,15 @@ def shape(**kw):
 
 
 def test_workspace_size_formula(lib):
-    for T in (64, 128, 256):
-        for keep in (False, True):
-            s = shape(keep=keep)
+    for T, keep, dt in [(T, k, d) for T in (64, 128, 256) for k in (False, True) for d in ("bf16", "f32")]:
+        if True:
+            s = shape(keep=keep, dtype=dt)
             nc = -(-1000 // T)
             seq = 4 * 2 * 8 * nc * T
             st = 4 * 2 * 8 * nc * 64 * 128
             up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-            want = up(seq) * 4 + up(st) * (2 if keep else 1)
+            own_h = keep or dt == "bf16"  # bf16 h_c is stored split, never over s_c
+            want = up(seq) * 4 + up(st) * (2 if own_h else 1)
             assert ssd.workspace_size(s, T) == want
             lay = ssd.workspace_layout(s, T)
             assert lay.total == want and lay.nchunks == nc and lay.padded_len == nc * T
@@ -82,7 +83,7 @@ def test_workspace_size_formula(lib):
             assert all(o % 256 == 0 for o in offs)
             assert lay.g2_hi == 0 and lay.g2_lo == up(seq) and lay.dt == 2 * up(seq)
             assert lay.w == 3 * up(seq) and lay.s == 4 * up(seq)
-            assert (lay.h == lay.s) != keep
+            assert (lay.h == lay.s) != own_h
 
 
 @pytest.mark.parametrize("bad", [
