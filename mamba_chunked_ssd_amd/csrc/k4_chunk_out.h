@@ -898,6 +898,369 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 }
 
 // ---------------------------------------------------------------------------
+// bf16 path with asynchronous copies (headdim 64, dstate 128)
+// ---------------------------------------------------------------------------
+// Same computation and tile assignment as k4_chunk_out_bf16, with the per-head
+// data moved by the hardware: the x rows and the h_c hi/lo planes of head
+// k + 1 are copied from global memory straight into a second LDS buffer
+// (buffer loads with an LDS destination, 16 bytes per lane) while head k
+// computes from the first, so no registers hold the next head and no VALU
+// stages it; one block barrier per head.  x stays row-major ([token][p]) in
+// LDS: the MFMA x operand, whose contraction index is the token, is read with
+// the gfx950 transposing LDS read (ds_read_b64_tr_b16: within each 16-lane
+// group, lane l receives element l % 4 of lanes 4r + (l % 16) / 4, r = 0..3),
+// which hands every lane 4 tokens of its column; the same read returns the
+// skip term's x in the MFMA output layout.  C fragments live in registers.
+// Rows past the sequence end read as zero (the buffer resource ends at the
+// chunk's last valid row).
+namespace acfg {
+constexpr int P = 64, N = 128, NK = N / 32, PT = P / 16;
+}
+
+template <int T>
+struct AsyncLds {
+    static constexpr size_t x = (size_t)T * acfg::P * 2;      // row-major x tile
+    static constexpr size_t plane = (size_t)acfg::P * acfg::N * 2;  // one h_c plane
+    static constexpr size_t buf = x + 2 * plane;              // one head's x and h_c
+    static constexpr size_t tab = Tables<T>::bytes;
+    static constexpr size_t total = 2 * buf + 2 * tab;
+    static_assert(total <= kLdsBytes, "async chunk-output LDS budget");
+    static_assert((size_t)T * acfg::N * 2 <= buf, "B rows staged in one buffer");
+};
+
+// x tile (128-byte token rows): 16-byte chunk c of row t is stored at chunk
+// c ^ xswz(t), which spreads the 16 rows of one transposing read over all banks
+__device__ __forceinline__ int xswz(int t) { return 2 * ((t >> 1) & 3); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 tr_read(const unsigned char *p) {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p));
+}
+
+// One wave's output tile of one head (skip term included), from buffers
+// xt (x tile) and hp (h_c hi plane, lo plane after it) and tables tb.
+template <int T, int W>
+__device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
+                                                const u32x4 (&cfr)[2][acfg::NK],
+                                                const unsigned char *xt, const unsigned char *hp,
+                                                const Tables<T> &tb, float Dh, int l16, int g4,
+                                                floatx4 (&acc)[2][acfg::PT]) {
+    using WT = WaveTiles<T, W>;
+    using LD = AsyncLds<T>;
+    constexpr int PT = acfg::PT, NK = acfg::NK;
+    constexpr int I0 = WT::I0, I1 = WT::I1;
+    constexpr int XROW = acfg::P * 2, HROW = acfg::N * 2;
+
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
+
+    // ---- inter-chunk term C_i h_c (h_c as hi + lo planes)
+    static_for<NK>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        const int cofs = ((4 * ks + g4) ^ l16) << 4;  // chunk 4 ks + g4 of row 16 pt + l16
+        u32x4 hh[PT], hl[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            hh[pt] = *reinterpret_cast<const u32x4 *>(hp + (16 * pt + l16) * HROW + cofs);
+            hl[pt] = *reinterpret_cast<const u32x4 *>(hp + LD::plane + (16 * pt + l16) * HROW + cofs);
+        }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) acc[ii][pt] = mfma_bf16(cfr[ii][ks], hh[pt], acc[ii][pt]);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) acc[ii][pt] = mfma_bf16(cfr[ii][ks], hl[pt], acc[ii][pt]);
+    });
+    // rows i = 16 I + 4 g4 + r take exp2(G2_i)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        const float4 e = *reinterpret_cast<const float4 *>(tb.e2 + 16 * (ii ? I1 : I0) + 4 * g4);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            acc[ii][pt][0] *= e.x;
+            acc[ii][pt][1] *= e.y;
+            acc[ii][pt][2] *= e.z;
+            acc[ii][pt][3] *= e.w;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- intra-chunk term
+    float mk;  // tile-pair factor of slot k = lane, read back wave-uniformly
+    {
+        const int k = l16 + 16 * g4;
+        const int Ik = k < WT::base1 ? I0 : I1;
+        const int Jk = k < WT::base1 ? k : k - WT::base1;
+        const bool off = k < WT::NSLOT && Jk < Ik;
+        const float m = tile_pair_factor(tb, off ? Ik : 1, off ? Jk : 0);  // in-range reads
+        mk = off ? m : 0.f;
+    }
+    const float rs[2] = {row_factor(tb, I0, tb.gh[16 * I0 + l16], tb.gl[16 * I0 + l16]),
+                         row_factor(tb, I1, tb.gh[16 * I1 + l16], tb.gl[16 * I1 + l16])};
+    auto row_g2 = [&](int I, float &h, float &lo) {
+        int off = 16 * I + l16;
+        asm volatile("" : "+v"(off));
+        h = tb.gh[off];
+        lo = tb.gl[off];
+    };
+    // transposing-read offsets: this lane supplies row 4 g4 + (l16 >> 2) of a
+    // 16-row tile and columns 16 pt + 4 (l16 & 3) .. +3
+    int trb[PT];
+    {
+        const int tr_row = 4 * g4 + (l16 >> 2), tr_a = l16 & 3;
+        const int f = xswz(tr_row);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            trb[pt] = tr_row * XROW + ((((2 * pt) ^ f) | (tr_a >> 1)) << 4) + 8 * (tr_a & 1);
+            asm volatile("" : "+v"(trb[pt]));
+        }
+    }
+    constexpr int NP = WT::NSLOT / 2;
+    struct AOps {
+        u32x4 hi, lo;
+        u32x4 xb[PT];
+    };
+    auto prep = [&](auto qc) {
+        constexpr int k0 = 2 * decltype(qc)::value;
+        constexpr int ii = k0 < WT::base1 ? 0 : 1;
+        constexpr int I = ii ? I1 : I0;
+        constexpr int Ja = k0 - (ii ? WT::base1 : 0), Jb = Ja + 1;
+        const float rma = rs[ii] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0));
+        const float rmb = rs[ii] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), k0 + 1));
+        float gih = 0.f, gil = 0.f;
+        if constexpr (Ja == I || Jb == I) row_g2(I, gih, gil);
+        float va[4], vb[4];
+        tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, rma, tb, va);
+        tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, rmb, tb, vb);
+        const HiLo p0 = split_bf16(va[0], va[1]), p1 = split_bf16(va[2], va[3]);
+        const HiLo p2 = split_bf16(vb[0], vb[1]), p3 = split_bf16(vb[2], vb[3]);
+        AOps o;
+        o.hi = u32x4{p0.hi, p1.hi, p2.hi, p3.hi};
+        o.lo = u32x4{p0.lo, p1.lo, p2.lo, p3.lo};
+        constexpr int JbR = Jb < WT::NT16 ? Jb : WT::NT16 - 1;  // padded tile: weights are 0
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            // tokens 16 Ja + 4 g4 .. +3 then 16 Jb + 4 g4 .. +3 of column 16 pt + l16
+            const u32x2 a = tr_read(xt + 16 * Ja * XROW + trb[pt]);
+            const u32x2 bq = tr_read(xt + 16 * JbR * XROW + trb[pt]);
+            o.xb[pt] = u32x4{a[0], a[1], bq[0], bq[1]};
+        }
+        return o;
+    };
+    AOps cur = prep(std::integral_constant<int, WT::pair_order(0)>{});
+    static_for<NP>([&](auto qc) {
+        constexpr int q = WT::pair_order(decltype(qc)::value);
+        constexpr int ii = 2 * q < WT::base1 ? 0 : 1;
+        constexpr int qn = decltype(qc)::value + 1;
+        AOps nxt;
+        if constexpr (qn < NP) nxt = prep(std::integral_constant<int, WT::pair_order(qn < NP ? qn : 0)>{});
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.hi, cur.xb[pt], acc[ii][pt]);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.lo, cur.xb[pt], acc[ii][pt]);
+        if constexpr (qn < NP) cur = nxt;
+        __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // skip term: the transposing read of row tile I returns x at rows
+    // 16 I + 4 g4 + r, column 16 pt + l16 -- the MFMA output layout
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        constexpr int Ic[2] = {I0, I1};
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const u32x2 xv2 = tr_read(xt + 16 * Ic[ii] * XROW + trb[pt]);
+            acc[ii][pt][0] += Dh * bf16lo(xv2[0]);
+            acc[ii][pt][1] += Dh * bf16hi(xv2[0]);
+            acc[ii][pt][2] += Dh * bf16lo(xv2[1]);
+            acc[ii][pt][3] += Dh * bf16hi(xv2[1]);
+        }
+    }
+}
+
+// Store a wave's two output tiles (rows 16 I + 4 g4 + r, column 16 pt + l16).
+template <typename OutT>
+__device__ __forceinline__ void store_tile(const floatx4 (&acc)[2][acfg::PT], __amdgpu_buffer_rsrc_t yr,
+                                           int NHP, int I0, int I1, int l16, int g4) {
+    constexpr int ES = (int)sizeof(OutT);
+    int lane_off = ((4 * g4) * NHP + l16) * ES;
+    asm volatile("" : "+v"(lane_off));
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        const int I = ii ? I1 : I0;
+#pragma unroll
+        for (int pt = 0; pt < acfg::PT; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                store_out<OutT>(yr, lane_off + (16 * I + r) * NHP * ES + 16 * pt * ES, acc[ii][pt][r]);
+    }
+}
+
+// Derived per-token tables (exp2(G2_t) and the column factor) from the G2
+// pair and dt already in the tables; thread t < T, same arithmetic as
+// token_tables.
+template <int T>
+__device__ __forceinline__ void token_derived(const Tables<T> &tb, int t) {
+    const float gh = tb.gh[t], gl = tb.gl[t], geh = tb.gh[t | 15], gel = tb.gl[t | 15];
+    tb.e2[t] = fast_exp2(gh + gl);
+    tb.cf[t] = fast_exp2((geh - gh) + (gel - gl)) * tb.dt[t];
+}
+
+template <int T, typename OutT>
+__global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
+    const uint16_t *__restrict__ Cm, const float *__restrict__ G2hi, const float *__restrict__ G2lo,
+    const float *__restrict__ DT, const float *__restrict__ Dv, const uint16_t *__restrict__ H,
+    OutT *__restrict__ y, int64_t L, int NH, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
+    using LD = AsyncLds<T>;
+    constexpr int P = acfg::P, N = acfg::N, NK = acfg::NK, PT = acfg::PT;
+    constexpr int NT16 = T / 16;
+    constexpr int NSLOT = NT16 + 2;
+    constexpr int NW = T / 32;
+    constexpr int NTHR = 2 * T;
+
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int hb = bid % nhb;
+    const int bcg = bid / nhb;
+    const int gi = bcg % G;
+    const int bc = bcg / G;
+    const int c = bc % NC;
+    const int64_t b = bc / NC;
+    const int h_begin = gi * HPG + hb * HB;
+    const int h_end = min(h_begin + HB, (gi + 1) * HPG);
+    const int64_t t0 = (int64_t)c * T;
+    const int rows = (int)min<int64_t>(T, L - t0);  // valid tokens in this chunk
+    const int64_t GN = (int64_t)G * N;
+    const int NHP = NH * P;
+    const uint16_t *Bc = Bm + ((b * L + t0) * G + gi) * N;
+    const uint16_t *Cc = Cm + ((b * L + t0) * G + gi) * N;
+
+    auto tables = [&](int k) {
+        return Tables<T>(reinterpret_cast<float *>(lds + 2 * LD::buf + k * LD::tab));
+    };
+    // ---- copies of one head's x rows, h_c planes, G2 pair and dt into buffer k.
+    // x: 1-KiB blocks of 8 token rows; lane l takes 16-byte chunk l % 8 of row
+    // 8 q + l / 8, from the global chunk that the row's swizzle puts there.
+    // h_c: 1-KiB blocks of 4 headdim rows of one plane, XOR-swizzled by row.
+    // G2 / dt: waves w < T / 64 copy tokens 64 w .. +63 (which they also
+    // derive the tables of).
+    const uint32_t x_bytes = (uint32_t)(((rows - 1) * NHP + P) * 2);
+    auto issue = [&](int h, int k) {
+        const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+        int ln = tid & 63;
+        asm volatile("" : "+v"(ln));
+        const uint32_t xb = lds_addr(lds + k * LD::buf);
+        const i32x4 xd = buffer_desc(x + ((b * L + t0) * NH + h) * P, x_bytes);
+        constexpr int XQ = (int)(LD::x / 1024);
+        const int xr = ln >> 3, xl = ((ln & 7) ^ xswz(ln >> 3)) * 16;
+#pragma unroll
+        for (int kk = 0; kk < XQ / NW; ++kk) {
+            const int q = wu + kk * NW;
+            lds_dma_x4(xd, xb + q * 1024, (8 * q + xr) * NHP * 2 + xl);
+        }
+        const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
+                                     (uint32_t)(2 * LD::plane));
+        constexpr int HQ = (int)(2 * LD::plane / 1024);
+#pragma unroll
+        for (int kk = 0; kk < HQ / NW; ++kk) {
+            const int q = wu + kk * NW;
+            const int row = 4 * q + (ln >> 4);  // row of the two stacked planes
+            lds_dma_x4(hd, xb + LD::x + q * 1024, row * (2 * N) + (((ln & 15) ^ (row & 15)) << 4));
+        }
+        if (wu < T / 64) {
+            const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
+            const Tables<T> tb = tables(k);
+            const int voff = (64 * wu + ln) * 4;
+            lds_dma_x1(buffer_desc(G2hi + hoff, T * 4), lds_addr(tb.gh + 64 * wu), voff);
+            lds_dma_x1(buffer_desc(G2lo + hoff, T * 4), lds_addr(tb.gl + 64 * wu), voff);
+            lds_dma_x1(buffer_desc(DT + hoff, T * 4), lds_addr(tb.dt + 64 * wu), voff);
+        }
+    };
+    static_assert((LD::x / 1024) % NW == 0 && (2 * LD::plane / 1024) % NW == 0, "copy split");
+
+    if (h_begin < h_end) issue(h_begin, 0);
+
+    // 16 bytes of row `row` of a (rows x N) bf16 matrix at dstate n0; rows past
+    // the chunk's valid rows read as zero (clamped address, value selected)
+    auto chunk16 = [&](const uint16_t *base, int row, int n0) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + (int64_t)min(row, rows - 1) * GN + n0);
+        return row < rows ? v : u32x4{0u, 0u, 0u, 0u};
+    };
+    // ---- C fragments (registers): lane holds C[t0 + 16 I + l16][32 ks + 8 g4 .. +7]
+    const int I0 = w, I1 = NT16 - 1 - w;
+    u32x4 cfr[2][NK];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks)
+            cfr[ii][ks] = chunk16(Cc, 16 * (ii ? I1 : I0) + l16, 32 * ks + 8 * g4);
+
+    // ---- C B^T tiles (transposed), once per block: B rows staged in buffer 1
+    floatx4 S[NSLOT];
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k) S[k] = zero4();
+    {
+        unsigned char *bt = lds + LD::buf;
+        constexpr int BCH = N / 8;           // 16-byte chunks per B row
+        constexpr int BPT = T * BCH / NTHR;  // per thread
+        constexpr int BB = BPT < 8 ? BPT : 8;
+        static_assert(BPT % BB == 0, "B staging batches");
+#pragma unroll
+        for (int k0 = 0; k0 < BPT; k0 += BB) {
+            u32x4 bv[BB];
+#pragma unroll
+            for (int k = 0; k < BB; ++k) {
+                const int u = tid + (k0 + k) * NTHR;
+                bv[k] = chunk16(Bc, u / BCH, 8 * (u % BCH));
+            }
+#pragma unroll
+            for (int k = 0; k < BB; ++k) {
+                const int u = tid + (k0 + k) * NTHR;
+                const int row = u / BCH, ch = u % BCH;
+                *reinterpret_cast<u32x4 *>(bt + row * (16 * BCH) + ((ch ^ (row & 15)) << 4)) = bv[k];
+            }
+        }
+        __syncthreads();
+        dispatch_wave<NW>(w, [&](auto wc) {
+            cbt_piece<T, NK, NK, 0, false, 0, decltype(wc)::value>(S, cfr, bt + l16 * (16 * BCH),
+                                                                   nullptr, l16, g4);
+        });
+    }
+    lds_dma_wait();  // this wave's copies of the first head have landed
+    if (h_begin < h_end && tid < T) token_derived(tables(0), tid);
+    __syncthreads();  // every wave's copies are visible; buffer 1 (B rows) is free again
+
+    // ---- heads: the copies for head i + 1 run while head i computes
+    floatx4 acc[2][PT];
+    const uint32_t y_bytes = (uint32_t)(((rows - 1) * NHP + P) * sizeof(OutT));
+    auto y_head = [&](int h) { return buffer_rsrc(y + ((b * L + t0) * NH + h) * P, y_bytes); };
+    for (int i = 0; h_begin + i < h_end; ++i) {
+        const int h = h_begin + i, cur = i & 1;
+        const LaneIds id = opaque_lane_ids(tid);
+        if (i > 0) store_tile<OutT>(acc, y_head(h - 1), NHP, id.w, NT16 - 1 - id.w, id.l16, id.g4);
+        if (h + 1 < h_end) issue(h + 1, cur ^ 1);
+        const unsigned char *xt = lds + cur * LD::buf;
+        const float Dh = (Dv != nullptr) ? Dv[h] : 0.f;
+        dispatch_wave<NW>(id.w, [&](auto wc) {
+            head_wave_async<T, decltype(wc)::value>(S, cfr, xt, xt + LD::x, tables(cur), Dh, id.l16,
+                                                    id.g4, acc);
+        });
+        lds_dma_wait();  // this wave's copies of the next head have landed
+        if (h + 1 < h_end && tid < T) token_derived(tables(cur ^ 1), tid);
+        __syncthreads();
+    }
+    if (h_begin < h_end) store_tile<OutT>(acc, y_head(h_end - 1), NHP, I0, I1, l16, g4);
+}
+
+// ---------------------------------------------------------------------------
 // launch: InT is the input element type, OutT the element type of y
 // ---------------------------------------------------------------------------
 template <int T, int P, int NKMAX, typename OutT>
@@ -933,6 +1296,22 @@ hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, cons
     return hipGetLastError();
 }
 
+template <int T, typename OutT>
+hipError_t launch_bf16_async(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
+                             const void *B, const void *C, G2View G2, const float *DT, const float *D,
+                             const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
+    constexpr auto kern = k4_chunk_out_bf16_async<T, OutT>;
+    constexpr size_t lds = AsyncLds<T>::total;
+    if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
+    launch_kernel(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream, ev,
+                  static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
+                  static_cast<const uint16_t *>(C), G2.hi, G2.lo, DT, D,
+                  reinterpret_cast<const uint16_t *>(H),  // hi/lo bf16 planes
+                  static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.ngroups, (int)p.nchunks,
+                  p.padded_len, (int)p.heads_per_group, HB, nhb);
+    return hipGetLastError();
+}
+
 template <typename InT, typename OutT, int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
                      G2View G2, const float *DT, const float *D, const float *H, void *y,
@@ -942,6 +1321,9 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
     if (blocks == 0) return hipSuccess;
     if constexpr (sizeof(InT) == 2) {
+        if constexpr (P == acfg::P)
+            if (p.dstate == acfg::N)
+                return launch_bf16_async<T, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
         if (p.dstate <= 128)
             return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
         return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);

@@ -81,4 +81,37 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int o
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Copies from a raw buffer straight into LDS (the load's LDS-destination
+// form): lane l's 16 (or 4) bytes land at lds_addr + 16 l (+ 4 l), where
+// lds_addr is a wave-uniform LDS byte address (it goes through M0, which
+// needs one wait state before the load).  The range check applies to voffset
+// only, so every per-lane offset goes there.  They are issued as inline
+// assembly: the compiler neither tracks nor waits for them (it would
+// otherwise wait for every pending copy before any LDS read it cannot prove
+// disjoint), so the caller waits (lds_dma_wait) before the destination is
+// read -- by the issuing wave, or by others after a barrier.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_desc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffffu), (int32_t)bytes, 0x00020000};
+}
+template <typename Ptr>
+__device__ __forceinline__ uint32_t lds_addr(Ptr p) {
+    typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+    return (uint32_t)reinterpret_cast<uintptr_t>((lds_byte *)(p));
+}
+__device__ __forceinline__ void lds_dma_x4(const i32x4 &desc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds), "s"(desc)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_x1(const i32x4 &desc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds), "s"(desc)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace ssd

@@ -38,6 +38,8 @@ STAGE_SHAPES = [
     (1, 100, 2, 64, 128, 1, 256),
     (1, 512, 2, 64, 256, 2, 256),
     (2, 130, 4, 128, 80, 2, 64),
+    (1, 600, 8, 64, 128, 1, 128),
+    (2, 1000, 6, 64, 128, 2, 256),
 ]
 
 
