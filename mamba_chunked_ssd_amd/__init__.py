@@ -78,6 +78,7 @@ class WorkspaceLayout(ctypes.Structure):
         ("w", ctypes.c_size_t),
         ("s", ctypes.c_size_t),
         ("h", ctypes.c_size_t),
+        ("cb", ctypes.c_size_t),
         ("total", ctypes.c_size_t),
         ("nchunks", ctypes.c_int64),
         ("padded_len", ctypes.c_int64),

@@ -115,7 +115,7 @@ hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, G2Pair G2, 
     dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadsPerBlock - 1) / kHeadsPerBlock),
               (unsigned)p.batch);
     launch_kernel((k1_cumsum<Tin, T>), grid, dim3(64 * kHeadsPerBlock), 0, stream, ev, dt, A,
-                       G2.hi, G2.lo, DT, W, p.seqlen, (int)p.nheads, p.padded_len);
+                  G2.hi, G2.lo, DT, W, p.seqlen, (int)p.nheads, p.padded_len);
     return hipGetLastError();
 }
 

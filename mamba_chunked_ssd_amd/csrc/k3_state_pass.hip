@@ -20,6 +20,14 @@
 // halves, so h is written split: per (batch, head, chunk) a hi plane and a lo
 // plane of (headdim, dstate) bf16 (hi = bf16(h), lo = bf16(h - hi)), in a
 // region of its own; the final state stays fp32.
+//
+// The same launch also computes, in extra blocks at the front of the grid,
+// the C B^T tiles that the chunk output reads (bf16 problems with headdim 64
+// and dstate 128): a little MFMA work that depends only on B and C, so it runs
+// beside the memory-bound stream instead of on the chunk output's critical
+// path ("Mamba-2 architecture": the C B^T factor of the chunk output).
+#include <climits>
+
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
@@ -29,13 +37,11 @@ namespace {
 constexpr int kDepth = 8;
 
 template <bool kSplit>
-__global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
-                                                     const float *__restrict__ G2hi,
-                                                     const float *__restrict__ G2lo,
-                                                     const float *init, float *final_states,
-                                                     int64_t n_vec, int64_t pn_vec,
-                                                     int64_t nchunks, int64_t Lp, int T) {
-    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index over (bh, pn)
+__device__ __forceinline__ void state_pass_body(const float *S, float *H, const float *__restrict__ G2hi,
+                                                const float *__restrict__ G2lo, const float *init,
+                                                float *final_states, int64_t n_vec, int64_t pn_vec,
+                                                int64_t nchunks, int64_t Lp, int T, int64_t blk) {
+    const int64_t v = blk * 256 + threadIdx.x;  // float4 index over (bh, pn)
     if (v >= n_vec) return;
     const int64_t bh = v / pn_vec;
     const int64_t e = v % pn_vec;
@@ -80,14 +86,119 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
     if (final_states != nullptr) reinterpret_cast<float4 *>(final_states)[bh * pn_vec + e] = h;
 }
 
+template <bool kSplit>
+__global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
+                                                     const float *__restrict__ G2hi,
+                                                     const float *__restrict__ G2lo,
+                                                     const float *init, float *final_states,
+                                                     int64_t n_vec, int64_t pn_vec,
+                                                     int64_t nchunks, int64_t Lp, int T) {
+    state_pass_body<kSplit>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp, T,
+                            blockIdx.x);
+}
+
+// C B^T tiles for the chunk-output stage (bf16 B and C, dstate 128): tile
+// (w, k) of (batch, chunk, group) is the 16 x 16 block (I, J) of
+// S_ij = C_i . B_j that the chunk output's wave w keeps in its slot k: I = w,
+// J = k for k < (w + 2) & ~1, else I = T/16 - 1 - w and J = k minus that.
+// Four MFMAs over dstate in the MFMA output layout (lane 16 q + m holds
+// S_{16I+m, 16J+4q+r}, r = 0..3), one float4 per lane, 1 KiB per tile.
+// Blocks past the diagonal are written as zero.  Each wave takes kCbPerWave
+// tiles; these blocks run at the front of the state-passing grid, beside the
+// memory-bound stream.
+constexpr int kCbPerWave = 4;
+
+template <int T>
+__device__ __forceinline__ void cb_tiles(const uint16_t *__restrict__ Bm,
+                                         const uint16_t *__restrict__ Cm, float *__restrict__ CB,
+                                         int64_t seqlen, int G, int64_t nc, int64_t ntiles) {
+    constexpr int N = 128;
+    constexpr int NT16 = T / 16, NSLOT = NT16 + 2, NSL = (T / 32) * NSLOT;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t GN = (int64_t)G * N;
+#pragma unroll 1
+    for (int it = 0; it < kCbPerWave; ++it) {
+        const int64_t s = gw * kCbPerWave + it;  // (b, c, g, w, k) flattened
+        if (s >= ntiles) return;
+        const int rem = (int)(s % NSL);
+        const int64_t bcg = s / NSL;
+        const int g = (int)(bcg % G);
+        const int64_t bc = bcg / G;
+        const int64_t c = bc % nc, b = bc / nc;
+        const int w = rem / NSLOT, k = rem % NSLOT;
+        const int I0 = w, I1 = NT16 - 1 - w, base1 = (I0 + 2) & ~1;
+        const int I = k < base1 ? I0 : I1, J = k < base1 ? k : k - base1;
+        const int64_t t0 = c * T;
+        const int rows = (int)min<int64_t>(T, seqlen - t0);
+        floatx4 acc = zero4();
+        if (J <= I) {
+            const uint16_t *Bc = Bm + ((b * seqlen + t0) * G + g) * N;
+            const uint16_t *Cc = Cm + ((b * seqlen + t0) * G + g) * N;
+            // 16 bytes of a chunk row at dstate n0; rows past seqlen read as zero
+            auto row16 = [&](const uint16_t *base, int row, int n0) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(base + (int64_t)min(row, rows - 1) * GN + n0);
+                return row < rows ? v : u32x4{0u, 0u, 0u, 0u};
+            };
+            u32x4 bf[N / 32], cf[N / 32];
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks) {
+                bf[ks] = row16(Bc, 16 * J + l16, 32 * ks + 8 * g4);
+                cf[ks] = row16(Cc, 16 * I + l16, 32 * ks + 8 * g4);
+            }
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks) acc = mfma_bf16(bf[ks], cf[ks], acc);
+        }
+        reinterpret_cast<floatx4 *>(CB)[s * 64 + lane] = acc;
+    }
+}
+
+template <int T>
+__global__ __launch_bounds__(256) void k3_state_pass_cb(const float *S, float *H,
+                                                        const float *__restrict__ G2hi,
+                                                        const float *__restrict__ G2lo,
+                                                        const float *init, float *final_states,
+                                                        int64_t n_vec, int64_t pn_vec,
+                                                        int64_t nchunks, int64_t Lp,
+                                                        const uint16_t *__restrict__ Bm,
+                                                        const uint16_t *__restrict__ Cm,
+                                                        float *__restrict__ CB, int64_t seqlen,
+                                                        int G, int64_t ntiles, int ncb) {
+    if ((int)blockIdx.x < ncb)
+        cb_tiles<T>(Bm, Cm, CB, seqlen, G, nchunks, ntiles);
+    else
+        state_pass_body<true>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp, T,
+                              (int64_t)blockIdx.x - ncb);
+}
+
 }  // namespace
 
 hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View G2,
-                             const float *init, float *final_states, hipStream_t stream, const LaunchEvents &ev) {
+                             const float *init, float *final_states, const void *B,
+                             const void *C, float *CB, hipStream_t stream, const LaunchEvents &ev) {
     const int64_t pn_vec = p.headdim * p.dstate / 4;
     const int64_t n_vec = p.batch * p.nheads * pn_vec;
     if (n_vec == 0) return hipSuccess;
     const int64_t blocks = (n_vec + 255) / 256;
+    const int64_t ntiles = uses_cb_tiles(p) ? p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) : 0;
+    if (ntiles > 0) {
+        const int64_t ncb = (ntiles + 4 * kCbPerWave - 1) / (4 * kCbPerWave);
+        if (blocks + ncb > INT_MAX) return hipErrorInvalidValue;
+        const auto *Bm = static_cast<const uint16_t *>(B);
+        const auto *Cm = static_cast<const uint16_t *>(C);
+#define SSD_K3_CB(TT)                                                                              \
+    launch_kernel(k3_state_pass_cb<TT>, dim3((unsigned)(blocks + ncb)), dim3(256), 0, stream, ev, S, \
+                  H, G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len, Bm,  \
+                  Cm, CB, p.seqlen, (int)p.ngroups, ntiles, (int)ncb)
+        switch (p.chunk) {
+            case 64: SSD_K3_CB(64); break;
+            case 128: SSD_K3_CB(128); break;
+            case 256: SSD_K3_CB(256); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef SSD_K3_CB
+        return hipGetLastError();
+    }
     if (p.bf16)
         launch_kernel(k3_state_pass<true>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H,
                       G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,

@@ -61,6 +61,10 @@ namespace k4 {
 // gfx950 LDS per CU (and the most one block may use)
 constexpr size_t kLdsBytes = 160 * 1024;
 
+#ifndef K4_SCHED_PATTERN
+#define K4_SCHED_PATTERN 1
+#endif
+
 // Wave w owns row tiles I0 = w and I1 = T/16 - 1 - w.  Its S slots are laid
 // out as [I0: J = 0..I0][pad to even][I1: J = 0..I1][pad to even]; the total
 // is always T/16 + 2 and a pair (2q, 2q + 1) never straddles the two tiles.
@@ -246,10 +250,13 @@ struct WaveTiles {
     }
 };
 
-// tile_values with the tile relation known at compile time
-template <int T, int J, int I>
+// tile_values with the tile relation known at compile time.  With kSkip the
+// diagonal tile also carries the skip term: D is added to the weight of j = i
+// (y_i = sum_j W_ij x_j + D x_i), so no separate pass over x is needed.
+template <int T, int J, int I, bool kSkip = false>
 __device__ __forceinline__ void tile_values_ct(const floatx4 &s, int l16, int g4, float gih, float gil,
-                                               float rm, const Tables<T> &tb, float (&v)[4]) {
+                                               float rm, const Tables<T> &tb, float (&v)[4],
+                                               float Dh = 0.f) {
     if constexpr (J > I) {
         v[0] = v[1] = v[2] = v[3] = 0.f;
     } else if constexpr (J < I) {
@@ -269,7 +276,10 @@ __device__ __forceinline__ void tile_values_ct(const floatx4 &s, int l16, int g4
         for (int r = 0; r < 4; ++r) {
             const bool keep = (4 * g4 + r) <= l16;  // j <= i (diagonal kept)
             const float arg = keep ? ((gih - hv[r]) + (gil - lv[r])) : -INFINITY;
-            v[r] = keep ? s[r] * (fast_exp2(arg) * dv[r]) : 0.f;
+            if constexpr (kSkip)
+                v[r] = keep ? fmaf(s[r], fast_exp2(arg) * dv[r], (4 * g4 + r) == l16 ? Dh : 0.f) : 0.f;
+            else
+                v[r] = keep ? s[r] * (fast_exp2(arg) * dv[r]) : 0.f;
         }
     }
 }
@@ -940,20 +950,43 @@ __device__ __forceinline__ u32x2 tr_read(const unsigned char *p) {
 
 // One wave's output tile of one head (skip term included), from buffers
 // xt (x tile) and hp (h_c hi plane, lo plane after it) and tables tb.
-template <int T, int W>
+// Rows 16 I + 4 g4 + r (r = 0..3), column 16 pt + l16 of one head's y.
+template <typename OutT>
+__device__ __forceinline__ void store_quad(const floatx4 &v, __amdgpu_buffer_rsrc_t yr, int NHP,
+                                           int I, int pt, int l16, int g4) {
+    constexpr int ES = (int)sizeof(OutT);
+    int lane_off = ((4 * g4) * NHP + l16) * ES;
+    asm volatile("" : "+v"(lane_off));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_out<OutT>(yr, lane_off + (16 * I + r) * NHP * ES + 16 * pt * ES, v[r]);
+}
+
+// acc holds the previous head's finished tile on entry (stored through yprev,
+// spread over the inter-chunk MFMAs; a resource of 0 bytes drops them) and
+// this head's tile on return.  pre(s), s = 0 .. 4, issues piece s of the next
+// head's copies: one per inter-chunk step, the last before the intra-chunk
+// MFMAs, so the memory traffic flows while the MFMAs run.
+template <int T, int W, typename OutT, typename Pre>
 __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
                                                 const u32x4 (&cfr)[2][acfg::NK],
                                                 const unsigned char *xt, const unsigned char *hp,
                                                 const Tables<T> &tb, float Dh, int l16, int g4,
-                                                floatx4 (&acc)[2][acfg::PT]) {
+                                                floatx4 (&acc)[2][acfg::PT],
+                                                __amdgpu_buffer_rsrc_t yprev, int NHP, Pre &&pre) {
     using WT = WaveTiles<T, W>;
     using LD = AsyncLds<T>;
     constexpr int PT = acfg::PT, NK = acfg::NK;
     constexpr int I0 = WT::I0, I1 = WT::I1;
     constexpr int XROW = acfg::P * 2, HROW = acfg::N * 2;
+    static_assert(NK == PT, "one (row tile, column tile) pair of stores per step and tile");
 
+    floatx4 prev[2][PT];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
+    for (int pt = 0; pt < PT; ++pt) {
+        prev[0][pt] = acc[0][pt];
+        prev[1][pt] = acc[1][pt];
+        acc[0][pt] = acc[1][pt] = zero4();
+    }
 
     // ---- inter-chunk term C_i h_c (h_c as hi + lo planes)
     static_for<NK>([&](auto kc) {
@@ -973,7 +1006,11 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) acc[ii][pt] = mfma_bf16(cfr[ii][ks], hl[pt], acc[ii][pt]);
+        pre(ks);
+        store_quad<OutT>(prev[0][ks], yprev, NHP, I0, ks, l16, g4);
+        store_quad<OutT>(prev[1][ks], yprev, NHP, I1, ks, l16, g4);
     });
+    pre(4);
     // rows i = 16 I + 4 g4 + r take exp2(G2_i)
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
@@ -1033,8 +1070,8 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         float gih = 0.f, gil = 0.f;
         if constexpr (Ja == I || Jb == I) row_g2(I, gih, gil);
         float va[4], vb[4];
-        tile_values_ct<T, Ja, I>(S[k0], l16, g4, gih, gil, rma, tb, va);
-        tile_values_ct<T, Jb, I>(S[k0 + 1], l16, g4, gih, gil, rmb, tb, vb);
+        tile_values_ct<T, Ja, I, true>(S[k0], l16, g4, gih, gil, rma, tb, va, Dh);
+        tile_values_ct<T, Jb, I, true>(S[k0 + 1], l16, g4, gih, gil, rmb, tb, vb, Dh);
         const HiLo p0 = split_bf16(va[0], va[1]), p1 = split_bf16(va[2], va[3]);
         const HiLo p2 = split_bf16(vb[0], vb[1]), p3 = split_bf16(vb[2], vb[3]);
         AOps o;
@@ -1062,23 +1099,26 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.lo, cur.xb[pt], acc[ii][pt]);
         if constexpr (qn < NP) cur = nxt;
+        // Interleave the next pair's VALU work with this pair's MFMAs: a
+        // wave64 VALU op takes 4 cycles and an MFMA 16, so four or five of
+        // them run under each MFMA instead of waiting for the whole group.
+#if K4_SCHED_PATTERN == 1
+#pragma unroll
+        for (int k = 0; k < 2 * PT; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        }
+#elif K4_SCHED_PATTERN == 2
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+        for (int k = 0; k < 2 * PT; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+#endif
         __builtin_amdgcn_sched_barrier(0);
     });
-
-    // skip term: the transposing read of row tile I returns x at rows
-    // 16 I + 4 g4 + r, column 16 pt + l16 -- the MFMA output layout
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        constexpr int Ic[2] = {I0, I1};
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const u32x2 xv2 = tr_read(xt + 16 * Ic[ii] * XROW + trb[pt]);
-            acc[ii][pt][0] += Dh * bf16lo(xv2[0]);
-            acc[ii][pt][1] += Dh * bf16hi(xv2[0]);
-            acc[ii][pt][2] += Dh * bf16lo(xv2[1]);
-            acc[ii][pt][3] += Dh * bf16hi(xv2[1]);
-        }
-    }
 }
 
 // Store a wave's two output tiles (rows 16 I + 4 g4 + r, column 16 pt + l16).
@@ -1111,7 +1151,7 @@ __device__ __forceinline__ void token_derived(const Tables<T> &tb, int t) {
 
 template <int T, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
+    const uint16_t *__restrict__ x, const float *__restrict__ CBt,
     const uint16_t *__restrict__ Cm, const float *__restrict__ G2hi, const float *__restrict__ G2lo,
     const float *__restrict__ DT, const float *__restrict__ Dv, const uint16_t *__restrict__ H,
     OutT *__restrict__ y, int64_t L, int NH, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
@@ -1140,7 +1180,6 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     const int rows = (int)min<int64_t>(T, L - t0);  // valid tokens in this chunk
     const int64_t GN = (int64_t)G * N;
     const int NHP = NH * P;
-    const uint16_t *Bc = Bm + ((b * L + t0) * G + gi) * N;
     const uint16_t *Cc = Cm + ((b * L + t0) * G + gi) * N;
 
     auto tables = [&](int k) {
@@ -1153,29 +1192,30 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     // G2 / dt: waves w < T / 64 copy tokens 64 w .. +63 (which they also
     // derive the tables of).
     const uint32_t x_bytes = (uint32_t)(((rows - 1) * NHP + P) * 2);
-    auto issue = [&](int h, int k) {
+    // Piece s (0 .. 3) of head h's x and h_c copies, and the G2 / dt copies
+    // (piece 4); the pieces go out spread over the previous head's MFMAs.
+    constexpr int XQ = (int)(LD::x / 1024), HQ = (int)(2 * LD::plane / 1024);
+    constexpr int XPW = XQ / NW, HPW = HQ / NW;  // copies per wave
+    static_assert(XQ % NW == 0 && HQ % NW == 0 && XPW == 4 && HPW % 4 == 0, "copy split");
+    auto issue_piece = [&](int h, int k, int s) {
         const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
         int ln = tid & 63;
         asm volatile("" : "+v"(ln));
         const uint32_t xb = lds_addr(lds + k * LD::buf);
-        const i32x4 xd = buffer_desc(x + ((b * L + t0) * NH + h) * P, x_bytes);
-        constexpr int XQ = (int)(LD::x / 1024);
-        const int xr = ln >> 3, xl = ((ln & 7) ^ xswz(ln >> 3)) * 16;
-#pragma unroll
-        for (int kk = 0; kk < XQ / NW; ++kk) {
-            const int q = wu + kk * NW;
+        if (s < 4) {
+            const i32x4 xd = buffer_desc(x + ((b * L + t0) * NH + h) * P, x_bytes);
+            const int xr = ln >> 3, xl = ((ln & 7) ^ xswz(ln >> 3)) * 16;
+            const int q = wu + s * NW;
             lds_dma_x4(xd, xb + q * 1024, (8 * q + xr) * NHP * 2 + xl);
-        }
-        const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
-                                     (uint32_t)(2 * LD::plane));
-        constexpr int HQ = (int)(2 * LD::plane / 1024);
+            const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
+                                         (uint32_t)(2 * LD::plane));
 #pragma unroll
-        for (int kk = 0; kk < HQ / NW; ++kk) {
-            const int q = wu + kk * NW;
-            const int row = 4 * q + (ln >> 4);  // row of the two stacked planes
-            lds_dma_x4(hd, xb + LD::x + q * 1024, row * (2 * N) + (((ln & 15) ^ (row & 15)) << 4));
-        }
-        if (wu < T / 64) {
+            for (int kk = s * (HPW / 4); kk < (s + 1) * (HPW / 4); ++kk) {
+                const int qh = wu + kk * NW;
+                const int row = 4 * qh + (ln >> 4);  // row of the two stacked planes
+                lds_dma_x4(hd, xb + LD::x + qh * 1024, row * (2 * N) + (((ln & 15) ^ (row & 15)) << 4));
+            }
+        } else if (wu < T / 64) {
             const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
             const Tables<T> tb = tables(k);
             const int voff = (64 * wu + ln) * 4;
@@ -1184,9 +1224,10 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
             lds_dma_x1(buffer_desc(DT + hoff, T * 4), lds_addr(tb.dt + 64 * wu), voff);
         }
     };
-    static_assert((LD::x / 1024) % NW == 0 && (2 * LD::plane / 1024) % NW == 0, "copy split");
-
-    if (h_begin < h_end) issue(h_begin, 0);
+    auto issue = [&](int h, int k) {
+#pragma unroll
+        for (int s = 0; s < 5; ++s) issue_piece(h, k, s);
+    };
 
     // 16 bytes of row `row` of a (rows x N) bf16 matrix at dstate n0; rows past
     // the chunk's valid rows read as zero (clamped address, value selected)
@@ -1203,55 +1244,42 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
         for (int ks = 0; ks < NK; ++ks)
             cfr[ii][ks] = chunk16(Cc, 16 * (ii ? I1 : I0) + l16, 32 * ks + 8 * g4);
 
-    // ---- C B^T tiles (transposed), once per block: B rows staged in buffer 1
+    // ---- C B^T tiles of this wave's slots, computed once per chunk by the
+    // cumsum stage; then the first head's copies (after every compiler-visible
+    // load, whose waits would otherwise count them)
     floatx4 S[NSLOT];
-#pragma unroll
-    for (int k = 0; k < NSLOT; ++k) S[k] = zero4();
     {
-        unsigned char *bt = lds + LD::buf;
-        constexpr int BCH = N / 8;           // 16-byte chunks per B row
-        constexpr int BPT = T * BCH / NTHR;  // per thread
-        constexpr int BB = BPT < 8 ? BPT : 8;
-        static_assert(BPT % BB == 0, "B staging batches");
+        const floatx4 *cb = reinterpret_cast<const floatx4 *>(CBt) +
+                            ((((b * NC + c) * G + gi) * NW + w) * NSLOT) * 64 + lane;
 #pragma unroll
-        for (int k0 = 0; k0 < BPT; k0 += BB) {
-            u32x4 bv[BB];
-#pragma unroll
-            for (int k = 0; k < BB; ++k) {
-                const int u = tid + (k0 + k) * NTHR;
-                bv[k] = chunk16(Bc, u / BCH, 8 * (u % BCH));
-            }
-#pragma unroll
-            for (int k = 0; k < BB; ++k) {
-                const int u = tid + (k0 + k) * NTHR;
-                const int row = u / BCH, ch = u % BCH;
-                *reinterpret_cast<u32x4 *>(bt + row * (16 * BCH) + ((ch ^ (row & 15)) << 4)) = bv[k];
-            }
-        }
-        __syncthreads();
-        dispatch_wave<NW>(w, [&](auto wc) {
-            cbt_piece<T, NK, NK, 0, false, 0, decltype(wc)::value>(S, cfr, bt + l16 * (16 * BCH),
-                                                                   nullptr, l16, g4);
-        });
+        for (int k = 0; k < NSLOT; ++k) S[k] = cb[k * 64];
     }
+    if (h_begin < h_end) issue(h_begin, 0);
     lds_dma_wait();  // this wave's copies of the first head have landed
     if (h_begin < h_end && tid < T) token_derived(tables(0), tid);
-    __syncthreads();  // every wave's copies are visible; buffer 1 (B rows) is free again
+    __syncthreads();  // every wave's copies are visible
 
     // ---- heads: the copies for head i + 1 run while head i computes
     floatx4 acc[2][PT];
     const uint32_t y_bytes = (uint32_t)(((rows - 1) * NHP + P) * sizeof(OutT));
     auto y_head = [&](int h) { return buffer_rsrc(y + ((b * L + t0) * NH + h) * P, y_bytes); };
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
     for (int i = 0; h_begin + i < h_end; ++i) {
         const int h = h_begin + i, cur = i & 1;
         const LaneIds id = opaque_lane_ids(tid);
-        if (i > 0) store_tile<OutT>(acc, y_head(h - 1), NHP, id.w, NT16 - 1 - id.w, id.l16, id.g4);
-        if (h + 1 < h_end) issue(h + 1, cur ^ 1);
+        const bool more = h + 1 < h_end;
+        auto pre = [&](int s) {
+            if (more) issue_piece(h + 1, cur ^ 1, s);
+        };
         const unsigned char *xt = lds + cur * LD::buf;
         const float Dh = (Dv != nullptr) ? Dv[h] : 0.f;
+        // the previous head's y goes out during this head's first MFMAs
+        const auto yprev = buffer_rsrc(y + ((b * L + t0) * NH + (i > 0 ? h - 1 : h)) * P,
+                                       i > 0 ? y_bytes : 0u);
         dispatch_wave<NW>(id.w, [&](auto wc) {
-            head_wave_async<T, decltype(wc)::value>(S, cfr, xt, xt + LD::x, tables(cur), Dh, id.l16,
-                                                    id.g4, acc);
+            head_wave_async<T, decltype(wc)::value, OutT>(S, cfr, xt, xt + LD::x, tables(cur), Dh,
+                                                          id.l16, id.g4, acc, yprev, NHP, pre);
         });
         lds_dma_wait();  // this wave's copies of the next head have landed
         if (h + 1 < h_end && tid < T) token_derived(tables(cur ^ 1), tid);
@@ -1265,7 +1293,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
 // ---------------------------------------------------------------------------
 template <int T, int P, int NKMAX, typename OutT>
 hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
-                          const void *B, const void *C, G2View G2, const float *DT, const float *D,
+                          const void *B, const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                           const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
     constexpr auto kern = k4_chunk_out_bf16<T, P, NKMAX, OutT>;
     constexpr size_t lds = Bf16Lds<T, P, NKMAX>::total;
@@ -1282,7 +1310,7 @@ hipError_t launch_bf16_in(const Problem &p, int HB, int nhb, int64_t blocks, con
 
 template <int T, int P, typename OutT>
 hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
-                         const void *B, const void *C, G2View G2, const float *DT, const float *D,
+                         const void *B, const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                          const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
     constexpr auto kern = k4_chunk_out_f32<T, P, OutT>;
     constexpr size_t lds = F32Lds<T, P>::total;
@@ -1298,14 +1326,14 @@ hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, cons
 
 template <int T, typename OutT>
 hipError_t launch_bf16_async(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
-                             const void *B, const void *C, G2View G2, const float *DT, const float *D,
+                             const void *B, const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                              const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
     constexpr auto kern = k4_chunk_out_bf16_async<T, OutT>;
     constexpr size_t lds = AsyncLds<T>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
     launch_kernel(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream, ev,
-                  static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
-                  static_cast<const uint16_t *>(C), G2.hi, G2.lo, DT, D,
+                  static_cast<const uint16_t *>(x), CB, static_cast<const uint16_t *>(C), G2.hi,
+                  G2.lo, DT, D,
                   reinterpret_cast<const uint16_t *>(H),  // hi/lo bf16 planes
                   static_cast<OutT *>(y), p.seqlen, (int)p.nheads, (int)p.ngroups, (int)p.nchunks,
                   p.padded_len, (int)p.heads_per_group, HB, nhb);
@@ -1314,7 +1342,7 @@ hipError_t launch_bf16_async(const Problem &p, int HB, int nhb, int64_t blocks, 
 
 template <typename InT, typename OutT, int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
-                     G2View G2, const float *DT, const float *D, const float *H, void *y,
+                     const float *CB, G2View G2, const float *DT, const float *D, const float *H, void *y,
                      hipStream_t stream, const LaunchEvents &ev) {
     const int HB = plan.k4_heads_per_block;
     const int nhb = (int)((p.heads_per_group + HB - 1) / HB);
@@ -1322,25 +1350,25 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
     if (blocks == 0) return hipSuccess;
     if constexpr (sizeof(InT) == 2) {
         if constexpr (P == acfg::P)
-            if (p.dstate == acfg::N)
-                return launch_bf16_async<T, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
+            if (uses_cb_tiles(p))
+                return launch_bf16_async<T, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
         if (p.dstate <= 128)
-            return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
-        return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
+            return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
+        return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
     } else {
-        return launch_f32_in<T, P, OutT>(p, HB, nhb, blocks, x, B, C, G2, DT, D, H, y, stream, ev);
+        return launch_f32_in<T, P, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
     }
 }
 
 template <typename InT, typename OutT>
 hipError_t launch(const Problem &p, const Plan &plan, const void *x, const void *B, const void *C,
-                  G2View G2, const float *DT, const float *D, const float *H, void *y,
+                  const float *CB, G2View G2, const float *DT, const float *D, const float *H, void *y,
                   hipStream_t stream, const LaunchEvents &ev) {
 #define SSD_K4_P(T)                                                                              \
     switch (p.headdim) {                                                                         \
-        case 32: return launch_tp<InT, OutT, T, 32>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);  \
-        case 64: return launch_tp<InT, OutT, T, 64>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);  \
-        case 128: return launch_tp<InT, OutT, T, 128>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev); \
+        case 32: return launch_tp<InT, OutT, T, 32>(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev);  \
+        case 64: return launch_tp<InT, OutT, T, 64>(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev);  \
+        case 128: return launch_tp<InT, OutT, T, 128>(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev); \
         default: return hipErrorInvalidValue;                                                    \
     }
     switch (p.chunk) {
@@ -1354,10 +1382,10 @@ hipError_t launch(const Problem &p, const Plan &plan, const void *x, const void 
 
 // One explicit instantiation per translation unit (compiled in parallel).
 hipError_t launch_bf16_in_f32_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                                  const void *C, G2View G2, const float *DT, const float *D,
+                                  const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                                   const float *H, void *y, hipStream_t stream, const LaunchEvents &ev);
 hipError_t launch_bf16_in_bf16_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                                   const void *C, G2View G2, const float *DT, const float *D,
+                                   const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                                    const float *H, void *y, hipStream_t stream, const LaunchEvents &ev);
 
 }  // namespace k4

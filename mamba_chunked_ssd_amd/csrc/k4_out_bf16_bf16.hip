@@ -6,9 +6,9 @@ namespace ssd {
 namespace k4 {
 
 hipError_t launch_bf16_in_bf16_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                                   const void *C, G2View G2, const float *DT, const float *D,
+                                   const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                                    const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
-    return launch<uint16_t, uint16_t>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);
+    return launch<uint16_t, uint16_t>(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev);
 }
 
 }  // namespace k4

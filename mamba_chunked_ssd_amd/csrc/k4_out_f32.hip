@@ -5,11 +5,11 @@
 namespace ssd {
 
 hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                            const void *C, G2View G2, const float *DT, const float *D,
+                            const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                             const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
-    if (!p.bf16) return k4::launch<float, float>(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);
-    if (p.y_bf16) return k4::launch_bf16_in_bf16_out(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);
-    return k4::launch_bf16_in_f32_out(p, plan, x, B, C, G2, DT, D, H, y, stream, ev);
+    if (!p.bf16) return k4::launch<float, float>(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev);
+    if (p.y_bf16) return k4::launch_bf16_in_bf16_out(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev);
+    return k4::launch_bf16_in_f32_out(p, plan, x, B, C, CB, G2, DT, D, H, y, stream, ev);
 }
 
 }  // namespace ssd

@@ -108,6 +108,10 @@ ssd_workspace_layout layout_for(const Problem &p, bool keep) {
     const bool own_h = keep || p.bf16;
     l.h = own_h ? off : l.s;
     if (own_h) off = align_up(off + states);
+    l.cb = off;
+    if (uses_cb_tiles(p))
+        off = align_up(off + (size_t)p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) * 64 * 4 *
+                                 sizeof(float));
     l.total = off;
     l.nchunks = p.nchunks;
     l.padded_len = p.padded_len;
@@ -246,6 +250,7 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     float *Wf = reinterpret_cast<float *>(ws + lay.w);
     float *S = reinterpret_cast<float *>(ws + lay.s);
     float *Hs = reinterpret_cast<float *>(ws + lay.h);
+    float *CB = reinterpret_cast<float *>(ws + lay.cb);
     const Plan plan = make_plan(p);
 
     // stage i's (start, stop) events, recorded by its kernel's dispatch; a
@@ -272,10 +277,10 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     } else if (!skip(0) || !skip(1)) {
         return SSD_ERROR_LAUNCH;
     }
-    if (launch_state_pass(p, S, Hs, G2v, init, final_states, stream, events_of(2)) != hipSuccess)
+    if (launch_state_pass(p, S, Hs, G2v, init, final_states, B, C, CB, stream, events_of(2)) != hipSuccess)
         return SSD_ERROR_LAUNCH;
     if (p.nchunks > 0) {
-        if (launch_chunk_out(p, plan, x, B, C, G2v, DTf, D, Hs, y, stream, events_of(3)) != hipSuccess)
+        if (launch_chunk_out(p, plan, x, B, C, CB, G2v, DTf, D, Hs, y, stream, events_of(3)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
     } else if (!skip(3)) {
         return SSD_ERROR_LAUNCH;

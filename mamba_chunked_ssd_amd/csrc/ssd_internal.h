@@ -27,6 +27,13 @@ struct Plan {
 
 Plan make_plan(const Problem &p);
 
+// bf16 problems with headdim 64 and dstate 128 take the chunk-output kernel
+// with asynchronous copies; it reads the chunk's C B^T tiles, which stage 3
+// writes once per (batch, chunk, group) into the workspace: cb_slots(T) tiles
+// of 64 lanes x 4 floats each (the layout is described in include/ssd.h).
+inline bool uses_cb_tiles(const Problem &p) { return p.bf16 && p.headdim == 64 && p.dstate == 128; }
+inline int64_t cb_slots(int64_t T) { return (T / 32) * (T / 16 + 2); }
+
 // Each launcher enqueues one kernel on `stream` and returns hipSuccess or the
 // launch error.  Buffers follow the layouts documented in include/ssd.h.
 
@@ -69,15 +76,19 @@ int chunk_state_blocks_per_cu(const Problem &p);
 
 // Stage 3: h_0 = init (or 0); for each chunk store h_c then
 // h_{c+1} = exp2(G2_last,c) h_c + s_c; final = h_nchunks.  H may equal S.
+// When uses_cb_tiles(p), extra blocks of the same launch also write the C B^T
+// tiles (CB) from B and C, beside the memory-bound state stream.
 hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View G2,
-                             const float *init, float *final_states, hipStream_t stream,
-                             const LaunchEvents &ev);
+                             const float *init, float *final_states, const void *B,
+                             const void *C, float *CB, hipStream_t stream, const LaunchEvents &ev);
 
 // Stage 4: chunk output
 // y_i = exp2(G2_i) C_i h_c + sum_{j<=i} exp2(G2_i - G2_j) (C_i . B_j) DT_j x_j + D x_i.
+// CB: the C B^T tiles of stage 1 when uses_cb_tiles(p), else unused.
 hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, const void *B,
-                            const void *C, G2View G2, const float *DT, const float *D,
-                            const float *H, void *y, hipStream_t stream, const LaunchEvents &ev);
+                            const void *C, const float *CB, G2View G2, const float *DT,
+                            const float *D, const float *H, void *y, hipStream_t stream,
+                            const LaunchEvents &ev);
 
 // Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
 // CU).  The template parameter is the kernel itself, so each kernel caches

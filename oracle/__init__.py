@@ -22,6 +22,8 @@ Pass Kernels in NVIDIA CUDA Tile":
   running the recurrence over that chunk alone.
 * :func:`chunk_start_states` -- the state at the start of every chunk, the
   quantity the fwd_pass_state section stores per chunk.
+* :func:`chunk_cb` -- the C B^T factor of the chunk output equation (section
+  "Mamba-2 architecture"): every product C_i . B_j of two tokens of a chunk.
 
 Inputs may be float32 or float64 numpy arrays; they are widened exactly to
 fp64.  bf16 data is passed as float32 arrays holding bf16-representable values
@@ -191,3 +193,21 @@ def chunk_start_states(x, dt, A, B, C, chunk_size: int, h0=None):
     """State at the start of every chunk: (b, nh, nchunks, p, n)."""
     _, _, ck = scan(x, dt, A, B, C, None, h0, ckpt_stride=chunk_size)
     return ck
+
+
+def chunk_cb(B, C, chunk_size: int):
+    """C B^T of every chunk, (b, nchunks, g, T, T), entry [..., i, j] = C_i . B_j
+    for chunk-local tokens i, j ("Accelerating Mamba-2 ...", section "Mamba-2
+    architecture": the C B^T factor of the chunk output, before the decay and
+    the causal mask are applied).  Tokens past seqlen have zero B and C rows.
+    """
+    B, C = _f64(B), _f64(C)
+    bsz, L, g, n = B.shape
+    nc = -(-L // chunk_size)
+    Lp = nc * chunk_size
+    Bs = _pad_tokens(B, Lp).reshape(bsz, nc, chunk_size, g, n)
+    Cs = _pad_tokens(C, Lp).reshape(bsz, nc, chunk_size, g, n)
+    out = np.zeros((bsz, nc, g, chunk_size, chunk_size))
+    for gi in range(g):
+        out[:, :, gi] = np.matmul(Cs[:, :, :, gi, :], Bs[:, :, :, gi, :].transpose(0, 1, 3, 2))
+    return out

@@ -79,4 +79,27 @@ def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = Tru
             out["H"] = hl[:, :, :, 0] + hl[:, :, :, 1]
         else:
             out["H"] = view(lay.h, (b, nh, nc, p, n))
+        if lay.cb < lay.total:
+            out["CB"] = decode_cb(view(lay.cb, (b, nc, g, chunk // 32, chunk // 16 + 2, 64, 4)), chunk)
+    return out
+
+
+def decode_cb(raw, T):
+    """Dense (b, nchunks, g, T, T) C B^T from the tile layout of include/ssd.h
+    (tiles past the diagonal must be zero and are checked here)."""
+    b, nc, g = raw.shape[:3]
+    nt = T // 16
+    out = np.zeros((b, nc, g, T, T))
+    lane = np.arange(64)
+    m, q = lane % 16, lane // 16
+    for w in range(T // 32):
+        base1 = (w + 2) & ~1
+        for k in range(nt + 2):
+            I, J = (w, k) if k < base1 else (nt - 1 - w, k - base1)
+            tile = raw[:, :, :, w, k]
+            if J > I:
+                assert not np.any(tile), "C B^T tile above the diagonal is not zero"
+                continue
+            for r in range(4):
+                out[:, :, :, 16 * I + m, 16 * J + 4 * q + r] = tile[..., r]
     return out

@@ -75,15 +75,23 @@ def test_workspace_size_formula(lib):
             st = 4 * 2 * 8 * nc * 64 * 128
             up = lambda v: (v + 255) // 256 * 256  # noqa: E731
             own_h = keep or dt == "bf16"  # bf16 h_c is stored split, never over s_c
-            want = up(seq) * 4 + up(st) * (2 if own_h else 1)
+            # bf16 with headdim 64, dstate 128: C B^T tiles per (batch, chunk, group),
+            # T/32 x (T/16 + 2) tiles of 1 KiB
+            cb = 2 * nc * 2 * (T // 32) * (T // 16 + 2) * 1024 if dt == "bf16" else 0
+            want = up(seq) * 4 + up(st) * (2 if own_h else 1) + up(cb)
             assert ssd.workspace_size(s, T) == want
             lay = ssd.workspace_layout(s, T)
             assert lay.total == want and lay.nchunks == nc and lay.padded_len == nc * T
-            offs = [lay.g2_hi, lay.g2_lo, lay.dt, lay.w, lay.s, lay.h]
+            offs = [lay.g2_hi, lay.g2_lo, lay.dt, lay.w, lay.s, lay.h, lay.cb]
             assert all(o % 256 == 0 for o in offs)
             assert lay.g2_hi == 0 and lay.g2_lo == up(seq) and lay.dt == 2 * up(seq)
             assert lay.w == 3 * up(seq) and lay.s == 4 * up(seq)
             assert (lay.h == lay.s) != own_h
+            assert lay.cb == want - up(cb)
+    # no tiles for other head / state sizes
+    for kw in (dict(headdim=32), dict(dstate=64)):
+        lay = ssd.workspace_layout(shape(**kw), 256)
+        assert lay.cb == lay.total
 
 
 @pytest.mark.parametrize("bad", [

@@ -63,6 +63,17 @@ def test_stage_parity(dtype, shp):
     # chunk-state weights exp(G_last - G_t) dt_t (fp64 exponent, fp32 exp2)
     Wref = oracle.chunk_state_weights(inp["dt"], inp["A"], T)
     assert nerr(out["W"], Wref) < 1e-5, ("W", nerr(out["W"], Wref))
+    # C B^T tiles (bf16, headdim 64, dstate 128): fp32 sums of exact bf16
+    # products, lower block triangle (blocks past the diagonal are zero).
+    # Bound per entry: n fp32 additions, |err| <= n 2^-24 sum_k |C_ik B_jk|.
+    if dtype == "bf16" and p == 64 and n == 128:
+        blk = np.arange(T) // 16
+        lower = (blk[:, None] >= blk[None, :])
+        cb = oracle.chunk_cb(inp["B"], inp["C"], T) * lower
+        bound = n * 2.0 ** -24 * oracle.chunk_cb(np.abs(inp["B"]), np.abs(inp["C"]), T) * lower
+        assert np.all(np.abs(out["CB"] - cb) <= bound), ("CB", nerr(out["CB"], cb))
+    else:
+        assert "CB" not in out
     # stage 2: per-chunk input states
     S = oracle.chunk_states(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], T)
     assert nerr(out["S"], S) < tol, ("S", nerr(out["S"], S))

@@ -215,3 +215,40 @@ def test_pins_catch_planted_mistake(name, mutant_libs):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, "no pin caught mutant %s" % name
+
+
+def test_chunk_cb_brute_force_and_linear_attention():
+    """chunk_cb against a double loop over token pairs, and -- with A = 0, the
+    linear-attention special case of section "Mamba-2 architecture" -- the
+    masked form sum_{j <= i} (C_i . B_j) dt_j x_j + D x_i of one chunk against
+    the sequential recurrence."""
+    rng = np.random.default_rng(11)
+    b, L, nh, p, n, g, T = 2, 11, 2, 3, 5, 2, 8
+    B = rng.standard_normal((b, L, g, n))
+    C = rng.standard_normal((b, L, g, n))
+    cb = oracle.chunk_cb(B, C, T)
+    assert cb.shape == (b, 2, g, T, T)
+    for bi in range(b):
+        for c in range(2):
+            for gi in range(g):
+                for i in range(T):
+                    for j in range(T):
+                        ti, tj = c * T + i, c * T + j
+                        want = 0.0
+                        if ti < L and tj < L:
+                            want = sum(C[bi, ti, gi, k] * B[bi, tj, gi, k] for k in range(n))
+                        assert abs(cb[bi, c, gi, i, j] - want) < 1e-12
+    # A = 0: one chunk of L tokens, no decay
+    L1 = T
+    x = rng.standard_normal((b, L1, nh, p))
+    dt = rng.uniform(0.1, 1.0, (b, L1, nh))
+    B1, C1 = B[:, :L1], C[:, :L1]
+    D = rng.standard_normal(nh)
+    y, _, _ = oracle.scan(x, dt, np.zeros(nh), B1, C1, D)
+    cb1 = oracle.chunk_cb(B1, C1, T)[:, 0]
+    hpg = nh // g
+    for bi in range(b):
+        for h in range(nh):
+            W = np.tril(cb1[bi, h // hpg]) * dt[bi, :, h][None, :]
+            want = W @ x[bi, :, h] + D[h] * x[bi, :, h]
+            assert np.max(np.abs(y[bi, :, h] - want)) < 1e-10
