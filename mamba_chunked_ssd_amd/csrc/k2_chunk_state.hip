@@ -297,7 +297,18 @@ struct K2WsLds {
     static constexpr size_t buf = (size_t)2 * P * T * 2;  // hi + lo tiles of one head
     static constexpr size_t total = 2 * buf;
     static constexpr bool fits = total <= 160 * 1024;
+    // dstate 128: each consumer wave's 32 B columns (T rows of 64 bytes) fit
+    // in the second buffer
+    static constexpr bool b_cols_fit = (size_t)T * 256 <= buf;
 };
+
+// A consumer wave's 32 columns of the chunk's B rows in LDS: T rows of 64
+// bytes, the 16-byte chunk q of row t at chunk q ^ b_swz(t).  A transposing
+// read (4 consecutive tokens x 16 columns per 16 lanes) by half a wave covers
+// rows t .. t + 3 and t + 8 .. t + 11 (t a multiple of 4): four 64-byte bank
+// quarters (t mod 4), each shared by two rows that the swizzle puts in
+// different halves -- no bank conflicts.
+__device__ __forceinline__ int b_swz(int t) { return 2 * ((t >> 3) & 1); }
 
 template <int T, int P, int NCW>
 __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_ws(
@@ -405,10 +416,46 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
     };
     if (producer && h_begin < h_end) load_x(h_begin);  // in flight during the B^T staging
 
-    // ---- B^T for this chunk, staged by all threads in pieces of dstate
-    //      columns; each consumer wave keeps its fragments in registers.
+    // ---- B for this chunk; each consumer wave keeps its fragments in
+    //      registers.  With dstate 128 each consumer wave copies its own 32
+    //      columns of the chunk's rows straight into the second buffer
+    //      (asynchronous copies, 16 bytes per lane; rows past seqlen read as
+    //      zero) and reads them back transposed, 4 tokens per read -- no
+    //      barrier, and the producers stage head 0 into the first buffer
+    //      meanwhile.  Otherwise all threads stage B^T through registers.
     u32x4 bfrag[KS][2];
-    {
+    const bool b_async = K2WsLds<T, P>::b_cols_fit && N == 128;
+    if (b_async) {
+        if (!producer && K2WsLds<T, P>::b_cols_fit) {
+            const int64_t rows_b = min<int64_t>(T, L - t0);
+            const int cwu = __builtin_amdgcn_readfirstlane(cw);
+            const i32x4 bd = buffer_desc(Bm + ((b * L + t0) * G + gi) * 128 + 32 * cwu,
+                                         (uint32_t)(((rows_b - 1) * G * 128 + 32) * 2));
+            unsigned char *breg = lds + BUF + cwu * (T * 64);
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int k = 0; k < T / 16; ++k) {  // 1-KiB copies: 16 rows of 64 bytes
+                const int t = 16 * k + (ln >> 2);
+                lds_dma_x4(bd, lds_addr(breg + k * 1024), (t * G * 128 + 8 * ((ln & 3) ^ b_swz(t))) * 2);
+            }
+            lds_dma_wait();
+            const int r = l16 >> 2, a = l16 & 3;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int ch = 2 * nt + (a >> 1);
+                    u32x2 v[2];
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int t = 32 * ks + 8 * g4 + 4 * hf + r;
+                        v[hf] = tr_read(breg + t * 64 + ((ch ^ b_swz(t)) << 4) + 8 * (a & 1));
+                    }
+                    bfrag[ks][nt] = u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
+                }
+        }
+    } else {
         constexpr int PIECE = (int)(2 * BUF / (T * 2)) < 256 ? (int)(2 * BUF / (T * 2)) : 256;
         for (int n_base = 0; n_base < N; n_base += PIECE) {
             const int ncols = min(PIECE, N - n_base);

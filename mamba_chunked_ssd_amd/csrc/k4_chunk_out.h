@@ -942,11 +942,6 @@ struct AsyncLds {
 // c ^ xswz(t), which spreads the 16 rows of one transposing read over all banks
 __device__ __forceinline__ int xswz(int t) { return 2 * ((t >> 1) & 3); }
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 tr_read(const unsigned char *p) {
-    typedef __attribute__((address_space(3))) v4s lds_v4s;
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p));
-}
 
 // One wave's output tile of one head (skip term included), from buffers
 // xt (x tile) and hp (h_c hi plane, lo plane after it) and tables tb.

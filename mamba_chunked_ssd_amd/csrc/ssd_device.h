@@ -114,4 +114,15 @@ __device__ __forceinline__ void lds_dma_x1(const i32x4 &desc, uint32_t lds, int 
 }
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// gfx950 transposing LDS read of 16-bit data (8 bytes per lane): within each
+// 16-lane group, lane l receives element l % 4 of the 4 elements addressed by
+// lanes 4 r + (l % 16) / 4, r = 0..3.  So when lane 4 r + a addresses row k_r,
+// columns 4 a .. 4 a + 3 of a bf16 matrix X, lane l gets X[k_r][l % 16] for
+// r = 0..3 (two bf16 per dword, r = 0 in the low half).
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 tr_read(const unsigned char *p) {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p));
+}
+
 }  // namespace ssd
