@@ -40,8 +40,8 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, y dtype, stage): (sources, sha256[:16], FETCH KiB, WRITE KiB)
     ("mamba2_2p7b_layer_bf16", "f32", "chunk_out"): (
-        ("k4_chunk_out.h", "k4_out_bf16_f32.hip", "ssd_device.h"), "e34f25b382fd891b",
-        44796.6, 81921.2),
+        ("k4_chunk_out.h", "k4_out_bf16_f32.hip", "ssd_device.h"), "3214c82c3b0f2504",
+        45037.1, 83845.2),
 }
 
 
@@ -73,12 +73,20 @@ def stage_model(w, y_bytes: int) -> dict:
     states = 4 * B * NH * NC * P * N
     init = 4 * B * NH * P * N if w.init_std > 0 else 0
     final = 4 * B * NH * P * N
+    # bf16, headdim 64, dstate 128: the state-passing launch also reads B and C
+    # and writes the chunks' C B^T tiles (T/32 x (T/16 + 2) tiles of 1 KiB per
+    # chunk and group), which the chunk output reads in place of B
+    cb_tiles = B * NC * G * (T // 32) * (T // 16 + 2) * 1024 if (
+        w.dtype == "bf16" and P == 64 and N == 128) else 0
+    bc = B * L * G * N * e
     m = {
         "chunk_cumsum": (tok_h * (e + 4), 0.0),
-        "chunk_state": (tok_h * P * e + B * L * G * N * e + tok_h * (e + 4) + states,
+        "chunk_state": (tok_h * P * e + bc + tok_h * (e + 4) + states,
                         2.0 * B * L * NH * N * P),
-        "state_pass": (2 * states + 4 * B * NH * NC + init + final, 0.0),
-        "chunk_out": (tok_h * P * (e + y_bytes) + tok_h * (e + 4) + 2 * B * L * G * N * e + states,
+        "state_pass": (2 * states + 4 * B * NH * NC + init + final + (2 * bc + cb_tiles if cb_tiles else 0),
+                       0.0),
+        "chunk_out": (tok_h * P * (e + y_bytes) + tok_h * (e + 4) + (bc + cb_tiles if cb_tiles else 2 * bc)
+                      + states,
                       float(B * NC * G * T * (T + 1) * N + B * NC * NH * T * (T + 1) * P
                             + 2 * B * L * NH * N * P)),
     }

@@ -111,11 +111,12 @@ constexpr int kCbPerWave = 4;
 template <int T>
 __device__ __forceinline__ void cb_tiles(const uint16_t *__restrict__ Bm,
                                          const uint16_t *__restrict__ Cm, float *__restrict__ CB,
-                                         int64_t seqlen, int G, int64_t nc, int64_t ntiles) {
+                                         int64_t seqlen, int G, int64_t nc, int64_t ntiles, int ncb) {
     constexpr int N = 128;
     constexpr int NT16 = T / 16, NSLOT = NT16 + 2, NSL = (T / 32) * NSLOT;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // consecutive tiles (one chunk's) on one XCD, whose L2 then serves B and C
+    const int64_t gw = (int64_t)xcd_remap(blockIdx.x, ncb) * 4 + (threadIdx.x >> 6);
     const int64_t GN = (int64_t)G * N;
 #pragma unroll 1
     for (int it = 0; it < kCbPerWave; ++it) {
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void k3_state_pass_cb(const float *S, float *H
                                                         float *__restrict__ CB, int64_t seqlen,
                                                         int G, int64_t ntiles, int ncb) {
     if ((int)blockIdx.x < ncb)
-        cb_tiles<T>(Bm, Cm, CB, seqlen, G, nchunks, ntiles);
+        cb_tiles<T>(Bm, Cm, CB, seqlen, G, nchunks, ntiles, ncb);
     else
         state_pass_body<true>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp, T,
                               (int64_t)blockIdx.x - ncb);
