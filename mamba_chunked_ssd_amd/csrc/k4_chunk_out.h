@@ -65,6 +65,7 @@ constexpr size_t kLdsBytes = 160 * 1024;
 #define K4_SCHED_PATTERN 1
 #endif
 
+
 // Wave w owns row tiles I0 = w and I1 = T/16 - 1 - w.  Its S slots are laid
 // out as [I0: J = 0..I0][pad to even][I1: J = 0..I1][pad to even]; the total
 // is always T/16 + 2 and a pair (2q, 2q + 1) never straddles the two tiles.
@@ -957,10 +958,14 @@ __device__ __forceinline__ void store_quad(const floatx4 &v, __amdgpu_buffer_rsr
 }
 
 // acc holds the previous head's finished tile on entry (stored through yprev,
-// spread over the inter-chunk MFMAs; a resource of 0 bytes drops them) and
-// this head's tile on return.  pre(s), s = 0 .. 4, issues piece s of the next
-// head's copies: one per inter-chunk step, the last before the intra-chunk
-// MFMAs, so the memory traffic flows while the MFMAs run.
+// spread over the inter-chunk MFMAs and the first intra-chunk pairs; a
+// resource of 0 bytes drops them) and
+// this head's tile on return.  pre(s), s = 0 .. 8, issues piece s of the next
+// head's copies: x and h_c pieces in the inter-chunk steps, the G2 / dt copies
+// before the intra-chunk MFMAs.  Issued any later, the copies land after the
+// head's MFMAs and the end-of-head wait shows their latency; the stores, which
+// need not land early, are spread further so that the memory queue never
+// fills and blocks the MFMA issue.
 template <int T, int W, typename OutT, typename Pre>
 __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
                                                 const u32x4 (&cfr)[2][acfg::NK],
@@ -1002,10 +1007,10 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) acc[ii][pt] = mfma_bf16(cfr[ii][ks], hl[pt], acc[ii][pt]);
         pre(ks);
+        pre(4 + ks);
         store_quad<OutT>(prev[0][ks], yprev, NHP, I0, ks, l16, g4);
-        store_quad<OutT>(prev[1][ks], yprev, NHP, I1, ks, l16, g4);
     });
-    pre(4);
+    pre(8);
     // rows i = 16 I + 4 g4 + r take exp2(G2_i)
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
@@ -1089,6 +1094,9 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         constexpr int qn = decltype(qc)::value + 1;
         AOps nxt;
         if constexpr (qn < NP) nxt = prep(std::integral_constant<int, WT::pair_order(qn < NP ? qn : 0)>{});
+        // the previous head's second row tile goes out over the first pairs
+        if constexpr (decltype(qc)::value < PT)
+            store_quad<OutT>(prev[1][decltype(qc)::value], yprev, NHP, I1, decltype(qc)::value, l16, g4);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.hi, cur.xb[pt], acc[ii][pt]);
 #pragma unroll
@@ -1113,6 +1121,10 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         }
 #endif
         __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<PT>([&](auto kc) {  // stores left over when there are fewer pairs than tiles
+        if constexpr (decltype(kc)::value >= NP)
+            store_quad<OutT>(prev[1][decltype(kc)::value], yprev, NHP, I1, decltype(kc)::value, l16, g4);
     });
 }
 
@@ -1187,8 +1199,9 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     // G2 / dt: waves w < T / 64 copy tokens 64 w .. +63 (which they also
     // derive the tables of).
     const uint32_t x_bytes = (uint32_t)(((rows - 1) * NHP + P) * 2);
-    // Piece s (0 .. 3) of head h's x and h_c copies, and the G2 / dt copies
-    // (piece 4); the pieces go out spread over the previous head's MFMAs.
+    // Pieces of head h's copies: s = 0 .. 3 a quarter of the x rows, 4 .. 7 a
+    // quarter of the h_c planes, 8 the G2 / dt copies; the pieces go out
+    // spread over the previous head's MFMAs.
     constexpr int XQ = (int)(LD::x / 1024), HQ = (int)(2 * LD::plane / 1024);
     constexpr int XPW = XQ / NW, HPW = HQ / NW;  // copies per wave
     static_assert(XQ % NW == 0 && HQ % NW == 0 && XPW == 4 && HPW % 4 == 0, "copy split");
@@ -1202,10 +1215,11 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
             const int xr = ln >> 3, xl = ((ln & 7) ^ xswz(ln >> 3)) * 16;
             const int q = wu + s * NW;
             lds_dma_x4(xd, xb + q * 1024, (8 * q + xr) * NHP * 2 + xl);
+        } else if (s < 8) {
             const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
                                          (uint32_t)(2 * LD::plane));
 #pragma unroll
-            for (int kk = s * (HPW / 4); kk < (s + 1) * (HPW / 4); ++kk) {
+            for (int kk = (s - 4) * (HPW / 4); kk < (s - 3) * (HPW / 4); ++kk) {
                 const int qh = wu + kk * NW;
                 const int row = 4 * qh + (ln >> 4);  // row of the two stacked planes
                 lds_dma_x4(hd, xb + LD::x + qh * 1024, row * (2 * N) + (((ln & 15) ^ (row & 15)) << 4));
@@ -1221,7 +1235,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     };
     auto issue = [&](int h, int k) {
 #pragma unroll
-        for (int s = 0; s < 5; ++s) issue_piece(h, k, s);
+        for (int s = 0; s < 9; ++s) issue_piece(h, k, s);
     };
 
     // 16 bytes of row `row` of a (rows x N) bf16 matrix at dstate n0; rows past
