@@ -957,15 +957,16 @@ __device__ __forceinline__ void store_quad(const floatx4 &v, __amdgpu_buffer_rsr
     for (int r = 0; r < 4; ++r) store_out<OutT>(yr, lane_off + (16 * I + r) * NHP * ES + 16 * pt * ES, v[r]);
 }
 
-// acc holds the previous head's finished tile on entry (stored through yprev,
-// spread over the inter-chunk MFMAs and the first intra-chunk pairs; a
-// resource of 0 bytes drops them) and
-// this head's tile on return.  pre(s), s = 0 .. 8, issues piece s of the next
+// acc holds this head's tile on return.  For the first-half waves it holds
+// the previous head's finished tile on entry, stored through yprev, spread
+// over the inter-chunk MFMAs and the first intra-chunk pairs (a resource of 0
+// bytes drops the stores); the second-half waves store their tile after the
+// call.  pre(s), s = 0 .. 8 (first-half waves), issues piece s of the next
 // head's copies: x and h_c pieces in the inter-chunk steps, the G2 / dt copies
-// before the intra-chunk MFMAs.  Issued any later, the copies land after the
-// head's MFMAs and the end-of-head wait shows their latency; the stores, which
-// need not land early, are spread further so that the memory queue never
-// fills and blocks the MFMA issue.
+// after them.  Issued any later, the copies land after the head's MFMAs and
+// the end-of-head wait shows their latency; the stores, which need not land
+// early, are spread further so that the memory queue never fills and blocks
+// the MFMA issue.
 template <int T, int W, typename OutT, typename Pre>
 __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
                                                 const u32x4 (&cfr)[2][acfg::NK],
@@ -980,47 +981,66 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
     constexpr int XROW = acfg::P * 2, HROW = acfg::N * 2;
     static_assert(NK == PT, "one (row tile, column tile) pair of stores per step and tile");
 
+    // Waves of the first half take the inter-chunk term first, with the next
+    // head's copies and the previous head's stores; waves of the second half
+    // (which share SIMDs with the first) take the VALU-heavy intra-chunk term
+    // first and store their tile at the end, so each SIMD overlaps one wave's
+    // memory traffic with the other's VALU work.
+    constexpr bool kIntraFirst = W >= T / 64;
     floatx4 prev[2][PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-        prev[0][pt] = acc[0][pt];
-        prev[1][pt] = acc[1][pt];
+        if constexpr (!kIntraFirst) {
+            prev[0][pt] = acc[0][pt];
+            prev[1][pt] = acc[1][pt];
+        }
         acc[0][pt] = acc[1][pt] = zero4();
     }
 
-    // ---- inter-chunk term C_i h_c (h_c as hi + lo planes)
-    static_for<NK>([&](auto kc) {
-        constexpr int ks = decltype(kc)::value;
-        const int cofs = ((4 * ks + g4) ^ l16) << 4;  // chunk 4 ks + g4 of row 16 pt + l16
-        u32x4 hh[PT], hl[PT];
+    // ---- inter-chunk term C_i h_c (h_c as hi + lo planes) into a; the
+    // first-half waves issue the memory pieces between its steps
+    auto inter = [&](floatx4 (&a)[2][PT]) {
+        static_for<NK>([&](auto kc) {
+            constexpr int ks = decltype(kc)::value;
+            const int cofs = ((4 * ks + g4) ^ l16) << 4;  // chunk 4 ks + g4 of row 16 pt + l16
+            u32x4 hh[PT], hl[PT];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            hh[pt] = *reinterpret_cast<const u32x4 *>(hp + (16 * pt + l16) * HROW + cofs);
-            hl[pt] = *reinterpret_cast<const u32x4 *>(hp + LD::plane + (16 * pt + l16) * HROW + cofs);
-        }
+            for (int pt = 0; pt < PT; ++pt) {
+                hh[pt] = *reinterpret_cast<const u32x4 *>(hp + (16 * pt + l16) * HROW + cofs);
+                hl[pt] = *reinterpret_cast<const u32x4 *>(hp + LD::plane + (16 * pt + l16) * HROW + cofs);
+            }
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
+            for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) acc[ii][pt] = mfma_bf16(cfr[ii][ks], hh[pt], acc[ii][pt]);
+                for (int ii = 0; ii < 2; ++ii) a[ii][pt] = mfma_bf16(cfr[ii][ks], hh[pt], a[ii][pt]);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
+            for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) acc[ii][pt] = mfma_bf16(cfr[ii][ks], hl[pt], acc[ii][pt]);
-        pre(ks);
-        pre(4 + ks);
-        store_quad<OutT>(prev[0][ks], yprev, NHP, I0, ks, l16, g4);
-    });
-    pre(8);
-    // rows i = 16 I + 4 g4 + r take exp2(G2_i)
+                for (int ii = 0; ii < 2; ++ii) a[ii][pt] = mfma_bf16(cfr[ii][ks], hl[pt], a[ii][pt]);
+            if constexpr (!kIntraFirst) {
+                pre(ks);
+                pre(4 + ks);
+                store_quad<OutT>(prev[0][ks], yprev, NHP, I0, ks, l16, g4);
+            }
+        });
+        if constexpr (!kIntraFirst) pre(8);
+    };
+    // exp2(G2_i) of rows i = 16 I + 4 g4 + r
+    auto e2_rows = [&](int ii) {
+        return *reinterpret_cast<const float4 *>(tb.e2 + 16 * (ii ? I1 : I0) + 4 * g4);
+    };
+    if constexpr (!kIntraFirst) {
+        inter(acc);
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const float4 e = *reinterpret_cast<const float4 *>(tb.e2 + 16 * (ii ? I1 : I0) + 4 * g4);
+        for (int ii = 0; ii < 2; ++ii) {
+            const float4 e = e2_rows(ii);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            acc[ii][pt][0] *= e.x;
-            acc[ii][pt][1] *= e.y;
-            acc[ii][pt][2] *= e.z;
-            acc[ii][pt][3] *= e.w;
+            for (int pt = 0; pt < PT; ++pt) {
+                acc[ii][pt][0] *= e.x;
+                acc[ii][pt][1] *= e.y;
+                acc[ii][pt][2] *= e.z;
+                acc[ii][pt][3] *= e.w;
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1095,7 +1115,7 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         AOps nxt;
         if constexpr (qn < NP) nxt = prep(std::integral_constant<int, WT::pair_order(qn < NP ? qn : 0)>{});
         // the previous head's second row tile goes out over the first pairs
-        if constexpr (decltype(qc)::value < PT)
+        if constexpr (!kIntraFirst && decltype(qc)::value < PT)
             store_quad<OutT>(prev[1][decltype(qc)::value], yprev, NHP, I1, decltype(qc)::value, l16, g4);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.hi, cur.xb[pt], acc[ii][pt]);
@@ -1123,9 +1143,27 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         __builtin_amdgcn_sched_barrier(0);
     });
     static_for<PT>([&](auto kc) {  // stores left over when there are fewer pairs than tiles
-        if constexpr (decltype(kc)::value >= NP)
+        if constexpr (!kIntraFirst && decltype(kc)::value >= NP)
             store_quad<OutT>(prev[1][decltype(kc)::value], yprev, NHP, I1, decltype(kc)::value, l16, g4);
     });
+    if constexpr (kIntraFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 t[2][PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) t[0][pt] = t[1][pt] = zero4();
+        inter(t);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const float4 e = e2_rows(ii);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                acc[ii][pt][0] = fmaf(e.x, t[ii][pt][0], acc[ii][pt][0]);
+                acc[ii][pt][1] = fmaf(e.y, t[ii][pt][1], acc[ii][pt][1]);
+                acc[ii][pt][2] = fmaf(e.z, t[ii][pt][2], acc[ii][pt][2]);
+                acc[ii][pt][3] = fmaf(e.w, t[ii][pt][3], acc[ii][pt][3]);
+            }
+        }
+    }
 }
 
 // Store a wave's two output tiles (rows 16 I + 4 g4 + r, column 16 pt + l16).
@@ -1199,32 +1237,37 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     // G2 / dt: waves w < T / 64 copy tokens 64 w .. +63 (which they also
     // derive the tables of).
     const uint32_t x_bytes = (uint32_t)(((rows - 1) * NHP + P) * 2);
-    // Pieces of head h's copies: s = 0 .. 3 a quarter of the x rows, 4 .. 7 a
-    // quarter of the h_c planes, 8 the G2 / dt copies; the pieces go out
-    // spread over the previous head's MFMAs.
+    // Pieces of head h's copies, issued by the first NW / 2 waves: s = 0 .. 3
+    // a quarter of the x rows, 4 .. 7 a quarter of the h_c planes, 8 the
+    // G2 / dt copies; the pieces go out spread over the previous head's MFMAs.
+    constexpr int MW = NW / 2;  // copy-issuing waves
     constexpr int XQ = (int)(LD::x / 1024), HQ = (int)(2 * LD::plane / 1024);
-    constexpr int XPW = XQ / NW, HPW = HQ / NW;  // copies per wave
-    static_assert(XQ % NW == 0 && HQ % NW == 0 && XPW == 4 && HPW % 4 == 0, "copy split");
+    constexpr int XPW = XQ / MW, HPW = HQ / MW;  // copies per issuing wave
+    static_assert(XQ % MW == 0 && HQ % MW == 0 && XPW % 4 == 0 && HPW % 4 == 0, "copy split");
+    static_assert(T / 64 == MW, "the issuing waves also derive the tables");
     auto issue_piece = [&](int h, int k, int s) {
-        const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // < MW
         int ln = tid & 63;
         asm volatile("" : "+v"(ln));
         const uint32_t xb = lds_addr(lds + k * LD::buf);
         if (s < 4) {
             const i32x4 xd = buffer_desc(x + ((b * L + t0) * NH + h) * P, x_bytes);
             const int xr = ln >> 3, xl = ((ln & 7) ^ xswz(ln >> 3)) * 16;
-            const int q = wu + s * NW;
-            lds_dma_x4(xd, xb + q * 1024, (8 * q + xr) * NHP * 2 + xl);
+#pragma unroll
+            for (int kk = s * (XPW / 4); kk < (s + 1) * (XPW / 4); ++kk) {
+                const int q = wu + kk * MW;
+                lds_dma_x4(xd, xb + q * 1024, (8 * q + xr) * NHP * 2 + xl);
+            }
         } else if (s < 8) {
             const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
                                          (uint32_t)(2 * LD::plane));
 #pragma unroll
             for (int kk = (s - 4) * (HPW / 4); kk < (s - 3) * (HPW / 4); ++kk) {
-                const int qh = wu + kk * NW;
+                const int qh = wu + kk * MW;
                 const int row = 4 * qh + (ln >> 4);  // row of the two stacked planes
                 lds_dma_x4(hd, xb + LD::x + qh * 1024, row * (2 * N) + (((ln & 15) ^ (row & 15)) << 4));
             }
-        } else if (wu < T / 64) {
+        } else {
             const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
             const Tables<T> tb = tables(k);
             const int voff = (64 * wu + ln) * 4;
@@ -1263,7 +1306,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
 #pragma unroll
         for (int k = 0; k < NSLOT; ++k) S[k] = cb[k * 64];
     }
-    if (h_begin < h_end) issue(h_begin, 0);
+    if (h_begin < h_end && w < MW) issue(h_begin, 0);
     lds_dma_wait();  // this wave's copies of the first head have landed
     if (h_begin < h_end && tid < T) token_derived(tables(0), tid);
     __syncthreads();  // every wave's copies are visible
@@ -1277,6 +1320,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     for (int i = 0; h_begin + i < h_end; ++i) {
         const int h = h_begin + i, cur = i & 1;
         const LaneIds id = opaque_lane_ids(tid);
+        const bool issuer = id.w < MW;  // wave-uniform
         const bool more = h + 1 < h_end;
         auto pre = [&](int s) {
             if (more) issue_piece(h + 1, cur ^ 1, s);
@@ -1290,11 +1334,15 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
             head_wave_async<T, decltype(wc)::value, OutT>(S, cfr, xt, xt + LD::x, tables(cur), Dh,
                                                           id.l16, id.g4, acc, yprev, NHP, pre);
         });
-        lds_dma_wait();  // this wave's copies of the next head have landed
-        if (h + 1 < h_end && tid < T) token_derived(tables(cur ^ 1), tid);
+        if (issuer) {
+            lds_dma_wait();  // this wave's copies of the next head have landed
+            if (more) token_derived(tables(cur ^ 1), tid);
+        } else {
+            store_tile<OutT>(acc, y_head(h), NHP, id.w, NT16 - 1 - id.w, id.l16, id.g4);
+        }
         __syncthreads();
     }
-    if (h_begin < h_end) store_tile<OutT>(acc, y_head(h_end - 1), NHP, I0, I1, l16, g4);
+    if (h_begin < h_end && w < MW) store_tile<OutT>(acc, y_head(h_end - 1), NHP, I0, I1, l16, g4);
 }
 
 // ---------------------------------------------------------------------------
