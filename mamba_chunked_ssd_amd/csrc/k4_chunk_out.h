@@ -1297,8 +1297,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
             cfr[ii][ks] = chunk16(Cc, 16 * (ii ? I1 : I0) + l16, 32 * ks + 8 * g4);
 
     // ---- C B^T tiles of this wave's slots, computed once per chunk by the
-    // cumsum stage; then the first head's copies (after every compiler-visible
-    // load, whose waits would otherwise count them)
+    // state-passing launch; then the first head's copies (after every
+    // compiler-visible load, whose waits would otherwise count them)
     floatx4 S[NSLOT];
     {
         const floatx4 *cb = reinterpret_cast<const floatx4 *>(CBt) +

@@ -90,10 +90,16 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int o
 // otherwise wait for every pending copy before any LDS read it cannot prove
 // disjoint), so the caller waits (lds_dma_wait) before the destination is
 // read -- by the issuing wave, or by others after a barrier.
+// The descriptor and the LDS address must live in scalar registers; they are
+// wave-uniform by construction, and readfirstlane says so to the compiler
+// (which otherwise may keep a value it cannot prove uniform in vector
+// registers, which the instruction does not accept).
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 buffer_desc(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffffu), (int32_t)bytes, 0x00020000};
+    return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int32_t)((a >> 32) & 0xffffu)),
+                 __builtin_amdgcn_readfirstlane((int32_t)bytes), 0x00020000};
 }
 template <typename Ptr>
 __device__ __forceinline__ uint32_t lds_addr(Ptr p) {
@@ -103,13 +109,13 @@ __device__ __forceinline__ uint32_t lds_addr(Ptr p) {
 __device__ __forceinline__ void lds_dma_x4(const i32x4 &desc, uint32_t lds, int voff) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                  :
-                 : "v"(voff), "s"(lds), "s"(desc)
+                 : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(desc)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma_x1(const i32x4 &desc, uint32_t lds, int voff) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
                  :
-                 : "v"(voff), "s"(lds), "s"(desc)
+                 : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(desc)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
