@@ -326,6 +326,8 @@ struct HeadCtx {
     const unsigned char *hl;  // h hi tile + l16 * HRS + 16 g4 (when staged in LDS)
     const unsigned char *cl;  // C tile + l16 * CRS (when staged in LDS)
     const uint16_t *hp;       // h_c hi plane in global memory (lo plane follows; when not staged)
+    const uint16_t *cg[2];    // C rows 16 I0 + l16 and 16 I1 + l16 (clamped; when re-read per head)
+    bool cok[2];              // those rows are within the sequence
     Tables<T> tb;
     __amdgpu_buffer_rsrc_t yr;  // y[b, t0 .., h, :] through the chunk's last valid row
     int NHP;                  // nheads * headdim (row stride of y)
@@ -334,10 +336,10 @@ struct HeadCtx {
     int l16, g4;
 };
 
-template <int T, int P, int NKMAX, bool HLDS, bool CLDS, typename OutT, int W>
+template <int T, int P, int NKMAX, bool HLDS, bool CLDS, bool CG, typename OutT, int W, typename Mid>
 __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
                                           const u32x4 (&cfr)[2][NKMAX],
-                                          const HeadCtx<T, P, NKMAX, OutT> &cx) {
+                                          const HeadCtx<T, P, NKMAX, OutT> &cx, Mid &&mid) {
     using Lds = Bf16Lds<T, P, NKMAX>;
     using WT = WaveTiles<T, W>;
     constexpr int XRS = Lds::XRS, HRS = Lds::HRS;
@@ -350,16 +352,37 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
 
-    // inter-chunk term C_i h_c (h split into hi + lo); fragments past dstate are 0
+    // inter-chunk term C_i h_c (h split into hi + lo); fragments past dstate are 0.
+    // With CG the C fragments are re-read from global memory (L2) two k-steps
+    // ahead instead of being held in registers for the whole block.
+    constexpr int CGD = 1;  // prefetch distance (k-steps)
+    u32x4 cq[CG ? CGD + 1 : 1][2];
+    auto cg_load = [&](int ks, u32x4 (&dst)[2]) {
+        const int n0 = 32 * ks + 8 * g4;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(cx.cg[ii] + min(n0, cx.N - 8));
+            dst[ii] = (cx.cok[ii] && n0 < cx.N) ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if constexpr (CG) {
+#pragma unroll
+        for (int d = 0; d < CGD && d < NKMAX; ++d) cg_load(d, cq[d]);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKMAX; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
         u32x4 cf[2];
+        if constexpr (CG) {
+            if (ks + CGD < NKMAX) cg_load(ks + CGD, cq[(ks + CGD) % (CGD + 1)]);
+        }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             if constexpr (CLDS)  // 16-byte chunk (4 ks + g4) of row 16 I + l16, swizzled by l16
                 cf[ii] = *reinterpret_cast<const u32x4 *>(
                     cx.cl + (16 * (ii ? I1 : I0)) * Lds::CRS + (((4 * ks + g4) ^ l16) << 4));
+            else if constexpr (CG)
+                cf[ii] = cq[ks % (CGD + 1)][ii];
             else
                 cf[ii] = cfr[ii][ks];
         }
@@ -397,6 +420,7 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
             acc[ii][pt][3] *= e.w;
         }
     }
+    mid();  // h_c is no longer read in this head
     // tile-pair factors m(I, J): lane k evaluates the one of slot k, which is
     // then read back as a wave-uniform value
     float mk;
@@ -513,6 +537,14 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
     unsigned char *hhi = xt + Lds::x;                      // [P][HRS] (if kHinLds)
     unsigned char *hlo = hhi + Lds::h / 2;                 // [P][HRS] (if kHinLds)
     constexpr bool kCinLds = Lds::c_in_lds;
+    // Eight waves of 256 registers each cannot hold the C fragments of the
+    // larger tiles beside the C B^T tiles and the next head's prefetch; those
+    // shapes re-read C (L2-resident) in every head instead.
+    constexpr bool kCglb = !kCinLds && T == 256 && (NKMAX == 8 || P == 128);
+    // Those shapes also copy h_c straight into LDS (asynchronous copies, no
+    // registers): issued once every wave is past the inter-chunk term of the
+    // current head, landing during its intra-chunk term.
+    constexpr bool kHdma = kCglb && kHinLds;
     unsigned char *ct = xt + Lds::x + (kHinLds ? Lds::h : 0);  // [T][HRS] (if kCinLds)
     const Tables<T> tb(reinterpret_cast<float *>(ct + (kCinLds ? Lds::c : 0)));
 
@@ -558,7 +590,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                     xr[ps][r] = *reinterpret_cast<const u32x4 *>(xh + (int64_t)t * NH * P + po * 8);
             }
         }
-        if constexpr (kHinLds) {
+        if constexpr (kHinLds && !kHdma) {
             const uint16_t *hp = H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N;
 #pragma unroll
             for (int ps = 0; ps < HPASS; ++ps) {
@@ -596,7 +628,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                 }
             }
         }
-        if constexpr (kHinLds) {
+        if constexpr (kHinLds && !kHdma) {
 #pragma unroll
             for (int ps = 0; ps < HPASS; ++ps) {
                 const int u = tid + ps * NTHR;
@@ -609,8 +641,33 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         }
         if (tid < T) token_tables(tb, tid, sgh, sgl, seh, sel, sdt);
     };
+    // h_c planes of head h into hhi / hlo (rows of HRS bytes): the region is
+    // copied as consecutive 1-KiB pieces, lane l of piece q landing at byte
+    // 1024 q + 16 l; a lane whose bytes fall in a row's padding or past
+    // dstate reads past the resource, which returns zeros.
+    auto issue_h_dma = [&](int h) {
+        constexpr int HBYTES = (int)Lds::h;  // both planes
+        constexpr int PLANE = HBYTES / 2;
+        constexpr int NQ = HBYTES / 1024;
+        static_assert(HBYTES % 1024 == 0, "h region is whole 1-KiB pieces");
+        const uint32_t src_bytes = (uint32_t)(2 * P * N * 2);
+        const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N, src_bytes);
+        const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+        int ln = tid & 63;
+        asm volatile("" : "+v"(ln));
+        for (int q = wu; q < NQ; q += NW) {
+            const int o = 1024 * q + 16 * ln;
+            const int pl = o / PLANE, r = o % PLANE;
+            const int row = r / HRS, within = r % HRS;
+            const bool ok = within < 2 * N;
+            const int voff = ok ? (pl * P * N + row * N) * 2 + within : (int)src_bytes;
+            lds_dma_x4(hd, lds_addr(hhi + 1024 * q), voff);
+        }
+    };
 
-    if (h_begin < h_end) load_head(h_begin);
+    // (with kCglb the first head's prefetch waits until the C B^T tiles are
+    // done, so its registers are not live beside the tiles' operands)
+    if (!kCglb && h_begin < h_end) load_head(h_begin);
 
     // ---------------- C B^T tiles (transposed), once per block -------------
     // All threads stage the chunk's C rows (into the C tile, when it lives in
@@ -643,7 +700,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
             const int row = u / CCH, ch = u % CCH;
             *reinterpret_cast<u32x4 *>(ct + row * Lds::CRS + ((ch ^ (row & 15)) << 4)) = cv[k];
         }
-    } else {
+    } else if constexpr (!kCglb) {
         // lane holds C[t0 + 16 I + l16][32 ks + 8 g4 .. +7]
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii)
@@ -661,6 +718,13 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         constexpr int BPT = T * BCH / NTHR;              // per thread
         constexpr int SWM = (BCH >= 16 ? 16 : BCH) - 1;
         if constexpr (PC > 0) __syncthreads();           // previous piece consumed
+        if constexpr (kCglb) {  // only this piece's C fragments
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int ksl = 0; ksl < KSP; ++ksl)
+                    cfr[ii][KSP * PC + ksl] = chunk16(Cc, 16 * (ii ? I1 : I0) + l16, 32 * (KSP * PC + ksl) + 8 * g4);
+        }
         u32x4 bv[BPT];
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
@@ -680,17 +744,24 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
         });
     });
     __syncthreads();  // the B rows are overwritten by the first head's staging
+    if (kCglb && h_begin < h_end) load_head(h_begin);
+    if constexpr (kHdma)
+        if (h_begin < h_end) issue_h_dma(h_begin);
 
     // ---------------- heads -------------------------------------------------
     for (int h = h_begin; h < h_end; ++h) {
         stage_head();
+        if constexpr (kHdma) lds_dma_wait();  // this wave's h_c copies have landed
         __syncthreads();
         if (h + 1 < h_end) load_head(h + 1);
         const LaneIds id = opaque_lane_ids(tid);
+        const int ra = 16 * id.w + id.l16, rb = 16 * (NT16 - 1 - id.w) + id.l16;  // rows of I0, I1
         HeadCtx<T, P, NKMAX, OutT> cx{xt + id.l16 * XRS + 16 * id.g4,
                                       hhi + id.l16 * HRS + 16 * id.g4,
                                       ct + id.l16 * Lds::CRS,
                                       H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
+                                      {Cc + (int64_t)min(ra, rows - 1) * GN, Cc + (int64_t)min(rb, rows - 1) * GN},
+                                      {ra < rows, rb < rows},
                                       tb,
                                       buffer_rsrc(y + ((b * L + t0) * NH + h) * P,
                                                   (uint32_t)(((rows - 1) * NH * P + P) * sizeof(OutT))),
@@ -700,7 +771,12 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16(
                                       id.l16,
                                       id.g4};
         dispatch_wave<NW>(id.w, [&](auto wc) {
-            head_wave<T, P, NKMAX, kHinLds, kCinLds, OutT, decltype(wc)::value>(S, cfr, cx);
+            head_wave<T, P, NKMAX, kHinLds, kCinLds, kCglb, OutT, decltype(wc)::value>(S, cfr, cx, [&]() {
+                if constexpr (kHdma) {
+                    __syncthreads();  // every wave is done reading this head's h_c
+                    if (h + 1 < h_end) issue_h_dma(h + 1);
+                }
+            });
         });
         __syncthreads();
     }

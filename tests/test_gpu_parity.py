@@ -40,6 +40,12 @@ STAGE_SHAPES = [
     (2, 130, 4, 128, 80, 2, 64),
     (1, 600, 8, 64, 128, 1, 128),
     (2, 1000, 6, 64, 128, 2, 256),
+    # chunk 256 with dstate > 128 or headdim 128: the chunk output re-reads C
+    # per head and copies h_c asynchronously; ragged tails, dstate not a
+    # multiple of 32
+    (1, 389, 3, 64, 144, 1, 256),
+    (1, 700, 2, 32, 256, 1, 256),
+    (1, 300, 2, 128, 96, 1, 256),
 ]
 
 
