@@ -39,27 +39,6 @@ __device__ __forceinline__ float load_dt<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load_dt<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
-template <int E>
-struct VecF;
-template <>
-struct VecF<1> { typedef float type; };
-template <>
-struct VecF<2> { typedef floatx2 type; };
-template <>
-struct VecF<4> { typedef floatx4 type; };
-
-template <int E>
-__device__ __forceinline__ void store_vec(float *p, const float (&v)[E]) {
-    typename VecF<E>::type t;
-    if constexpr (E == 1) {
-        t = v[0];
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) t[e] = v[e];
-    }
-    *reinterpret_cast<typename VecF<E>::type *>(p) = t;
-}
-
 template <typename Tin, int T>
 __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
     const Tin *__restrict__ dt, const float *__restrict__ A, float *__restrict__ G2hi,
@@ -72,36 +51,13 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
     const int lane = threadIdx.x & 63;
     if (h >= nheads) return;  // wave-uniform; no barrier follows
 
-    const double a2 = (double)A[h] * 1.4426950408889634;  // log2(e)
     const int64_t t0 = (int64_t)c * T + lane * E;
     float d[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
         d[e] = (t0 + e < seqlen) ? load_dt(dt + (b * seqlen + t0 + e) * nheads + h) : 0.f;
-    double run[E];
-    double tot = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        tot += a2 * (double)d[e];
-        run[e] = tot;
-    }
-    // Inclusive scan of the lane totals across the wave.
-    double inc = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double up = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += up;
-    }
-    const double excl = inc - tot;
-    const double last = __shfl(inc, 63, 64);  // G2 at the chunk's last token
     float hi[E], lo[E], wt[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const double g = excl + run[e];
-        hi[e] = (float)g;
-        lo[e] = (float)(g - (double)hi[e]);
-        wt[e] = fast_exp2((float)(last - g)) * d[e];
-    }
+    chunk_cumsum_wave<E>(d, A[h], lane, hi, lo, wt);
     const int64_t base = (b * nheads + h) * Lp + t0;
     store_vec<E>(G2hi + base, hi);
     store_vec<E>(G2lo + base, lo);

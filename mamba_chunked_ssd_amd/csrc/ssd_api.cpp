@@ -270,9 +270,12 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
                hipEventRecord(ev.stop, stream) == hipSuccess;
     };
     if (p.nchunks > 0) {
-        if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess)
+        if (chunk_state_fuses_cumsum(p, plan)) {
+            if (!skip(0)) return SSD_ERROR_LAUNCH;  // the chunk-state launch computes it
+        } else if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess) {
             return SSD_ERROR_LAUNCH;
-        if (launch_chunk_state(p, plan, x, B, Wf, S, stream, events_of(1)) != hipSuccess)
+        }
+        if (launch_chunk_state(p, plan, x, B, Wf, S, dt, A, G2, DTf, stream, events_of(1)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
     } else if (!skip(0) || !skip(1)) {
         return SSD_ERROR_LAUNCH;

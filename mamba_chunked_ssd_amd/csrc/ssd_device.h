@@ -56,6 +56,80 @@ __device__ __forceinline__ HiLo split_bf16(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// E consecutive floats as one vector store
+template <int E>
+struct VecF;
+template <>
+struct VecF<1> { typedef float type; };
+template <>
+struct VecF<2> { typedef floatx2 type; };
+template <>
+struct VecF<4> { typedef floatx4 type; };
+
+template <int E>
+__device__ __forceinline__ void store_vec(float *p, const float (&v)[E]) {
+    typename VecF<E>::type t;
+    if constexpr (E == 1) {
+        t = v[0];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) t[e] = v[e];
+    }
+    *reinterpret_cast<typename VecF<E>::type *>(p) = t;
+}
+
+// A double moved across lanes by one DPP control (both 32-bit halves); a lane
+// with no source lane (or in a row the row mask leaves out) gets 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Per-chunk log-decay cumsum of one head by one wave ("Kernel 1: Computing
+// cumulative sums" of the CUDA Tile post): lane l holds dt of the chunk's
+// tokens E l .. E l + E - 1 (0 past seqlen).  The running sum of
+// log2(e) A dt_t is taken in fp64 (serial within the lane, then a wave scan)
+// and returned as hi + lo floats, together with the weight with which each
+// token enters its chunk's state, W_t = exp2(G2_last - G2_t) dt_t, whose
+// exponent is formed in fp64 before the fp32 exp2.
+template <int E>
+__device__ __forceinline__ void chunk_cumsum_wave(const float (&d)[E], float A, int lane, float (&hi)[E],
+                                                  float (&lo)[E], float (&wt)[E]) {
+    const double a2 = (double)A * 1.4426950408889634;  // log2(e)
+    double run[E];
+    double tot = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        tot += a2 * (double)d[e];
+        run[e] = tot;
+    }
+    // inclusive scan of the lane totals across the wave, with DPP lane moves:
+    // shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of
+    // row 0 (2) added to row 1 (3), then lane 31 added to rows 2 and 3
+    double inc = tot;
+    inc += dpp_move_f64<0x111, 0xf>(inc);  // row_shr:1
+    inc += dpp_move_f64<0x112, 0xf>(inc);  // row_shr:2
+    inc += dpp_move_f64<0x114, 0xf>(inc);  // row_shr:4
+    inc += dpp_move_f64<0x118, 0xf>(inc);  // row_shr:8
+    inc += dpp_move_f64<0x142, 0xa>(inc);  // row_bcast:15 into rows 1, 3
+    inc += dpp_move_f64<0x143, 0xc>(inc);  // row_bcast:31 into rows 2, 3
+    const double excl = inc - tot;
+    const uint64_t lb = (uint64_t)__double_as_longlong(inc);
+    const uint32_t llo = __builtin_amdgcn_readlane((int)(uint32_t)lb, 63);
+    const uint32_t lhi = __builtin_amdgcn_readlane((int)(uint32_t)(lb >> 32), 63);
+    const double last = __longlong_as_double((long long)(((uint64_t)lhi << 32) | llo));  // chunk's last token
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const double g = excl + run[e];
+        hi[e] = (float)g;
+        lo[e] = (float)(g - (double)hi[e]);
+        wt[e] = __builtin_amdgcn_exp2f((float)(last - g)) * d[e];
+    }
+}
+
 __device__ __forceinline__ floatx4 mfma_bf16(const u32x4 &a, const u32x4 &b, const floatx4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
