@@ -243,12 +243,12 @@ def main(argv=None):
 
     model = stage_model(w, 4 if ydt == torch.float32 else (2 if w.dtype == "bf16" else 4))
     peak_tf = PEAK_TFLOPS[w.dtype]
-    # A stage whose event pair records no time was not launched: the cumsum
-    # is computed inside the chunk-state launch for some shapes.  That launch
-    # reads dt and writes the cumsum, which the chunk-state byte model already
-    # counts (dt in, fp32 cumsum), so the fused stage adds no floor of its own.
-    fused = {name: "chunk_state" for j, name in enumerate(STAGES)
-             if name == "chunk_cumsum" and stage_ms[j] < 1e-4}
+    # The cumsum is computed inside the chunk-state launch for some shapes (the
+    # library reports which stages launch kernels).  That launch reads dt and
+    # writes the cumsum, which the chunk-state byte model already counts (dt
+    # in, fp32 cumsum), so the fused stage adds no floor of its own.
+    launched = ssd.stage_launches(shape, w.chunk_size)
+    fused = {name: "chunk_state" for name in STAGES if name == "chunk_cumsum" and name not in launched}
     stages = {}
     for j, name in enumerate(STAGES):
         if name in fused:
@@ -316,8 +316,9 @@ def main(argv=None):
             for ev in e:
                 hip.destroy(ev)
         cold = np.array(cold).mean(axis=0)
-        out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES)}
-        out["cold_tokens_per_s"] = round(w.tokens / (cold.sum() * 1e-3), 1)
+        out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES) if n not in fused}
+        out["cold_tokens_per_s"] = round(
+            w.tokens / (sum(cold[j] for j, n in enumerate(STAGES) if n not in fused) * 1e-3), 1)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps)

@@ -41,6 +41,7 @@ EXPORTS = [
     "ssd_chunk_scan_fwd_workspace_layout",
     "ssd_chunk_scan_fwd",
     "ssd_chunk_scan_fwd_profiled",
+    "ssd_chunk_scan_fwd_stage_launches",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -112,6 +113,8 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
         lib.ssd_chunk_scan_fwd_profiled.argtypes = fwd_args + [ctypes.POINTER(ctypes.c_void_p)]
         lib.ssd_chunk_scan_fwd_profiled.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_stage_launches.argtypes = [sp, i64, ctypes.POINTER(ctypes.c_uint32)]
+        lib.ssd_chunk_scan_fwd_stage_launches.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []
@@ -153,6 +156,19 @@ def workspace_layout(shape: Shape, chunk_size: int) -> WorkspaceLayout:
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_workspace_layout")
     return lay
+
+
+STAGES = ("chunk_cumsum", "chunk_state", "state_pass", "chunk_out")
+
+
+def stage_launches(shape: Shape, chunk_size: int) -> tuple:
+    """Names of the stages that launch a kernel of their own for this problem."""
+    mask = ctypes.c_uint32()
+    st = load_library().ssd_chunk_scan_fwd_stage_launches(ctypes.byref(shape), chunk_size,
+                                                          ctypes.byref(mask))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_stage_launches")
+    return tuple(n for i, n in enumerate(STAGES) if mask.value >> i & 1)
 
 
 def _ptr(t):

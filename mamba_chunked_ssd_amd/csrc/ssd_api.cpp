@@ -309,6 +309,23 @@ ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape, const void *x, co
                    workspace_bytes, stream, stage_events);
 }
 
+ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size, uint32_t *mask) {
+    if (mask == nullptr) return SSD_ERROR_INVALID_VALUE;
+    Problem p;
+    const ssd_status st = check_shape(shape, chunk_size, &p);
+    if (st != SSD_OK) return st;
+    uint32_t m = 0;
+    if (p.batch > 0) {
+        if (p.nchunks > 0) {
+            if (!chunk_state_fuses_cumsum(p, make_plan(p))) m |= 1u;
+            m |= 2u | 8u;
+        }
+        if (p.nheads > 0) m |= 4u;
+    }
+    *mask = m;
+    return SSD_OK;
+}
+
 const char *ssd_status_string(ssd_status s) {
     switch (s) {
         case SSD_OK: return "ok";

@@ -50,6 +50,26 @@ def test_missing_library_fails_loudly(tmp_path):
         ssd.load_library(str(tmp_path / "libssd.so"))
 
 
+def test_stage_launches(lib):
+    # the 2.7B-layer shape (bf16, dstate 128, 5 heads per block): the
+    # chunk-state kernel computes the cumsum, so stage 0 launches nothing
+    s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
+    assert ssd.stage_launches(s, 256) == ("chunk_state", "state_pass", "chunk_out")
+    # fp32 inputs and dstate 256 keep the separate cumsum kernel
+    s = ssd.make_shape(4, 16384, 64, 128, 256, 8, "f32")
+    assert ssd.stage_launches(s, 128) == ssd.STAGES
+    s = ssd.make_shape(1, 65536, 32, 64, 256, 1, "bf16")
+    assert ssd.stage_launches(s, 256) == ssd.STAGES
+    # no tokens: only the state pass (initial state to final state) runs
+    s = ssd.make_shape(2, 0, 4, 64, 128, 1, "bf16")
+    assert ssd.stage_launches(s, 256) == ("state_pass",)
+    s = ssd.make_shape(0, 100, 4, 64, 128, 1, "bf16")
+    assert ssd.stage_launches(s, 256) == ()
+    m = ctypes.c_uint32()
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 256, None) == 1
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 96, ctypes.byref(m)) != 0
+
+
 def test_status_strings(lib):
     assert lib.ssd_status_string(0) == b"ok"
     for code in range(1, 6):
