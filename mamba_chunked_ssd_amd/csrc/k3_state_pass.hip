@@ -11,8 +11,8 @@
 //
 // Design for gfx950: this is a pure HBM stream (one read of s, one write of h
 // per element, 2 flops).  Each thread owns 4 consecutive state elements of one
-// (batch, head) and walks the chunks; loads of up to 8 chunks are issued
-// before the dependent FMA chain so each thread keeps 128 B in flight, and
+// (batch, head) and walks the chunks; the loads of a batch of 4 chunks (8
+// beyond 128 chunks) are issued before the dependent FMA chain, and
 // consecutive threads touch consecutive 16-byte words, so every wave access
 // is a fully coalesced 1 KiB.  For fp32 problems h is fp32 and may alias s
 // (in place: each element is read before it is overwritten, by the same
@@ -34,9 +34,11 @@
 namespace ssd {
 namespace {
 
-constexpr int kDepth = 8;
-
-template <bool kSplit>
+// Chunks whose loads are issued together before their stores (see
+// state_depth): with few chunks per thread a smaller batch lets one batch's
+// stores overlap the next batch's loads; with many, a deeper batch keeps more
+// bytes in flight.
+template <int kDepth, bool kSplit>
 __device__ __forceinline__ void state_pass_body(const float *S, float *H, const float *__restrict__ G2hi,
                                                 const float *__restrict__ G2lo, const float *init,
                                                 float *final_states, int64_t n_vec, int64_t pn_vec,
@@ -86,15 +88,15 @@ __device__ __forceinline__ void state_pass_body(const float *S, float *H, const 
     if (final_states != nullptr) reinterpret_cast<float4 *>(final_states)[bh * pn_vec + e] = h;
 }
 
-template <bool kSplit>
+template <int kDepth, bool kSplit>
 __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
                                                      const float *__restrict__ G2hi,
                                                      const float *__restrict__ G2lo,
                                                      const float *init, float *final_states,
                                                      int64_t n_vec, int64_t pn_vec,
                                                      int64_t nchunks, int64_t Lp, int T) {
-    state_pass_body<kSplit>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp, T,
-                            blockIdx.x);
+    state_pass_body<kDepth, kSplit>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp, T,
+                                    blockIdx.x);
 }
 
 // C B^T tiles for the chunk-output stage (bf16 B and C, dstate 128): tile
@@ -154,7 +156,7 @@ __device__ __forceinline__ void cb_tiles(const uint16_t *__restrict__ Bm,
     }
 }
 
-template <int T>
+template <int T, int kDepth>
 __global__ __launch_bounds__(256) void k3_state_pass_cb(const float *S, float *H,
                                                         const float *__restrict__ G2hi,
                                                         const float *__restrict__ G2lo,
@@ -168,8 +170,8 @@ __global__ __launch_bounds__(256) void k3_state_pass_cb(const float *S, float *H
     if ((int)blockIdx.x < ncb)
         cb_tiles<T>(Bm, Cm, CB, seqlen, G, nchunks, ntiles, ncb);
     else
-        state_pass_body<true>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp, T,
-                              (int64_t)blockIdx.x - ncb);
+        state_pass_body<kDepth, true>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp,
+                                      T, (int64_t)blockIdx.x - ncb);
 }
 
 }  // namespace
@@ -181,33 +183,44 @@ hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View 
     const int64_t n_vec = p.batch * p.nheads * pn_vec;
     if (n_vec == 0) return hipSuccess;
     const int64_t blocks = (n_vec + 255) / 256;
+    // measured on MI355X: batches of 4 chunks up to 128 chunks (2.7B layer
+    // 16.9 -> 15.4 us, grouped fp32 workload 1.94 -> 1.84 ms), 8 beyond
+    constexpr int kShallow = 4, kDeep = 8;
+    const bool deep = p.nchunks > 128;
     const int64_t ntiles = uses_cb_tiles(p) ? p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) : 0;
     if (ntiles > 0) {
         const int64_t ncb = (ntiles + 4 * kCbPerWave - 1) / (4 * kCbPerWave);
         if (blocks + ncb > INT_MAX) return hipErrorInvalidValue;
         const auto *Bm = static_cast<const uint16_t *>(B);
         const auto *Cm = static_cast<const uint16_t *>(C);
-#define SSD_K3_CB(TT)                                                                              \
-    launch_kernel(k3_state_pass_cb<TT>, dim3((unsigned)(blocks + ncb)), dim3(256), 0, stream, ev, S, \
-                  H, G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len, Bm,  \
+#define SSD_K3_CB(TT, DD)                                                                            \
+    launch_kernel(k3_state_pass_cb<TT, DD>, dim3((unsigned)(blocks + ncb)), dim3(256), 0, stream, ev,  \
+                  S, H, G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len, Bm, \
                   Cm, CB, p.seqlen, (int)p.ngroups, ntiles, (int)ncb)
+#define SSD_K3_CB_T(TT)          \
+    if (deep)                    \
+        SSD_K3_CB(TT, kDeep);    \
+    else                         \
+        SSD_K3_CB(TT, kShallow);
         switch (p.chunk) {
-            case 64: SSD_K3_CB(64); break;
-            case 128: SSD_K3_CB(128); break;
-            case 256: SSD_K3_CB(256); break;
+            case 64: SSD_K3_CB_T(64); break;
+            case 128: SSD_K3_CB_T(128); break;
+            case 256: SSD_K3_CB_T(256); break;
             default: return hipErrorInvalidValue;
         }
+#undef SSD_K3_CB_T
 #undef SSD_K3_CB
         return hipGetLastError();
     }
-    if (p.bf16)
-        launch_kernel(k3_state_pass<true>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H,
-                      G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
-                      (int)p.chunk);
-    else
-        launch_kernel(k3_state_pass<false>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H,
-                      G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len,
-                      (int)p.chunk);
+#define SSD_K3(DD, SPLIT)                                                                          \
+    launch_kernel(k3_state_pass<DD, SPLIT>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, S, H, \
+                  G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len, (int)p.chunk)
+    if (p.bf16) {
+        if (deep) SSD_K3(kDeep, true); else SSD_K3(kShallow, true);
+    } else {
+        if (deep) SSD_K3(kDeep, false); else SSD_K3(kShallow, false);
+    }
+#undef SSD_K3
     return hipGetLastError();
 }
 
