@@ -910,23 +910,50 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[0][pt] = acc[1][pt] = zero4();
 
-        // inter-chunk term C_i h_c
-        for (int s = 0; s < ns; ++s) {
-            floatx4 cv[2];
+        // inter-chunk term C_i h_c.  Headdim 128 at chunk <= 128 runs one
+        // wave per SIMD (the register budget), so the C and h fragments of
+        // dstate step s + 1 are loaded (from L2) while step s's MFMAs run:
+        // two register sets, alternating.  Other shapes keep one set (the
+        // second would cost them occupancy or spill).
+        struct InterOps {
+            floatx4 c[2], h[PT];
+        };
+        auto inter_load = [&](int s, InterOps &o) {
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) {
-                cv[ii] = zero4();
+                o.c[ii] = zero4();
                 if (full || rc[ii] < L)
-                    cv[ii] = *reinterpret_cast<const floatx4 *>(Cm + ((b * L + rc[ii]) * G + gi) * N + 16 * s + 4 * id.g4);
+                    o.c[ii] = *reinterpret_cast<const floatx4 *>(Cm + ((b * L + rc[ii]) * G + gi) * N + 16 * s + 4 * id.g4);
             }
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const floatx4 hv = *reinterpret_cast<const floatx4 *>(hp + (16 * pt + id.l16) * N + 16 * s + 4 * id.g4);
+            for (int pt = 0; pt < PT; ++pt)
+                o.h[pt] = *reinterpret_cast<const floatx4 *>(hp + (16 * pt + id.l16) * N + 16 * s + 4 * id.g4);
+        };
+        auto inter_mfma = [&](const InterOps &o) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[0][pt] = mfma_f32(cv[0][q], hv[q], acc[0][pt]);
-                    acc[1][pt] = mfma_f32(cv[1][q], hv[q], acc[1][pt]);
+                    acc[0][pt] = mfma_f32(o.c[0][q], o.h[pt][q], acc[0][pt]);
+                    acc[1][pt] = mfma_f32(o.c[1][q], o.h[pt][q], acc[1][pt]);
                 }
+        };
+        if constexpr (T <= 128 && P == 128) {
+            InterOps opa, opb;
+            inter_load(0, opa);
+            for (int s = 0; s < ns; s += 2) {
+                if (s + 1 < ns) inter_load(s + 1, opb);
+                inter_mfma(opa);
+                if (s + 1 < ns) {
+                    if (s + 2 < ns) inter_load(s + 2, opa);
+                    inter_mfma(opb);
+                }
+            }
+        } else {
+            for (int s = 0; s < ns; ++s) {
+                InterOps o;
+                inter_load(s, o);
+                inter_mfma(o);
             }
         }
 #pragma unroll
