@@ -872,6 +872,39 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
     floatx4 S[NSLOT];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) S[k] = zero4();
+    if constexpr (T <= 128) {
+        // per dstate step: both C rows and the B row of every column tile J
+        // <= I1 are loaded once, then all of the step's (I, J) MFMAs run (a
+        // B row serves both row tiles)
+        // (code specialised per wave, so every slot index is a constant)
+        const bool cok[2] = {full || rowC[0] < L, full || rowC[1] < L};
+        const float *crow[2] = {Cm + ((b * L + (cok[0] ? rowC[0] : 0)) * G + gi) * N,
+                                Cm + ((b * L + (cok[1] ? rowC[1] : 0)) * G + gi) * N};
+        dispatch_wave<T / 32>(w, [&](auto wc) {
+            constexpr int WI0 = decltype(wc)::value, WI1 = NT16 - 1 - WI0, WB1 = (WI0 + 2) & ~1;
+            for (int s = 0; s < ns; ++s) {
+                floatx4 cv[2], bv[WI1 + 1];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+                    cv[ii] = cok[ii] ? *reinterpret_cast<const floatx4 *>(crow[ii] + 16 * s + 4 * g4) : zero4();
+#pragma unroll
+                for (int J = 0; J <= WI1; ++J) {  // WI1 >= WI0
+                    bv[J] = zero4();
+                    const int64_t row = t0 + 16 * J + l16;
+                    if (full || row < L)
+                        bv[J] = *reinterpret_cast<const floatx4 *>(Bm + ((b * L + row) * G + gi) * N + 16 * s + 4 * g4);
+                }
+#pragma unroll
+                for (int J = 0; J <= WI1; ++J) {
+                    if (J <= WI0)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) S[J] = mfma_f32(bv[J][q], cv[0][q], S[J]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) S[WB1 + J] = mfma_f32(bv[J][q], cv[1][q], S[WB1 + J]);
+                }
+            }
+        });
+    } else {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
         const int I = ii ? I1 : I0;
@@ -893,6 +926,7 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 for (int q = 0; q < 4; ++q) S[k] = mfma_f32(bv[q], cv[q], S[k]);
             }
         }
+    }
     }
 
     for (int h = h_begin; h < h_end; ++h) {
