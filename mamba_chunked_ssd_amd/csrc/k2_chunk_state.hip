@@ -638,7 +638,11 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
 // ---------------------------------------------------------------------------
 constexpr int kSlab = 64;  // tokens of w*x staged in LDS at a time
 
-template <int T, int P>
+// With PF (eight waves, dstate > 224; not chunk 256 with headdim 128, which
+// has no registers left for it) the x rows and weights of the next
+// (head, slab) step are loaded into registers while the current slab's MFMAs
+// run, instead of after them.
+template <int T, int P, bool PF>
 __global__ __launch_bounds__(512) void k2_chunk_state_f32(
     const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ W,
     float *__restrict__ S, int64_t L,
@@ -675,6 +679,32 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
             bfrag[ks][nt] = (n < N && tok < L) ? Bm[((b * L + tok) * G + gi) * N + n] : 0.f;
         }
 
+    constexpr int NSL = T / kSlab;
+    constexpr int XV = kSlab * (P / 4);              // float4 units of a slab
+    constexpr int XPT = PF ? (XV + 511) / 512 : 1;   // per thread (PF: 512 threads)
+    struct XPre {
+        float4 v[XPT];
+        float wt[XPT];
+    };
+    XPre pre;
+    auto pre_load = [&](int h, int slab) {
+        const float *wh = W + ((int64_t)b * NH + h) * Lp + t0;
+#pragma unroll
+        for (int q = 0; q < XPT; ++q) {
+            const int v = tid + q * 512;
+            const int tt = v / (P / 4), p4 = v % (P / 4);
+            const int t = slab * kSlab + tt;
+            pre.v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            pre.wt[q] = 0.f;
+            if (v < XV && t0 + t < L) {
+                pre.v[q] = *reinterpret_cast<const float4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
+                pre.wt[q] = wh[t];
+            }
+        }
+    };
+    if constexpr (PF)
+        if (h_begin < h_end) pre_load(h_begin, 0);
+
     for (int h = h_begin; h < h_end; ++h) {
         const float *wh = W + ((int64_t)b * NH + h) * Lp + t0;
         int tid_o = tid;  // opaque lane coordinates, as in the bf16 kernel
@@ -684,20 +714,40 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[pt][0] = acc[pt][1] = zero4();
 #pragma unroll
-        for (int slab = 0; slab < T / kSlab; ++slab) {
+        for (int slab = 0; slab < NSL; ++slab) {
             // stage w_t x_t for tokens [slab*64, slab*64 + 64)
-            for (int v = tid; v < kSlab * (P / 4); v += nthr) {
-                const int tt = v / (P / 4), p4 = v % (P / 4);
-                const int t = slab * kSlab + tt;
-                float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (t0 + t < L) {
-                    xv = *reinterpret_cast<const float4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
-                    const float wt = wh[t];
-                    xv.x *= wt; xv.y *= wt; xv.z *= wt; xv.w *= wt;
+            if constexpr (PF) {
+#pragma unroll
+                for (int q = 0; q < XPT; ++q) {
+                    const int v = tid + q * 512;
+                    if (v < XV) {
+                        const int tt = v / (P / 4), p4 = v % (P / 4);
+                        float4 xv = pre.v[q];
+                        const float wt = pre.wt[q];
+                        xv.x *= wt; xv.y *= wt; xv.z *= wt; xv.w *= wt;
+                        *reinterpret_cast<float4 *>(&xs[tt * LDP + 4 * p4]) = xv;
+                    }
                 }
-                *reinterpret_cast<float4 *>(&xs[tt * LDP + 4 * p4]) = xv;
+            } else {
+                for (int v = tid; v < XV; v += nthr) {
+                    const int tt = v / (P / 4), p4 = v % (P / 4);
+                    const int t = slab * kSlab + tt;
+                    float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (t0 + t < L) {
+                        xv = *reinterpret_cast<const float4 *>(x + ((b * L + t0 + t) * NH + h) * P + 4 * p4);
+                        const float wt = wh[t];
+                        xv.x *= wt; xv.y *= wt; xv.z *= wt; xv.w *= wt;
+                    }
+                    *reinterpret_cast<float4 *>(&xs[tt * LDP + 4 * p4]) = xv;
+                }
             }
             __syncthreads();
+            if constexpr (PF) {  // the next step's rows, in flight during this slab's MFMAs
+                if (slab + 1 < NSL)
+                    pre_load(h, slab + 1);
+                else if (h + 1 < h_end)
+                    pre_load(h + 1, 0);
+            }
 #pragma unroll
             for (int ks = 0; ks < SLAB_KS; ++ks) {
 #pragma unroll
@@ -773,11 +823,18 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
                            (int)p.heads_per_group, HB, nhb);
     } else {
         const int waves = (int)((p.dstate + 31) / 32);
-        launch_kernel((k2_chunk_state_f32<T, P>), dim3((unsigned)blocks), dim3(64 * waves), 0,
-                           stream, ev, static_cast<const float *>(x), static_cast<const float *>(B),
-                           W, S, p.seqlen, (int)p.nheads, (int)p.dstate,
-                           (int)p.ngroups,
-                           (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB, nhb);
+        // (chunk 256 with headdim 128 has no registers left for the prefetch)
+        constexpr bool kPfOk = !(T == 256 && P == 128);
+        if (kPfOk && waves == 8)
+            launch_kernel((k2_chunk_state_f32<T, P, kPfOk>), dim3((unsigned)blocks), dim3(512), 0, stream, ev,
+                          static_cast<const float *>(x), static_cast<const float *>(B), W, S, p.seqlen,
+                          (int)p.nheads, (int)p.dstate, (int)p.ngroups, (int)p.nchunks, p.padded_len,
+                          (int)p.heads_per_group, HB, nhb);
+        else
+            launch_kernel((k2_chunk_state_f32<T, P, false>), dim3((unsigned)blocks), dim3(64 * waves), 0,
+                          stream, ev, static_cast<const float *>(x), static_cast<const float *>(B), W, S,
+                          p.seqlen, (int)p.nheads, (int)p.dstate, (int)p.ngroups, (int)p.nchunks,
+                          p.padded_len, (int)p.heads_per_group, HB, nhb);
     }
     return hipGetLastError();
 }
