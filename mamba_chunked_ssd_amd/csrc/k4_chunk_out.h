@@ -946,8 +946,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 
         // inter-chunk term C_i h_c.  Headdim 128 at chunk <= 128 runs one
         // wave per SIMD (the register budget), so the C and h fragments of
-        // dstate step s + 1 are loaded (from L2) while step s's MFMAs run:
-        // two register sets, alternating.  Other shapes keep one set (the
+        // dstate step s + 2 are loaded while step s's MFMAs run: three
+        // register sets in rotation.  Other shapes keep one set (the
         // second would cost them occupancy or spill).
         struct InterOps {
             floatx4 c[2], h[PT];
@@ -973,14 +973,19 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
                 }
         };
         if constexpr (T <= 128 && P == 128) {
-            InterOps opa, opb;
+            InterOps opa, opb, opc;
             inter_load(0, opa);
-            for (int s = 0; s < ns; s += 2) {
-                if (s + 1 < ns) inter_load(s + 1, opb);
+            if (1 < ns) inter_load(1, opb);
+            for (int s = 0; s < ns; s += 3) {
+                if (s + 2 < ns) inter_load(s + 2, opc);
                 inter_mfma(opa);
                 if (s + 1 < ns) {
-                    if (s + 2 < ns) inter_load(s + 2, opa);
+                    if (s + 3 < ns) inter_load(s + 3, opa);
                     inter_mfma(opb);
+                }
+                if (s + 2 < ns) {
+                    if (s + 4 < ns) inter_load(s + 4, opb);
+                    inter_mfma(opc);
                 }
             }
         } else {
