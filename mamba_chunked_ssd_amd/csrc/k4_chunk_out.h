@@ -355,7 +355,7 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
     // inter-chunk term C_i h_c (h split into hi + lo); fragments past dstate are 0.
     // With CG the C fragments are re-read from global memory (L2) two k-steps
     // ahead instead of being held in registers for the whole block.
-    constexpr int CGD = 1;  // prefetch distance (k-steps)
+    constexpr int CGD = 2;  // prefetch distance (k-steps)
     u32x4 cq[CG ? CGD + 1 : 1][2];
     auto cg_load = [&](int ks, u32x4 (&dst)[2]) {
         const int n0 = 32 * ks + 8 * g4;
