@@ -11,7 +11,7 @@
 //
 // Design for gfx950: this is a pure HBM stream (one read of s, one write of h
 // per element, 2 flops).  Each thread owns 4 consecutive state elements of one
-// (batch, head) and walks the chunks; the loads of a batch of 4 chunks (8
+// (batch, head) and walks the chunks; the loads of a batch of 4 chunks (16
 // beyond 128 chunks) are issued before the dependent FMA chain, and
 // consecutive threads touch consecutive 16-byte words, so every wave access
 // is a fully coalesced 1 KiB.  For fp32 problems h is fp32 and may alias s
@@ -184,8 +184,8 @@ hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View 
     if (n_vec == 0) return hipSuccess;
     const int64_t blocks = (n_vec + 255) / 256;
     // measured on MI355X: batches of 4 chunks up to 128 chunks (2.7B layer
-    // 16.9 -> 15.4 us, grouped fp32 workload 1.94 -> 1.84 ms), 8 beyond
-    constexpr int kShallow = 4, kDeep = 8;
+    // 16.9 -> 15.4 us, grouped fp32 workload 1.94 -> 1.84 ms), 16 beyond
+    constexpr int kShallow = 4, kDeep = 16;
     const bool deep = p.nchunks > 128;
     const int64_t ntiles = uses_cb_tiles(p) ? p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) : 0;
     if (ntiles > 0) {
