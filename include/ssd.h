@@ -140,9 +140,8 @@ ssd_status ssd_chunk_scan_fwd_workspace_layout(const ssd_shape *shape, int64_t c
  *                    ssd_workspace_layout
  *   stream           hipStream_t or NULL
  * The four stages run in stream order: chunk cumsum, chunk state, state
- * passing, chunk output.  For some shapes the chunk-state kernel also
- * computes the cumsum and the cumsum kernel is not launched
- * (ssd_chunk_scan_fwd_stage_launches says which). */
+ * passing, chunk output, one kernel each (ssd_chunk_scan_fwd_stage_launches
+ * says which stages launch a kernel for a given problem). */
 ssd_status ssd_chunk_scan_fwd(const ssd_shape *shape,
                               const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D,
@@ -166,10 +165,10 @@ ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape,
 
 /* Which stages launch a kernel of their own for this problem (host only):
  * bit i of *mask is set for stage i (0 chunk cumsum, 1 chunk state, 2 state
- * passing, 3 chunk output).  Stage 0 is clear when the chunk-state kernel
- * computes the cumsum itself (bf16 inputs, dstate <= 128, few enough heads
- * per block); stages 0, 1 and 3 are clear when there are no tokens.  A stage
- * that launches nothing records its two profiling events back to back.
+ * passing, 3 chunk output).  Stages 0, 1 and 3 are clear when there are no
+ * tokens (only the state passing runs: final state = initial state), and
+ * every bit is clear for an empty batch.  A stage that launches nothing
+ * records its two profiling events back to back.
  * Returns SSD_ERROR_INVALID_VALUE for a NULL mask, else what the shape check
  * of ssd_chunk_scan_fwd returns. */
 ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size,

@@ -291,8 +291,6 @@ __global__ __launch_bounds__(512) void k2_chunk_state_bf16(
 // heads; they never load from global memory in the head loop, and producers
 // never store to it, so neither role waits on the other's memory traffic.
 constexpr int kProducers = 4;
-// most heads per block whose cumsum the chunk-state block computes itself
-constexpr int kFuseMaxHeads = 16;
 
 template <int T, int P>
 struct K2WsLds {
@@ -312,16 +310,11 @@ struct K2WsLds {
 // different halves -- no bank conflicts.
 __device__ __forceinline__ int b_swz(int t) { return 2 * ((t >> 3) & 1); }
 
-// With FUSE the block also computes the chunk cumsum of its own heads (the
-// stage-1 arithmetic, chunk_cumsum_wave) instead of reading the weights W from
-// a separate launch: it reads dt and A, writes G2 (hi, lo), DT and W for the
-// later stages, and keeps its heads' weights in an LDS table.
-template <int T, int P, int NCW, bool FUSE>
+template <int T, int P, int NCW>
 __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_ws(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, float *__restrict__ W,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, const float *__restrict__ W,
     float *__restrict__ S, int64_t L, int NH, int N, int G, int NC, int64_t Lp, int HPG, int HB,
-    int nhb, const uint16_t *__restrict__ dtin, const float *__restrict__ Av,
-    float *__restrict__ G2hi, float *__restrict__ G2lo, float *__restrict__ DTo) {
+    int nhb) {
     constexpr int KS = T / 32;   // k-steps of the contraction over tokens
     constexpr int PT = P / 16;   // 16-row tiles of headdim
     constexpr int TO = T / 8;    // token octets
@@ -351,31 +344,6 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
     const int h_end = min(h_begin + HB, (gi + 1) * HPG);
     const int64_t t0 = (int64_t)c * T;
 
-    // ---- fused cumsum (FUSE): every producer wave computes head 0 of the
-    //      block (each then reads back only weights it wrote itself); head
-    //      k >= 1 goes to producer wave (k - 1) % kProducers.  The dt loads
-    //      are issued before any x load so the scan does not wait for x.
-    constexpr int E = T / 64;
-    constexpr int FMH = 1 + (kFuseMaxHeads - 1 + kProducers - 1) / kProducers;  // heads per wave
-    float *wtab = reinterpret_cast<float *>(lds + 2 * BUF);  // [HB][T] (FUSE)
-    const int nhead = h_end - h_begin;
-    auto fused_head = [&](int j) { return j == 0 ? 0 : 1 + w + kProducers * (j - 1); };
-    float dv[FUSE ? FMH : 1][E];
-    if constexpr (FUSE) {
-        if (producer) {
-            const int64_t tl = t0 + lane * E;
-#pragma unroll
-            for (int j = 0; j < FMH; ++j) {
-                const int hr = fused_head(j);
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    dv[j][e] = (hr < nhead && tl + e < L)
-                                   ? bf16_to_f32(dtin[(b * L + tl + e) * NH + h_begin + hr])
-                                   : 0.f;
-            }
-        }
-    }
-
     // ---- producer side: x rows and weights of XPASS units, one head ahead,
     //      through per-head buffer resources (rows past seqlen read as 0)
     struct Pre {
@@ -393,7 +361,7 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
     };
     auto load_x = [&](int h) __attribute__((always_inline)) {
         const auto xres = buffer_rsrc(x + ((b * L + t0) * NH + h) * P, x_bytes);
-        const auto wr = buffer_rsrc(W + ((int64_t)b * NH + h) * Lp + t0, FUSE ? 0u : (uint32_t)(T * 4));
+        const auto wr = buffer_rsrc(W + ((int64_t)b * NH + h) * Lp + t0, T * 4);
 #pragma unroll
         for (int ps = 0; ps < XPASS; ++ps) {
             int po, to;
@@ -401,14 +369,13 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 pre[ps].rows[r] = buffer_load_x4(xres, ((to * 8 + r) * NH * P + po * 8) * 2);
-            if constexpr (!FUSE)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    pre[ps].wv[q] = __builtin_bit_cast(floatx4, buffer_load_x4(wr, (to * 8 + 4 * q) * 4));
+            for (int q = 0; q < 2; ++q)
+                pre[ps].wv[q] = __builtin_bit_cast(floatx4, buffer_load_x4(wr, (to * 8 + 4 * q) * 4));
         }
     };
     // scale by w_t, split into hi/lo bf16, write transposed into buffer `bf`
-    auto store_x = [&](int bf, int hr) __attribute__((always_inline)) {
+    auto store_x = [&](int bf) __attribute__((always_inline)) {
         unsigned char *xhi = lds + bf * BUF;
         unsigned char *xlo = xhi + P * T * 2;
 #pragma unroll
@@ -417,15 +384,9 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
             if (!unit(ps, po, to)) continue;
             float wt[8];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                floatx4 wq;
-                if constexpr (FUSE)
-                    wq = *reinterpret_cast<const floatx4 *>(wtab + hr * T + to * 8 + 4 * q);
-                else
-                    wq = pre[ps].wv[q];
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) wt[4 * q + i] = wq[i];
-            }
+                for (int i = 0; i < 4; ++i) wt[4 * q + i] = pre[ps].wv[q][i];
             // one pair of columns (dword i of every row) at a time
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -454,33 +415,6 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
         }
     };
     if (producer && h_begin < h_end) load_x(h_begin);  // in flight during the B^T staging
-    // cumsums of this producer wave's heads j in [j0, j1)
-    auto fused_cumsums = [&](int j0, int j1) __attribute__((always_inline)) {
-        if constexpr (FUSE) {
-#pragma unroll
-            for (int j = 0; j < FMH; ++j) {
-                if (j < j0 || j >= j1) continue;
-                const int hr = fused_head(j);
-                if (hr < nhead) {  // wave-uniform
-                    float ghi[E], glo[E], wt[E];
-                    chunk_cumsum_wave<E>(dv[j], Av[h_begin + hr], lane, ghi, glo, wt);
-                    store_vec<E>(wtab + hr * T + lane * E, wt);
-                    if (j > 0 || w == 0) {  // one writer per head
-                        const int64_t base = ((int64_t)b * NH + h_begin + hr) * Lp + t0 + lane * E;
-                        store_vec<E>(G2hi + base, ghi);
-                        store_vec<E>(G2lo + base, glo);
-                        store_vec<E>(DTo + base, dv[j]);
-                        store_vec<E>(W + base, wt);
-                    }
-                }
-            }
-            // this wave's table writes are done before it reads head 0 back
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-    };
-    // head 0 before its staging; the other heads after head 1's loads are
-    // issued (they are first read after the barrier that ends the prologue)
-    if (producer) fused_cumsums(0, 1);
 
     // ---- B for this chunk; each consumer wave keeps its fragments in
     //      registers.  With dstate 128 each consumer wave copies its own 32
@@ -563,16 +497,15 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
 
     // ---- heads: producers stage head i + 1 while consumers compute head i
     if (producer && h_begin < h_end) {
-        store_x(0, 0);
+        store_x(0);
         if (h_begin + 1 < h_end) load_x(h_begin + 1);
     }
-    if (producer) fused_cumsums(1, FMH);
     __syncthreads();
     for (int i = 0; h_begin + i < h_end; ++i) {
         const int h = h_begin + i;
         if (producer) {
             if (h + 1 < h_end) {
-                store_x((i + 1) & 1, i + 1);
+                store_x((i + 1) & 1);
                 if (h + 2 < h_end) load_x(h + 2);
             }
         } else if (32 * cw < N) {
@@ -773,41 +706,31 @@ __global__ __launch_bounds__(512) void k2_chunk_state_f32(
     }
 }
 
-// The producer/consumer kernel computes the cumsum itself when its heads'
-// weight tables fit in the LDS beside the two x^T buffers.
-template <int T, int P>
-bool fuses_cumsum_tp(const Problem &p, const Plan &plan) {
-    return p.bf16 && p.dstate <= 128 && K2WsLds<T, P>::fits && plan.k2_heads_per_block <= kFuseMaxHeads &&
-           K2WsLds<T, P>::total + (size_t)plan.k2_heads_per_block * T * 4 <= 160 * 1024;
-}
-
 template <int T, int P>
 hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const void *B,
-                     float *W, float *S, const void *dt, const float *A, G2Pair G2, float *DT,
-                     hipStream_t stream, const LaunchEvents &ev) {
+                     const float *W, float *S, hipStream_t stream, const LaunchEvents &ev) {
     const int HB = plan.k2_heads_per_block;
     const int nhb = (int)((p.heads_per_group + HB - 1) / HB);
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
     if (blocks == 0) return hipSuccess;
     if (p.bf16 && p.dstate <= 128 && K2WsLds<T, P>::fits) {
         if constexpr (K2WsLds<T, P>::fits) {
-            const bool fuse = fuses_cumsum_tp<T, P>(p, plan);
-            const size_t lds = K2WsLds<T, P>::total + (fuse ? (size_t)HB * T * 4 : 0);
+            constexpr size_t lds = K2WsLds<T, P>::total;
             auto go = [&](auto kern, int ncw) -> hipError_t {
                 if (allow_lds<decltype(kern)::value>(lds) != hipSuccess) return hipErrorInvalidValue;
                 launch_kernel(decltype(kern)::value, dim3((unsigned)blocks),
                                    dim3(64 * (kProducers + ncw)), lds, stream, ev,
                                    static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                                    W, S, p.seqlen, (int)p.nheads, (int)p.dstate, (int)p.ngroups,
-                                   (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB, nhb,
-                                   static_cast<const uint16_t *>(dt), A, G2.hi, G2.lo, DT);
+                                   (int)p.nchunks, p.padded_len, (int)p.heads_per_group, HB, nhb);
                 return hipSuccess;
             };
-#define SSD_K2_WS(NCW, F) \
-    go(std::integral_constant<decltype(&k2_chunk_state_bf16_ws<T, P, NCW, F>), &k2_chunk_state_bf16_ws<T, P, NCW, F>>{}, NCW)
-            const hipError_t e = p.dstate <= 64 ? (fuse ? SSD_K2_WS(2, true) : SSD_K2_WS(2, false))
-                                                : (fuse ? SSD_K2_WS(4, true) : SSD_K2_WS(4, false));
-#undef SSD_K2_WS
+            const hipError_t e =
+                p.dstate <= 64
+                    ? go(std::integral_constant<decltype(&k2_chunk_state_bf16_ws<T, P, 2>),
+                                                &k2_chunk_state_bf16_ws<T, P, 2>>{}, 2)
+                    : go(std::integral_constant<decltype(&k2_chunk_state_bf16_ws<T, P, 4>),
+                                                &k2_chunk_state_bf16_ws<T, P, 4>>{}, 4);
             if (e != hipSuccess) return e;
         }
     } else if (p.bf16) {
@@ -841,23 +764,12 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
 
 template <int T>
 hipError_t launch_t(const Problem &p, const Plan &plan, const void *x, const void *B,
-                    float *W, float *S, const void *dt, const float *A, G2Pair G2, float *DT,
-                    hipStream_t stream, const LaunchEvents &ev) {
+                    const float *W, float *S, hipStream_t stream, const LaunchEvents &ev) {
     switch (p.headdim) {
-        case 32: return launch_tp<T, 32>(p, plan, x, B, W, S, dt, A, G2, DT, stream, ev);
-        case 64: return launch_tp<T, 64>(p, plan, x, B, W, S, dt, A, G2, DT, stream, ev);
-        case 128: return launch_tp<T, 128>(p, plan, x, B, W, S, dt, A, G2, DT, stream, ev);
+        case 32: return launch_tp<T, 32>(p, plan, x, B, W, S, stream, ev);
+        case 64: return launch_tp<T, 64>(p, plan, x, B, W, S, stream, ev);
+        case 128: return launch_tp<T, 128>(p, plan, x, B, W, S, stream, ev);
         default: return hipErrorInvalidValue;
-    }
-}
-
-template <int T>
-bool fuses_cumsum_t(const Problem &p, const Plan &plan) {
-    switch (p.headdim) {
-        case 32: return fuses_cumsum_tp<T, 32>(p, plan);
-        case 64: return fuses_cumsum_tp<T, 64>(p, plan);
-        case 128: return fuses_cumsum_tp<T, 128>(p, plan);
-        default: return false;
     }
 }
 
@@ -876,22 +788,12 @@ int chunk_state_blocks_per_cu(const Problem &p) {
     return (int)std::max<size_t>(1, std::min<size_t>(2, by_lds));
 }
 
-bool chunk_state_fuses_cumsum(const Problem &p, const Plan &plan) {
-    switch (p.chunk) {
-        case 64: return fuses_cumsum_t<64>(p, plan);
-        case 128: return fuses_cumsum_t<128>(p, plan);
-        case 256: return fuses_cumsum_t<256>(p, plan);
-        default: return false;
-    }
-}
-
 hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
-                              float *W, float *S, const void *dt, const float *A, G2Pair G2,
-                              float *DT, hipStream_t stream, const LaunchEvents &ev) {
+                              const float *W, float *S, hipStream_t stream, const LaunchEvents &ev) {
     switch (p.chunk) {
-        case 64: return launch_t<64>(p, plan, x, B, W, S, dt, A, G2, DT, stream, ev);
-        case 128: return launch_t<128>(p, plan, x, B, W, S, dt, A, G2, DT, stream, ev);
-        case 256: return launch_t<256>(p, plan, x, B, W, S, dt, A, G2, DT, stream, ev);
+        case 64: return launch_t<64>(p, plan, x, B, W, S, stream, ev);
+        case 128: return launch_t<128>(p, plan, x, B, W, S, stream, ev);
+        case 256: return launch_t<256>(p, plan, x, B, W, S, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -270,12 +270,9 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
                hipEventRecord(ev.stop, stream) == hipSuccess;
     };
     if (p.nchunks > 0) {
-        if (chunk_state_fuses_cumsum(p, plan)) {
-            if (!skip(0)) return SSD_ERROR_LAUNCH;  // the chunk-state launch computes it
-        } else if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess) {
+        if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
-        }
-        if (launch_chunk_state(p, plan, x, B, Wf, S, dt, A, G2, DTf, stream, events_of(1)) != hipSuccess)
+        if (launch_chunk_state(p, plan, x, B, Wf, S, stream, events_of(1)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
     } else if (!skip(0) || !skip(1)) {
         return SSD_ERROR_LAUNCH;
@@ -316,10 +313,7 @@ ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chu
     if (st != SSD_OK) return st;
     uint32_t m = 0;
     if (p.batch > 0) {
-        if (p.nchunks > 0) {
-            if (!chunk_state_fuses_cumsum(p, make_plan(p))) m |= 1u;
-            m |= 2u | 8u;
-        }
+        if (p.nchunks > 0) m |= 1u | 2u | 8u;
         if (p.nheads > 0) m |= 4u;
     }
     *mask = m;

@@ -69,13 +69,8 @@ hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A,
 
 // Stage 2: per-chunk input state s_c = sum_t W_t x_t B_t^T,
 // written as (batch, nheads, nchunks, headdim, dstate) fp32.
-// With the producer/consumer bf16 kernel and few enough heads per block, the
-// launch also computes the stage-1 cumsum (G2, DT and W) of its own heads
-// from dt and A, and stage 1 is not launched (chunk_state_fuses_cumsum).
 hipError_t launch_chunk_state(const Problem &p, const Plan &plan, const void *x, const void *B,
-                              float *W, float *S, const void *dt, const float *A, G2Pair G2,
-                              float *DT, hipStream_t stream, const LaunchEvents &ev);
-bool chunk_state_fuses_cumsum(const Problem &p, const Plan &plan);
+                              const float *W, float *S, hipStream_t stream, const LaunchEvents &ev);
 // How many stage-2 blocks one CU holds (set by the kernel variant's LDS use).
 int chunk_state_blocks_per_cu(const Problem &p);
 
