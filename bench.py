@@ -247,16 +247,14 @@ def main(argv=None):
 
     model = stage_model(w, 4 if ydt == torch.float32 else (2 if w.dtype == "bf16" else 4))
     peak_tf = PEAK_TFLOPS[w.dtype]
-    # The cumsum is computed inside the chunk-state launch for some shapes (the
-    # library reports which stages launch kernels).  That launch reads dt and
-    # writes the cumsum, which the chunk-state byte model already counts (dt
-    # in, fp32 cumsum), so the fused stage adds no floor of its own.
+    # Stages that launch no kernel for this problem (the library says which)
+    # are reported as such and add no floor; their event pairs time nothing.
     launched = ssd.stage_launches(shape, w.chunk_size)
-    fused = {name: "chunk_state" for name in STAGES if name == "chunk_cumsum" and name not in launched}
+    skipped = {name for name in STAGES if name not in launched}
     stages = {}
     for j, name in enumerate(STAGES):
-        if name in fused:
-            stages[name] = {"us": 0.0, "fused_into": fused[name]}
+        if name in skipped:
+            stages[name] = {"us": 0.0, "launched": False}
             continue
         byts, flops = model[name]
         t_s = stage_ms[j] * 1e-3
@@ -282,7 +280,7 @@ def main(argv=None):
     e2e_t = ms_per_step * 1e-3
     e2e_floor = max(e2e_bytes / (PEAK_HBM_GBS * 1e9), e2e_flops / (peak_tf * 1e12))
     sigma_floor = sum(max(model[s][0] / (PEAK_HBM_GBS * 1e9), model[s][1] / (peak_tf * 1e12))
-                      for s in STAGES if s not in fused)
+                      for s in STAGES if s not in skipped)
 
     out = {
         "metric": METRIC,
@@ -320,9 +318,9 @@ def main(argv=None):
             for ev in e:
                 hip.destroy(ev)
         cold = np.array(cold).mean(axis=0)
-        out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES) if n not in fused}
+        out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES) if n not in skipped}
         out["cold_tokens_per_s"] = round(
-            w.tokens / (sum(cold[j] for j, n in enumerate(STAGES) if n not in fused) * 1e-3), 1)
+            w.tokens / (sum(cold[j] for j, n in enumerate(STAGES) if n not in skipped) * 1e-3), 1)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps, a.cpu_seconds)
