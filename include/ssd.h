@@ -163,16 +163,63 @@ ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape,
                                        void *workspace, size_t workspace_bytes, void *stream,
                                        void *const *stage_events);
 
+/* Launch plan: how the stages divide their work among thread blocks.  Every
+ * plan computes the same result (up to summation order); plans differ only in
+ * speed.  ssd_chunk_scan_fwd uses the plan ssd_chunk_scan_fwd_default_plan
+ * returns; ssd_chunk_scan_fwd_ex accepts any valid plan, for instance one
+ * chosen by ssd_chunk_scan_fwd_tune.  A plan is plain data owned by the
+ * caller; the library keeps none. */
+typedef enum {
+    SSD_STATE_SPLIT = 0, /* the chunk states s_c in one fully parallel launch, then
+                            the sequential carry across chunks in a second */
+    SSD_STATE_FUSED = 1  /* one launch walks the chunks of each (batch, head,
+                            dstate tile) in order, forming s_c and carrying the
+                            state in registers ("Kernel 2: fwd_pass_state");
+                            s_c is never written to the workspace */
+} ssd_state_path;
+
+typedef struct {
+    int32_t state_path;        /* ssd_state_path */
+    int32_t chunk_state_heads; /* split path: heads of one group per chunk-state
+                                  block, 1 .. nheads / ngroups */
+    int32_t chunk_out_heads;   /* heads of one group per chunk-output block,
+                                  1 .. nheads / ngroups */
+    int32_t fused_cols;        /* fused path: dstate columns per block (a
+                                  multiple of 32 that divides dstate, or dstate);
+                                  ignored by the split path */
+    int32_t reserved[4];       /* must be 0 */
+} ssd_plan;
+
+/* The plan ssd_chunk_scan_fwd uses for this problem (host only: a static
+ * model of the launch, no device access). */
+ssd_status ssd_chunk_scan_fwd_default_plan(const ssd_shape *shape, int64_t chunk_size,
+                                           ssd_plan *plan);
+
+/* ssd_chunk_scan_fwd with an explicit plan (NULL: the default plan) and
+ * optional stage events (NULL: none; else as ssd_chunk_scan_fwd_profiled).
+ * Returns SSD_ERROR_INVALID_VALUE for a plan whose fields are out of range and
+ * SSD_ERROR_UNSUPPORTED for a state path this problem has no kernel for
+ * (the fused path needs bf16 inputs). */
+ssd_status ssd_chunk_scan_fwd_ex(const ssd_shape *shape,
+                                 const void *x, const void *dt, const float *A,
+                                 const void *B, const void *C, const float *D,
+                                 int64_t chunk_size, const float *initial_states,
+                                 void *y, float *final_states,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const ssd_plan *plan, void *const *stage_events);
+
 /* Which stages launch a kernel of their own for this problem (host only):
  * bit i of *mask is set for stage i (0 chunk cumsum, 1 chunk state, 2 state
  * passing, 3 chunk output).  Stages 0, 1 and 3 are clear when there are no
  * tokens (only the state passing runs: final state = initial state), and
- * every bit is clear for an empty batch.  A stage that launches nothing
- * records its two profiling events back to back.
- * Returns SSD_ERROR_INVALID_VALUE for a NULL mask, else what the shape check
- * of ssd_chunk_scan_fwd returns. */
+ * every bit is clear for an empty batch.  Under a plan with the fused state
+ * path (plan NULL: the default plan) stage 1 is that fused launch and stage 2
+ * launches nothing.  A stage that launches nothing records its two profiling
+ * events back to back.
+ * Returns SSD_ERROR_INVALID_VALUE for a NULL mask or an invalid plan, else
+ * what the shape check of ssd_chunk_scan_fwd returns. */
 ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size,
-                                             uint32_t *mask);
+                                             const ssd_plan *plan, uint32_t *mask);
 
 /* Static, human-readable description of a status code. */
 const char *ssd_status_string(ssd_status status);

@@ -42,6 +42,8 @@ EXPORTS = [
     "ssd_chunk_scan_fwd",
     "ssd_chunk_scan_fwd_profiled",
     "ssd_chunk_scan_fwd_stage_launches",
+    "ssd_chunk_scan_fwd_default_plan",
+    "ssd_chunk_scan_fwd_ex",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -86,6 +88,34 @@ class WorkspaceLayout(ctypes.Structure):
     ]
 
 
+SSD_STATE_SPLIT = 0
+SSD_STATE_FUSED = 1
+
+
+class Plan(ctypes.Structure):
+    """ssd_plan: how the stages divide their work among thread blocks."""
+    _fields_ = [
+        ("state_path", ctypes.c_int32),
+        ("chunk_state_heads", ctypes.c_int32),
+        ("chunk_out_heads", ctypes.c_int32),
+        ("fused_cols", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
+    ]
+
+    def as_dict(self) -> dict:
+        return {"state_path": "fused" if self.state_path == SSD_STATE_FUSED else "split",
+                "chunk_state_heads": self.chunk_state_heads,
+                "chunk_out_heads": self.chunk_out_heads, "fused_cols": self.fused_cols}
+
+    def __repr__(self):
+        return "Plan(%s)" % ", ".join("%s=%s" % kv for kv in self.as_dict().items())
+
+
+def make_plan(state_path="split", chunk_state_heads=1, chunk_out_heads=1, fused_cols=0) -> Plan:
+    sp = SSD_STATE_FUSED if state_path in ("fused", SSD_STATE_FUSED) else SSD_STATE_SPLIT
+    return Plan(sp, chunk_state_heads, chunk_out_heads, fused_cols)
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -113,8 +143,13 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
         lib.ssd_chunk_scan_fwd_profiled.argtypes = fwd_args + [ctypes.POINTER(ctypes.c_void_p)]
         lib.ssd_chunk_scan_fwd_profiled.restype = ctypes.c_int
-        lib.ssd_chunk_scan_fwd_stage_launches.argtypes = [sp, i64, ctypes.POINTER(ctypes.c_uint32)]
+        pp = ctypes.POINTER(Plan)
+        lib.ssd_chunk_scan_fwd_stage_launches.argtypes = [sp, i64, pp, ctypes.POINTER(ctypes.c_uint32)]
         lib.ssd_chunk_scan_fwd_stage_launches.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_default_plan.argtypes = [sp, i64, pp]
+        lib.ssd_chunk_scan_fwd_default_plan.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_ex.argtypes = fwd_args + [pp, ctypes.POINTER(ctypes.c_void_p)]
+        lib.ssd_chunk_scan_fwd_ex.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []
@@ -161,11 +196,26 @@ def workspace_layout(shape: Shape, chunk_size: int) -> WorkspaceLayout:
 STAGES = ("chunk_cumsum", "chunk_state", "state_pass", "chunk_out")
 
 
-def stage_launches(shape: Shape, chunk_size: int) -> tuple:
-    """Names of the stages that launch a kernel of their own for this problem."""
+def default_plan(shape: Shape, chunk_size: int) -> Plan:
+    """The launch plan ``ssd_chunk_scan_fwd`` uses for this problem (host only)."""
+    plan = Plan()
+    st = load_library().ssd_chunk_scan_fwd_default_plan(ctypes.byref(shape), chunk_size,
+                                                        ctypes.byref(plan))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_default_plan")
+    return plan
+
+
+def _plan_ref(plan):
+    return None if plan is None else ctypes.byref(plan)
+
+
+def stage_launches(shape: Shape, chunk_size: int, plan: Plan | None = None) -> tuple:
+    """Names of the stages that launch a kernel of their own for this problem
+    (under ``plan``; None = the default plan)."""
     mask = ctypes.c_uint32()
     st = load_library().ssd_chunk_scan_fwd_stage_launches(ctypes.byref(shape), chunk_size,
-                                                          ctypes.byref(mask))
+                                                          _plan_ref(plan), ctypes.byref(mask))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_stage_launches")
     return tuple(n for i, n in enumerate(STAGES) if mask.value >> i & 1)
@@ -197,7 +247,7 @@ def _check(t, name, dtype, shape, device):
 def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states=None,
                    return_final_states: bool = False, *, y_dtype=None, out=None,
                    final_out=None, workspace=None, keep_intermediates: bool = False,
-                   stream=None, events=None):
+                   stream=None, events=None, plan: Plan | None = None):
     """Run ``ssd_chunk_scan_fwd`` on the current (or given) stream.
 
     x (b, L, nh, p) and dt (b, L, nh), B/C (b, L, g, n): float32 or bfloat16,
@@ -208,7 +258,8 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
     with ``keep_intermediates`` its layout is :func:`workspace_layout` of the
     shape with the keep flag.  ``events``: 8 raw hipEvent_t handles (ints), a
     (start, stop) pair per stage recorded by each kernel's own dispatch
-    (``ssd_chunk_scan_fwd_profiled``).
+    (``ssd_chunk_scan_fwd_profiled``).  ``plan``: an explicit launch plan
+    (:class:`Plan`; ``ssd_chunk_scan_fwd_ex``), None for the default one.
     """
     torch = _torch()
     lib = load_library()
@@ -253,13 +304,18 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
     args = [ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
             int(chunk_size), _ptr(initial_states), _ptr(y), _ptr(fin), _ptr(workspace),
             workspace.numel() * workspace.element_size(), ctypes.c_void_p(s)]
-    if events is None:
-        st = lib.ssd_chunk_scan_fwd(*args)
-        where = "ssd_chunk_scan_fwd"
-    else:
+    ev = None
+    if events is not None:
         if len(events) != 8:
             raise ValueError("events: a (start, stop) pair for each of the 4 stages")
         ev = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e) for e in events])
+    if plan is not None:
+        st = lib.ssd_chunk_scan_fwd_ex(*args, ctypes.byref(plan), ev)
+        where = "ssd_chunk_scan_fwd_ex"
+    elif ev is None:
+        st = lib.ssd_chunk_scan_fwd(*args)
+        where = "ssd_chunk_scan_fwd"
+    else:
         st = lib.ssd_chunk_scan_fwd_profiled(*args, ev)
         where = "ssd_chunk_scan_fwd_profiled"
     if st != 0:

@@ -61,10 +61,6 @@ namespace k4 {
 // gfx950 LDS per CU (and the most one block may use)
 constexpr size_t kLdsBytes = 160 * 1024;
 
-#ifndef K4_SCHED_PATTERN
-#define K4_SCHED_PATTERN 1
-#endif
-
 
 // Wave w owns row tiles I0 = w and I1 = T/16 - 1 - w.  Its S slots are laid
 // out as [I0: J = 0..I0][pad to even][I1: J = 0..I1][pad to even]; the total
@@ -1267,21 +1263,11 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         // Interleave the next pair's VALU work with this pair's MFMAs: a
         // wave64 VALU op takes 4 cycles and an MFMA 16, so four or five of
         // them run under each MFMA instead of waiting for the whole group.
-#if K4_SCHED_PATTERN == 1
 #pragma unroll
         for (int k = 0; k < 2 * PT; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
         }
-#elif K4_SCHED_PATTERN == 2
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
-#pragma unroll
-        for (int k = 0; k < 2 * PT; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        }
-#endif
         __builtin_amdgcn_sched_barrier(0);
     });
     static_for<PT>([&](auto kc) {  // stores left over when there are fewer pairs than tiles

@@ -161,11 +161,60 @@ const int kNumCUs = 256;
 
 Plan make_plan(const Problem &p) {
     Plan plan;
+    plan.fused_state = false;
     plan.k2_heads_per_block = pick_heads_per_block(p, chunk_state_blocks_per_cu(p) * kNumCUs, 1.0);
     plan.k4_heads_per_block = pick_heads_per_block(p, kNumCUs, 1.0);
+    plan.fused_cols = (int)p.dstate;
     return plan;
 }
 
+namespace {
+
+// The fused state path has no kernel yet; its blocks cover a multiple of 32
+// dstate columns (or all of them).
+bool fused_supported(const Problem &) { return false; }
+bool fused_cols_ok(const Problem &p, int64_t cols) {
+    if (cols == p.dstate) return true;
+    return cols >= 32 && cols % 32 == 0 && p.dstate % cols == 0;
+}
+
+ssd_plan to_abi(const Plan &q) {
+    ssd_plan r;
+    std::memset(&r, 0, sizeof(r));
+    r.state_path = q.fused_state ? SSD_STATE_FUSED : SSD_STATE_SPLIT;
+    r.chunk_state_heads = q.k2_heads_per_block;
+    r.chunk_out_heads = q.k4_heads_per_block;
+    r.fused_cols = q.fused_cols;
+    return r;
+}
+
+// Check a caller's plan against the problem; NULL selects the default plan.
+ssd_status plan_from_abi(const Problem &p, const ssd_plan *in, Plan *out) {
+    if (in == nullptr) {
+        *out = make_plan(p);
+        return SSD_OK;
+    }
+    for (int i = 0; i < 4; ++i)
+        if (in->reserved[i] != 0) return SSD_ERROR_INVALID_VALUE;
+    if (in->state_path != SSD_STATE_SPLIT && in->state_path != SSD_STATE_FUSED)
+        return SSD_ERROR_INVALID_VALUE;
+    const int64_t hpg = p.heads_per_group;
+    if (in->chunk_state_heads < 1 || in->chunk_state_heads > hpg || in->chunk_out_heads < 1 ||
+        in->chunk_out_heads > hpg)
+        return SSD_ERROR_INVALID_VALUE;
+    const bool fused = in->state_path == SSD_STATE_FUSED;
+    if (fused && !fused_cols_ok(p, in->fused_cols)) return SSD_ERROR_INVALID_VALUE;
+    if (fused && !fused_supported(p)) return SSD_ERROR_UNSUPPORTED;
+    Plan q;
+    q.fused_state = fused;
+    q.k2_heads_per_block = in->chunk_state_heads;
+    q.k4_heads_per_block = in->chunk_out_heads;
+    q.fused_cols = fused ? in->fused_cols : (int)p.dstate;
+    *out = q;
+    return SSD_OK;
+}
+
+}  // namespace
 }  // namespace ssd
 
 using namespace ssd;
@@ -188,12 +237,25 @@ ssd_status ssd_chunk_scan_fwd_workspace_layout(const ssd_shape *shape, int64_t c
     return SSD_OK;
 }
 
+ssd_status ssd_chunk_scan_fwd_default_plan(const ssd_shape *shape, int64_t chunk_size, ssd_plan *plan) {
+    if (plan == nullptr) return SSD_ERROR_INVALID_VALUE;
+    Problem p;
+    const ssd_status st = check_shape(shape, chunk_size, &p);
+    if (st != SSD_OK) return st;
+    *plan = to_abi(make_plan(p));
+    return SSD_OK;
+}
+
 static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt, const float *A,
                           const void *B, const void *C, const float *D, int64_t chunk_size,
                           const float *init, void *y, float *final_states, void *workspace,
-                          size_t workspace_bytes, void *stream_handle, void *const *events) {
+                          size_t workspace_bytes, void *stream_handle, const ssd_plan *abi_plan,
+                          void *const *events) {
     Problem p;
-    const ssd_status st = check_shape(shape, chunk_size, &p);
+    ssd_status st = check_shape(shape, chunk_size, &p);
+    if (st != SSD_OK) return st;
+    Plan plan;
+    st = plan_from_abi(p, abi_plan, &plan);
     if (st != SSD_OK) return st;
     const bool keep = (shape->flags & SSD_FLAG_KEEP_INTERMEDIATES) != 0;
     const ssd_workspace_layout lay = layout_for(p, keep);
@@ -251,7 +313,6 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
     float *S = reinterpret_cast<float *>(ws + lay.s);
     float *Hs = reinterpret_cast<float *>(ws + lay.h);
     float *CB = reinterpret_cast<float *>(ws + lay.cb);
-    const Plan plan = make_plan(p);
 
     // stage i's (start, stop) events, recorded by its kernel's dispatch; a
     // stage with nothing to do records both at once
@@ -293,7 +354,16 @@ ssd_status ssd_chunk_scan_fwd(const ssd_shape *shape, const void *x, const void 
                               const float *initial_states, void *y, float *final_states,
                               void *workspace, size_t workspace_bytes, void *stream) {
     return forward(shape, x, dt, A, B, C, D, chunk_size, initial_states, y, final_states, workspace,
-                   workspace_bytes, stream, nullptr);
+                   workspace_bytes, stream, nullptr, nullptr);
+}
+
+ssd_status ssd_chunk_scan_fwd_ex(const ssd_shape *shape, const void *x, const void *dt, const float *A,
+                                 const void *B, const void *C, const float *D, int64_t chunk_size,
+                                 const float *initial_states, void *y, float *final_states,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const ssd_plan *plan, void *const *stage_events) {
+    return forward(shape, x, dt, A, B, C, D, chunk_size, initial_states, y, final_states, workspace,
+                   workspace_bytes, stream, plan, stage_events);
 }
 
 ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape, const void *x, const void *dt,
@@ -303,18 +373,26 @@ ssd_status ssd_chunk_scan_fwd_profiled(const ssd_shape *shape, const void *x, co
                                        void *stream, void *const *stage_events) {
     if (stage_events == nullptr) return SSD_ERROR_INVALID_VALUE;
     return forward(shape, x, dt, A, B, C, D, chunk_size, initial_states, y, final_states, workspace,
-                   workspace_bytes, stream, stage_events);
+                   workspace_bytes, stream, nullptr, stage_events);
 }
 
-ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size, uint32_t *mask) {
+ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size,
+                                             const ssd_plan *abi_plan, uint32_t *mask) {
     if (mask == nullptr) return SSD_ERROR_INVALID_VALUE;
     Problem p;
-    const ssd_status st = check_shape(shape, chunk_size, &p);
+    ssd_status st = check_shape(shape, chunk_size, &p);
+    if (st != SSD_OK) return st;
+    Plan plan;
+    st = plan_from_abi(p, abi_plan, &plan);
     if (st != SSD_OK) return st;
     uint32_t m = 0;
     if (p.batch > 0) {
-        if (p.nchunks > 0) m |= 1u | 2u | 8u;
-        if (p.nheads > 0) m |= 4u;
+        if (p.nchunks > 0) m |= 1u | 8u;
+        // the fused path is one launch (stage 1) that also carries the state
+        // and writes the final state; with no chunks only the carry runs
+        if (p.nchunks > 0 && plan.fused_state) m |= 2u;
+        else if (p.nchunks > 0) m |= 2u | 4u;
+        else m |= 4u;
     }
     *mask = m;
     return SSD_OK;
@@ -332,6 +410,6 @@ const char *ssd_status_string(ssd_status s) {
     return "unknown status";
 }
 
-int ssd_version(void) { return 100; }
+int ssd_version(void) { return 200; }
 
 }  // extern "C"

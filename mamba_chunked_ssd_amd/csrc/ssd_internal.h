@@ -8,6 +8,9 @@
 
 namespace ssd {
 
+// LDS per compute unit on gfx950, the most one block may use.
+constexpr size_t kLdsPerCu = 160 * 1024;
+
 // Problem description after validation, with the derived sizes every stage
 // needs.  All element counts are int64.
 struct Problem {
@@ -19,10 +22,12 @@ struct Problem {
     bool y_bf16;              // element type of y
 };
 
-// Launch configuration chosen on the host per problem.
+// Launch configuration chosen on the host per problem (the C ABI's ssd_plan).
 struct Plan {
+    bool fused_state;         // stages 2 and 3 in one launch (bf16 only)
     int k2_heads_per_block;   // heads of one group sharing a staged B chunk
     int k4_heads_per_block;   // heads of one group sharing one C B^T tile set
+    int fused_cols;           // fused path: dstate columns per block
 };
 
 Plan make_plan(const Problem &p);
@@ -91,16 +96,18 @@ hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, c
                             const LaunchEvents &ev);
 
 // Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
-// CU).  The template parameter is the kernel itself, so each kernel caches
-// its own "done" flag; a racing second call only repeats a harmless set.
+// CU).  The template parameter is the kernel itself.  The attribute is set on
+// the first call for that kernel through a function-local static, whose
+// initialisation C++ makes thread-safe (concurrent first calls wait for the
+// one that runs it); afterwards the result is only read, so there is no
+// mutable shared state.  A failure is kept and returned to every caller.
 template <auto Kernel>
 hipError_t allow_lds(size_t bytes) {
-    static bool done = false;
-    if (done || bytes <= 65536) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) done = true;
-    return e;
+    if (bytes <= 65536) return hipSuccess;
+    static const hipError_t status = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kLdsPerCu);
+    return status;
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).

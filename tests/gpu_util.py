@@ -38,28 +38,32 @@ def to_device(inp: dict, dtype: str, dev="cuda"):
 
 
 def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = True,
-        y_dtype: str = "f32"):
-    """Forward pass; returns numpy fp64 dict with y, final and (keep) G2/DT/W/S/H
-    (G2 = the stored hi + lo pair, summed in fp64)."""
+        y_dtype: str = "f32", plan=None):
+    """Forward pass (under ``plan``, None = the default plan); returns numpy
+    fp64 dict with y, final and (keep) G2/DT/W/S/H (G2 = the stored hi + lo
+    pair, summed in fp64).  S is absent when the plan fuses the state stages
+    (the fused launch never writes s_c)."""
     t = to_device(inp, dtype)
     b, L, nh, p = t["x"].shape
     g, n = t["B"].shape[2], t["B"].shape[3]
     ws = None
     lay = None
+    shape = ssd.make_shape(b, L, nh, p, n, g, dtype, keep=keep, y_dtype=y_dtype)
+    eff = plan if plan is not None else ssd.default_plan(shape, chunk)
     if keep:
-        shape = ssd.make_shape(b, L, nh, p, n, g, dtype, keep=True, y_dtype=y_dtype)
         lay = ssd.workspace_layout(shape, chunk)
         ws = torch.empty(max(lay.total, 1), dtype=torch.uint8, device="cuda")
     res = ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=chunk,
                              initial_states=t["h0"], return_final_states=final, workspace=ws,
-                             keep_intermediates=keep,
+                             keep_intermediates=keep, plan=plan,
                              y_dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32)
     torch.cuda.synchronize()
     if final:
         y, fin = res
     else:
         y, fin = res, None
-    out = {"y": y.double().cpu().numpy(), "final": None if fin is None else fin.double().cpu().numpy()}
+    out = {"y": y.double().cpu().numpy(), "final": None if fin is None else fin.double().cpu().numpy(),
+           "plan": eff}
     if keep:
         nc, Lp = lay.nchunks, lay.padded_len
 
@@ -70,7 +74,8 @@ def run(inp: dict, dtype: str, chunk: int, keep: bool = False, final: bool = Tru
         out["G2"] = view(lay.g2_hi, (b, nh, Lp)) + view(lay.g2_lo, (b, nh, Lp))
         out["DT"] = view(lay.dt, (b, nh, Lp))
         out["W"] = view(lay.w, (b, nh, Lp))
-        out["S"] = view(lay.s, (b, nh, nc, p, n))
+        if eff.state_path != ssd.SSD_STATE_FUSED:
+            out["S"] = view(lay.s, (b, nh, nc, p, n))
         if dtype == "bf16":
             # h_c as hi and lo bf16 planes per (batch, head, chunk)
             cnt = b * nh * nc * 2 * p * n

@@ -64,15 +64,15 @@ def test_stage_launches(lib):
     s = ssd.make_shape(0, 100, 4, 64, 128, 1, "bf16")
     assert ssd.stage_launches(s, 256) == ()
     m = ctypes.c_uint32()
-    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 256, None) == 1
-    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 96, ctypes.byref(m)) != 0
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 256, None, None) == 1
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 96, None, ctypes.byref(m)) != 0
 
 
 def test_status_strings(lib):
     assert lib.ssd_status_string(0) == b"ok"
     for code in range(1, 6):
         assert len(lib.ssd_status_string(code)) > 10
-    assert lib.ssd_version() == 100
+    assert lib.ssd_version() == 200
 
 
 def shape(**kw):
@@ -242,3 +242,66 @@ def test_empty_batch_is_a_noop(lib):
     # batch == 0: nothing to compute, so no pointer is needed and nothing launches
     s = shape(batch=0)
     assert lib.ssd_chunk_scan_fwd(ctypes.byref(s), *([None] * 6), 256, None, None, None, None, 0, None) == 0
+
+
+# ---------------------------------------------------------------------------
+# launch plans (host only)
+# ---------------------------------------------------------------------------
+
+def test_default_plan_is_valid(lib):
+    for s, T in [(ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16"), 256),
+                 (ssd.make_shape(8, 4096, 80, 64, 128, 1, "bf16"), 256),
+                 (ssd.make_shape(1, 65536, 32, 64, 256, 1, "bf16"), 256),
+                 (ssd.make_shape(4, 16384, 64, 128, 256, 8, "f32"), 128),
+                 (ssd.make_shape(1, 256, 4, 32, 16, 1, "f32"), 64)]:
+        plan = ssd.default_plan(s, T)
+        hpg = s.nheads // s.ngroups
+        assert 1 <= plan.chunk_state_heads <= hpg and 1 <= plan.chunk_out_heads <= hpg
+        assert plan.state_path in (ssd.SSD_STATE_SPLIT, ssd.SSD_STATE_FUSED)
+        assert list(plan.reserved) == [0, 0, 0, 0]
+        # the default plan and no plan launch the same stages
+        assert ssd.stage_launches(s, T, plan) == ssd.stage_launches(s, T)
+
+
+def test_default_plan_errors(lib):
+    s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
+    assert lib.ssd_chunk_scan_fwd_default_plan(ctypes.byref(s), 256, None) == 1
+    plan = ssd.Plan()
+    assert lib.ssd_chunk_scan_fwd_default_plan(ctypes.byref(s), 96, ctypes.byref(plan)) == 2
+    assert lib.ssd_chunk_scan_fwd_default_plan(None, 256, ctypes.byref(plan)) == 1
+
+
+@pytest.mark.parametrize("bad", [
+    dict(chunk_state_heads=0), dict(chunk_out_heads=0), dict(chunk_state_heads=81),
+    dict(chunk_out_heads=81), dict(state_path=2), dict(state_path=-1),
+])
+def test_invalid_plans_rejected(lib, bad):
+    s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
+    plan = ssd.default_plan(s, 256)
+    for k, v in bad.items():
+        setattr(plan, k, v)
+    m = ctypes.c_uint32()
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 256, ctypes.byref(plan),
+                                                 ctypes.byref(m)) == 1
+
+
+def test_plan_reserved_must_be_zero(lib):
+    s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
+    plan = ssd.default_plan(s, 256)
+    plan.reserved[2] = 7
+    m = ctypes.c_uint32()
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 256, ctypes.byref(plan),
+                                                 ctypes.byref(m)) == 1
+
+
+@no_gpu
+def test_invalid_plan_rejected_before_launch(lib):
+    s = shape()
+    plan = ssd.default_plan(s, 256)
+    plan.chunk_out_heads = 0
+    f = Fake()
+    v = lambda a: ctypes.c_void_p(a)  # noqa: E731
+    st = lib.ssd_chunk_scan_fwd_ex(ctypes.byref(s), v(f()), v(f()), v(f()), v(f()), v(f()), v(f()), 256,
+                                   None, v(f()), v(f()), v(f()), ssd.workspace_size(s, 256), None,
+                                   ctypes.byref(plan), None)
+    assert st == 1
