@@ -58,7 +58,9 @@ typedef enum {
     SSD_ERROR_UNSUPPORTED = 2,   /* valid problem outside the sizes the kernels are built for */
     SSD_ERROR_MISALIGNED = 3,    /* a pointer below its required alignment */
     SSD_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than ssd_chunk_scan_fwd_workspace_size */
-    SSD_ERROR_LAUNCH = 5         /* the HIP runtime refused a launch or an event record */
+    SSD_ERROR_LAUNCH = 5,        /* the HIP runtime refused a launch or an event record */
+    SSD_ERROR_SCRATCH = 6        /* ssd_chunk_scan_fwd_noalloc: the problem needs more workspace
+                                    than the library's scratch holds (SSD_NOALLOC_SCRATCH_BYTES) */
 } ssd_status;
 
 /* Keep the per-chunk input states s_c and the chunk-start states h_c in two
@@ -220,6 +222,28 @@ ssd_status ssd_chunk_scan_fwd_ex(const ssd_shape *shape,
  * what the shape check of ssd_chunk_scan_fwd returns. */
 ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size,
                                              const ssd_plan *plan, uint32_t *mask);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * pass of ssd_chunk_scan_fwd (default plan) with no workspace argument.  The
+ * workspace is a device array of SSD_NOALLOC_SCRATCH_BYTES inside the library
+ * (each GPU the library runs on holds its own copy from the first call on it
+ * until the process ends); this call allocates nothing.  The caller still
+ * owns and passes every input and output, with the conventions and checks of
+ * ssd_chunk_scan_fwd.  Problems whose workspace
+ * (ssd_chunk_scan_fwd_workspace_size) exceeds the scratch are rejected with
+ * SSD_ERROR_SCRATCH before anything is enqueued; shape->flags must be 0.
+ * All calls on one GPU share its scratch, and the scratch keeps the last
+ * call's contents (nothing in it needs clearing: the stages overwrite what
+ * they read): calls that overlap in time on one GPU -- from two streams or
+ * two threads -- race and give undefined results.  This entry point is the
+ * one exception to "no mutable global state". */
+#define SSD_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_shape *shape,
+                                      const void *x, const void *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      int64_t chunk_size, const float *initial_states,
+                                      void *y, float *final_states, void *stream);
 
 /* Static, human-readable description of a status code. */
 const char *ssd_status_string(ssd_status status);

@@ -33,7 +33,9 @@ STATUS = {
     3: "SSD_ERROR_MISALIGNED",
     4: "SSD_ERROR_WORKSPACE",
     5: "SSD_ERROR_LAUNCH",
+    6: "SSD_ERROR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 # Symbols include/ssd.h declares (checked by the CPU tests).
 EXPORTS = [
@@ -44,6 +46,7 @@ EXPORTS = [
     "ssd_chunk_scan_fwd_stage_launches",
     "ssd_chunk_scan_fwd_default_plan",
     "ssd_chunk_scan_fwd_ex",
+    "ssd_chunk_scan_fwd_noalloc",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -150,6 +153,8 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_scan_fwd_default_plan.restype = ctypes.c_int
         lib.ssd_chunk_scan_fwd_ex.argtypes = fwd_args + [pp, ctypes.POINTER(ctypes.c_void_p)]
         lib.ssd_chunk_scan_fwd_ex.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+        lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []

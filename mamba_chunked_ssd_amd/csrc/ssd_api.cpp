@@ -406,6 +406,7 @@ const char *ssd_status_string(ssd_status s) {
         case SSD_ERROR_MISALIGNED: return "misaligned pointer (16 B for x/B/C/y/states, 256 B for workspace)";
         case SSD_ERROR_WORKSPACE: return "workspace missing or smaller than ssd_chunk_scan_fwd_workspace_size()";
         case SSD_ERROR_LAUNCH: return "the HIP runtime refused a kernel launch or event record";
+        case SSD_ERROR_SCRATCH: return "problem needs more workspace than the no-allocation entry point's 128 MiB scratch";
     }
     return "unknown status";
 }

@@ -70,7 +70,7 @@ def test_stage_launches(lib):
 
 def test_status_strings(lib):
     assert lib.ssd_status_string(0) == b"ok"
-    for code in range(1, 6):
+    for code in range(1, 7):
         assert len(lib.ssd_status_string(code)) > 10
     assert lib.ssd_version() == 200
 
@@ -305,3 +305,26 @@ def test_invalid_plan_rejected_before_launch(lib):
                                    None, v(f()), v(f()), v(f()), ssd.workspace_size(s, 256), None,
                                    ctypes.byref(plan), None)
     assert st == 1
+
+
+@no_gpu
+def test_noalloc_checks_before_any_device_access(lib):
+    f = Fake()
+    v = lambda a: ctypes.c_void_p(a)  # noqa: E731
+    args = lambda: [v(f()), v(f()), v(f()), v(f()), v(f()), v(f())]  # noqa: E731
+    # workspace beyond the 128 MiB scratch: rejected (the throughput workload needs ~0.7 GB)
+    s = ssd.make_shape(8, 4096, 80, 64, 128, 1, "bf16")
+    assert ssd.workspace_size(s, 256) > ssd.NOALLOC_SCRATCH_BYTES
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(s), *args(), 256, None, v(f()), v(f()), None) == 6
+    # invalid and unsupported shapes report as the forward call does
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(shape(nheads=6, ngroups=4)), *args(), 256, None,
+                                          v(f()), v(f()), None) == 1
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(shape()), *args(), 96, None, v(f()), v(f()),
+                                          None) == 2
+    assert lib.ssd_chunk_scan_fwd_noalloc(None, *args(), 256, None, v(f()), v(f()), None) == 1
+    # the intermediates flag is refused (the scratch is not readable by the caller)
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(shape(keep=True)), *args(), 256, None, v(f()),
+                                          v(f()), None) == 1
+    # an empty batch touches no device
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(shape(batch=0)), *([None] * 6), 256, None, None,
+                                          None, None) == 0
