@@ -25,7 +25,7 @@
 // whose exponent is formed exactly in fp64 before the fp32 exp2.  Tokens past
 // seqlen are treated as dt = 0: G2 stays flat and DT, W are 0.
 #include "ssd_device.h"
-#include "ssd_internal.h"
+#include "ssd_launch.h"
 
 namespace ssd {
 namespace {

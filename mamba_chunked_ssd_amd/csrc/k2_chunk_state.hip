@@ -39,7 +39,7 @@
 #include <utility>
 
 #include "ssd_device.h"
-#include "ssd_internal.h"
+#include "ssd_launch.h"
 
 namespace ssd {
 namespace {

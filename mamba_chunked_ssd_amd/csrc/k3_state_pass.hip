@@ -29,7 +29,7 @@
 #include <climits>
 
 #include "ssd_device.h"
-#include "ssd_internal.h"
+#include "ssd_launch.h"
 
 namespace ssd {
 namespace {

@@ -53,7 +53,7 @@
 #include <utility>
 
 #include "ssd_device.h"
-#include "ssd_internal.h"
+#include "ssd_launch.h"
 
 namespace ssd {
 namespace k4 {

@@ -7,7 +7,7 @@
 // architecture", with the state stage split in two: the parallel per-chunk
 // contraction and the sequential carry).  Validation touches no HIP API, so
 // every error path runs without a device.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdint>

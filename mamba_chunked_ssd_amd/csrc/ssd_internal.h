@@ -1,9 +1,12 @@
 // ssd_internal.h -- interface between the C-ABI host code (ssd_api.cpp) and
-// the four kernel translation units.  Not installed; not part of the ABI.
+// the kernel translation units.  Not installed; not part of the ABI.  Host
+// declarations only (the HIP runtime API, no device code), so the host code
+// also builds with a plain C++ compiler (the sanitizer builds of the tests);
+// the launch helpers the kernel files share are in ssd_launch.h.
 #pragma once
 
-#include <hip/hip_ext.h>
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace ssd {
@@ -59,14 +62,6 @@ struct LaunchEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 
-// Launch on `stream`; when `ev` holds events they time this dispatch alone.
-template <typename... Args, typename F>
-inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                                const LaunchEvents &ev, Args... args) {
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, ev.start, ev.stop, 0u, args...);
-    return hipGetLastError();
-}
-
 // Stage 1: G2 (hi/lo), dt widened to fp32 -> DT and the chunk-state weights
 // W_t = exp2(G2_last - G2_t) DT_t, all head-major.
 hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
@@ -94,28 +89,5 @@ hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, c
                             const void *C, const float *CB, G2View G2, const float *DT,
                             const float *D, const float *H, void *y, hipStream_t stream,
                             const LaunchEvents &ev);
-
-// Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
-// CU).  The template parameter is the kernel itself.  The attribute is set on
-// the first call for that kernel through a function-local static, whose
-// initialisation C++ makes thread-safe (concurrent first calls wait for the
-// one that runs it); afterwards the result is only read, so there is no
-// mutable shared state.  A failure is kept and returned to every caller.
-template <auto Kernel>
-hipError_t allow_lds(size_t bytes) {
-    if (bytes <= 65536) return hipSuccess;
-    static const hipError_t status = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)kLdsPerCu);
-    return status;
-}
-
-// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).
-// Remap a hardware block index so that consecutive logical indices land on
-// the same XCD: logical = (hw % 8) * (n / 8) + hw / 8 when n % 8 == 0.
-__device__ __forceinline__ int xcd_remap(int hw, int n) {
-    if (n % 8 != 0) return hw;
-    return (hw % 8) * (n / 8) + hw / 8;
-}
 
 }  // namespace ssd

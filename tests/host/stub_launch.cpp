@@ -1,0 +1,44 @@
+// Stub stage launchers for the host-only sanitizer builds of ssd_api.cpp: each
+// records that it was called and enqueues nothing, so the C ABI's host logic
+// (validation, workspace layout, plans, stage order) runs under ASan, UBSan
+// and TSan on a machine without a GPU.  Not part of the library.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+
+#include "../../mamba_chunked_ssd_amd/csrc/ssd_internal.h"
+
+std::atomic<long> g_launches[4];  // calls per stage
+std::atomic<long> g_event_records;
+
+namespace ssd {
+
+hipError_t launch_chunk_cumsum(const Problem &, const void *, const float *, G2Pair, float *, float *,
+                               hipStream_t, const LaunchEvents &) {
+    g_launches[0]++;
+    return hipSuccess;
+}
+hipError_t launch_chunk_state(const Problem &, const Plan &, const void *, const void *, const float *,
+                              float *, hipStream_t, const LaunchEvents &) {
+    g_launches[1]++;
+    return hipSuccess;
+}
+int chunk_state_blocks_per_cu(const Problem &p) { return p.bf16 ? 1 : 2; }
+hipError_t launch_state_pass(const Problem &, const float *, float *, G2View, const float *, float *,
+                             const void *, const void *, float *, hipStream_t, const LaunchEvents &) {
+    g_launches[2]++;
+    return hipSuccess;
+}
+hipError_t launch_chunk_out(const Problem &, const Plan &, const void *, const void *, const void *,
+                            const float *, G2View, const float *, const float *, const float *, void *,
+                            hipStream_t, const LaunchEvents &) {
+    g_launches[3]++;
+    return hipSuccess;
+}
+
+}  // namespace ssd
+
+extern "C" hipError_t hipEventRecord(hipEvent_t, hipStream_t) {
+    g_event_records++;
+    return hipSuccess;
+}
