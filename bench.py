@@ -65,7 +65,7 @@ def measured_traffic(workload: str, y_dtype: str, stage: str):
 # algorithmic bytes and MFMA flops per stage (what the method must move or
 # compute; intermediates fp32; C B^T once per group; triangles with diagonal)
 # ---------------------------------------------------------------------------
-def stage_model(w, y_bytes: int) -> dict:
+def stage_model(w, y_bytes: int, fused: bool = False) -> dict:
     e = 2 if w.dtype == "bf16" else 4
     B, L, NH, P, N, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     NC = -(-L // T)
@@ -90,6 +90,13 @@ def stage_model(w, y_bytes: int) -> dict:
                       float(B * NC * G * T * (T + 1) * N + B * NC * NH * T * (T + 1) * P
                             + 2 * B * L * NH * N * P)),
     }
+    if fused:
+        # one launch for the chunk states and the carry: x, B and the token
+        # weights in, the chunk-start states (and the final state) out, s_c
+        # never stored (+ B, C in and the C B^T tiles out, as the state pass)
+        m["chunk_state"] = (tok_h * P * e + bc + tok_h * (e + 4) + states + init + final
+                            + (2 * bc + cb_tiles if cb_tiles else 0), 2.0 * B * L * NH * N * P)
+        m["state_pass"] = (0, 0.0)
     e2e_bytes = tok_h * P * (e + y_bytes) + tok_h * e + 2 * B * L * G * N * e + init + final
     m["e2e"] = (e2e_bytes, m["chunk_state"][1] + m["chunk_out"][1])
     return m
@@ -163,6 +170,10 @@ def main(argv=None):
                     help="repeat the oracle run until this much CPU time has passed")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps after a 1 GiB cache-flush write (reported separately)")
+    ap.add_argument("--plan", choices=["default", "split", "fused"], default="default",
+                    help="launch plan: the library's default, or the split / fused state path")
+    ap.add_argument("--fused-cols", type=int, default=0,
+                    help="dstate columns per fused-state block (0: 32 for headdim <= 64, else 64)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy (for scaling rocprofv3 FETCH/WRITE counters)")
     a = ap.parse_args(argv)
@@ -200,11 +211,16 @@ def main(argv=None):
     ws = torch.empty(ssd.workspace_size(shape, w.chunk_size), dtype=torch.uint8, device=dev)
     hip = Hip()
     stream = torch.cuda.current_stream(dev)
+    plan = ssd.default_plan(shape, w.chunk_size)
+    if a.plan != "default":
+        cols = a.fused_cols or (32 if w.headdim <= 64 else 64)
+        plan = ssd.make_plan(a.plan, plan.chunk_state_heads, plan.chunk_out_heads,
+                             cols if a.plan == "fused" else 0)
 
     def step(events=None):
         ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=w.chunk_size,
                            initial_states=t["h0"], y_dtype=ydt, out=y, final_out=fin, workspace=ws,
-                           stream=stream.cuda_stream, events=events)
+                           stream=stream.cuda_stream, events=events, plan=plan)
 
     if a.calibrate_copy:
         # a plain device copy of known size (1 GiB read + 1 GiB written) whose
@@ -245,11 +261,12 @@ def main(argv=None):
             hip.destroy(ev)
     stage_ms = per_stage.mean(axis=0)
 
-    model = stage_model(w, 4 if ydt == torch.float32 else (2 if w.dtype == "bf16" else 4))
+    model = stage_model(w, 4 if ydt == torch.float32 else (2 if w.dtype == "bf16" else 4),
+                        fused=plan.state_path == ssd.SSD_STATE_FUSED)
     peak_tf = PEAK_TFLOPS[w.dtype]
     # Stages that launch no kernel for this problem (the library says which)
     # are reported as such and add no floor; their event pairs time nothing.
-    launched = ssd.stage_launches(shape, w.chunk_size)
+    launched = ssd.stage_launches(shape, w.chunk_size, plan)
     skipped = {name for name in STAGES if name not in launched}
     stages = {}
     for j, name in enumerate(STAGES):
@@ -299,7 +316,8 @@ def main(argv=None):
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk_size": w.chunk_size, "accumulate": "f32",
                    "y_dtype": "f32" if ydt == torch.float32 else w.dtype,
-                   "initial_states": w.init_std > 0, "parallelism": "single_gpu"},
+                   "initial_states": w.init_std > 0, "parallelism": "single_gpu",
+                   "plan": plan.as_dict()},
         "roofline": roof,
         "stages": stages,
         "e2e_roofline_frac": round(e2e_floor / e2e_t, 4),

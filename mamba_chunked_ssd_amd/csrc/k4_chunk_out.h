@@ -143,16 +143,36 @@ __device__ __forceinline__ void tile_values(const floatx4 &s, int J, int I, int 
 
 // y is written with raw buffer stores: the resource covers a chunk's rows of
 // one head up to the last valid row, so the hardware drops the stores of rows
-// past the sequence end, and the row offsets stay 32-bit.
+// past the sequence end, and the row offsets stay 32-bit.  A buffer store
+// reads its data register after it issues (later still when copies are
+// queued ahead of it), and the compiler does not wait for that before it
+// reuses the register (measured: such reuse corrupted stored values).  So
+// values go out four at a time, at off + r * stride, followed by an expcnt
+// wait that takes the four data registers as operands: they stay untouched
+// until the stores have read them (not until the stores complete).
 template <typename OutT>
-__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off, float v);
+__device__ __forceinline__ void store_out4(__amdgpu_buffer_rsrc_t r, int off, int stride, const float (&v)[4]);
 template <>
-__device__ __forceinline__ void store_out<float>(__amdgpu_buffer_rsrc_t r, int off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+__device__ __forceinline__ void store_out4<float>(__amdgpu_buffer_rsrc_t r, int off, int stride,
+                                                  const float (&v)[4]) {
+    uint32_t d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        d[k] = __float_as_uint(v[k]);
+        __builtin_amdgcn_raw_buffer_store_b32(d[k], r, off + k * stride, 0, 0);
+    }
+    asm volatile("s_waitcnt expcnt(0)" ::"v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]) : "memory");
 }
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(__amdgpu_buffer_rsrc_t r, int off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(v, 0.f) & 0xffffu), r, off, 0, 0);
+__device__ __forceinline__ void store_out4<uint16_t>(__amdgpu_buffer_rsrc_t r, int off, int stride,
+                                                     const float (&v)[4]) {
+    uint32_t d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        d[k] = pack_bf16(v[k], 0.f) & 0xffffu;
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)d[k], r, off + k * stride, 0, 0);
+    }
+    asm volatile("s_waitcnt expcnt(0)" ::"v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]) : "memory");
 }
 
 __device__ __forceinline__ uint32_t sel_half(int q) { return (q & 1) ? 0x07060302u : 0x05040100u; }
@@ -496,10 +516,9 @@ __device__ __forceinline__ void head_wave(const floatx4 (&S)[T / 16 + 2],
         for (int pt = 0; pt < PT; ++pt) {
             const u32x2 xv2 = *reinterpret_cast<const u32x2 *>(cx.xl + pt * 16 * XRS + 32 * (I & ~1) + 8 * (I & 1));
             const float xv[4] = {bf16lo(xv2[0]), bf16hi(xv2[0]), bf16lo(xv2[1]), bf16hi(xv2[1])};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                store_out<OutT>(cx.yr, lane_off + (16 * I + r) * cx.NHP * ES + 16 * pt * ES,
-                                acc[ii][pt][r] + cx.Dh * xv[r]);
+            const float yv[4] = {acc[ii][pt][0] + cx.Dh * xv[0], acc[ii][pt][1] + cx.Dh * xv[1],
+                                 acc[ii][pt][2] + cx.Dh * xv[2], acc[ii][pt][3] + cx.Dh * xv[3]};
+            store_out4<OutT>(cx.yr, lane_off + 16 * I * cx.NHP * ES + 16 * pt * ES, cx.NHP * ES, yv);
         }
     }
 }
@@ -1034,12 +1053,11 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int p = 16 * pt + id.l16;
+                const int i0 = 16 * I + 4 * id.g4;
+                float yv[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * id.g4 + r;
-                    store_out<OutT>(yr, (i * NH * P + p) * (int)sizeof(OutT),
-                                    acc[ii][pt][r] + Dh * xs[i * LDP + p]);
-                }
+                for (int r = 0; r < 4; ++r) yv[r] = acc[ii][pt][r] + Dh * xs[(i0 + r) * LDP + p];
+                store_out4<OutT>(yr, (i0 * NH * P + p) * (int)sizeof(OutT), NH * P * (int)sizeof(OutT), yv);
             }
         }
         __syncthreads();
@@ -1091,8 +1109,8 @@ __device__ __forceinline__ void store_quad(const floatx4 &v, __amdgpu_buffer_rsr
     constexpr int ES = (int)sizeof(OutT);
     int lane_off = ((4 * g4) * NHP + l16) * ES;
     asm volatile("" : "+v"(lane_off));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) store_out<OutT>(yr, lane_off + (16 * I + r) * NHP * ES + 16 * pt * ES, v[r]);
+    const float yv[4] = {v[0], v[1], v[2], v[3]};
+    store_out4<OutT>(yr, lane_off + 16 * I * NHP * ES + 16 * pt * ES, NHP * ES, yv);
 }
 
 // acc holds this head's tile on return.  For the first-half waves it holds
@@ -1305,10 +1323,10 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[2][acfg::PT], __
     for (int ii = 0; ii < 2; ++ii) {
         const int I = ii ? I1 : I0;
 #pragma unroll
-        for (int pt = 0; pt < acfg::PT; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                store_out<OutT>(yr, lane_off + (16 * I + r) * NHP * ES + 16 * pt * ES, acc[ii][pt][r]);
+        for (int pt = 0; pt < acfg::PT; ++pt) {
+            const float yv[4] = {acc[ii][pt][0], acc[ii][pt][1], acc[ii][pt][2], acc[ii][pt][3]};
+            store_out4<OutT>(yr, lane_off + 16 * I * NHP * ES + 16 * pt * ES, NHP * ES, yv);
+        }
     }
 }
 

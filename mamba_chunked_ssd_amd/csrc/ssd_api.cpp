@@ -75,8 +75,10 @@ ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
         return SSD_ERROR_UNSUPPORTED;
     if (q.nheads > kMaxI32 || q.nchunks > kMaxI32 || q.ngroups > kMaxI32 || q.batch > 65535)
         return SSD_ERROR_UNSUPPORTED;
-    // The chunk output stage addresses one chunk's y rows with 32-bit byte offsets.
+    // The chunk output stage addresses one chunk's y rows, and the state
+    // stages one chunk's B rows, with 32-bit byte offsets.
     if (q.chunk * q.nheads * q.headdim * 4 > kMaxI32) return SSD_ERROR_UNSUPPORTED;
+    if (q.chunk * q.ngroups * q.dstate * 4 > kMaxI32) return SSD_ERROR_UNSUPPORTED;
     // Launch geometry limits (work-items per grid dimension < 2^32).
     const int64_t tiles = q.batch * q.nchunks * q.ngroups * q.heads_per_group;  // upper bound on blocks
     if (tiles > ((int64_t)1 << 31) / 512) return SSD_ERROR_UNSUPPORTED;
@@ -161,22 +163,30 @@ const int kNumCUs = 256;
 
 Plan make_plan(const Problem &p) {
     Plan plan;
-    plan.fused_state = false;
     plan.k2_heads_per_block = pick_heads_per_block(p, chunk_state_blocks_per_cu(p) * kNumCUs, 1.0);
     plan.k4_heads_per_block = pick_heads_per_block(p, kNumCUs, 1.0);
-    plan.fused_cols = (int)p.dstate;
+    // The fused state launch (bf16) walks the chunks of one (batch, head,
+    // 64 dstate columns) per block in order: it saves the s_c round trip
+    // through memory but keeps only that many blocks busy.  Measured on
+    // MI355X it wins once those blocks fill the CUs (2.7B-shaped layer: 320
+    // blocks, 36.6 us against 37.6 us for the two split launches; 8 x 4096
+    // tokens: 281 us against 340 us) and loses below (65 536 tokens, 32
+    // heads, dstate 256: 128 blocks, 666 us against 426 us).
+    plan.fused_cols = 64;
+    plan.fused_state = p.nchunks > 0 && state_fused_supported(p, 64) &&
+                       p.batch * p.nheads * (p.dstate / 64) >= kNumCUs;
+    if (!plan.fused_state) plan.fused_cols = (int)std::min<int64_t>(p.dstate, 64);
     return plan;
 }
 
 namespace {
 
-// The fused state path has no kernel yet; its blocks cover a multiple of 32
-// dstate columns (or all of them).
-bool fused_supported(const Problem &) { return false; }
+// The fused state path: bf16 inputs, blocks of 32 or 64 dstate columns that
+// divide dstate, at least half the headdim (state_fused_supported).
 bool fused_cols_ok(const Problem &p, int64_t cols) {
-    if (cols == p.dstate) return true;
-    return cols >= 32 && cols % 32 == 0 && p.dstate % cols == 0;
+    return cols >= 32 && cols % 32 == 0 && cols <= p.dstate && p.dstate % cols == 0;
 }
+bool fused_supported(const Problem &p, int cols) { return state_fused_supported(p, cols); }
 
 ssd_plan to_abi(const Plan &q) {
     ssd_plan r;
@@ -204,7 +214,7 @@ ssd_status plan_from_abi(const Problem &p, const ssd_plan *in, Plan *out) {
         return SSD_ERROR_INVALID_VALUE;
     const bool fused = in->state_path == SSD_STATE_FUSED;
     if (fused && !fused_cols_ok(p, in->fused_cols)) return SSD_ERROR_INVALID_VALUE;
-    if (fused && !fused_supported(p)) return SSD_ERROR_UNSUPPORTED;
+    if (fused && !fused_supported(p, in->fused_cols)) return SSD_ERROR_UNSUPPORTED;
     Plan q;
     q.fused_state = fused;
     q.k2_heads_per_block = in->chunk_state_heads;
@@ -330,16 +340,27 @@ static ssd_status forward(const ssd_shape *shape, const void *x, const void *dt,
         return hipEventRecord(ev.start, stream) == hipSuccess &&
                hipEventRecord(ev.stop, stream) == hipSuccess;
     };
-    if (p.nchunks > 0) {
+    if (p.nchunks > 0 && plan.fused_state) {
+        // stage 1 is the fused launch (chunk states and carry); stage 2 has no kernel
         if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
-        if (launch_chunk_state(p, plan, x, B, Wf, S, stream, events_of(1)) != hipSuccess)
+        if (launch_state_fused(p, plan, x, B, Wf, G2v, init, Hs, final_states, C, CB, stream,
+                               events_of(1)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
-    } else if (!skip(0) || !skip(1)) {
-        return SSD_ERROR_LAUNCH;
+        if (!skip(2)) return SSD_ERROR_LAUNCH;
+    } else {
+        if (p.nchunks > 0) {
+            if (launch_chunk_cumsum(p, dt, A, G2, DTf, Wf, stream, events_of(0)) != hipSuccess)
+                return SSD_ERROR_LAUNCH;
+            if (launch_chunk_state(p, plan, x, B, Wf, S, stream, events_of(1)) != hipSuccess)
+                return SSD_ERROR_LAUNCH;
+        } else if (!skip(0) || !skip(1)) {
+            return SSD_ERROR_LAUNCH;
+        }
+        if (launch_state_pass(p, S, Hs, G2v, init, final_states, B, C, CB, stream, events_of(2)) !=
+            hipSuccess)
+            return SSD_ERROR_LAUNCH;
     }
-    if (launch_state_pass(p, S, Hs, G2v, init, final_states, B, C, CB, stream, events_of(2)) != hipSuccess)
-        return SSD_ERROR_LAUNCH;
     if (p.nchunks > 0) {
         if (launch_chunk_out(p, plan, x, B, C, CB, G2v, DTf, D, Hs, y, stream, events_of(3)) != hipSuccess)
             return SSD_ERROR_LAUNCH;

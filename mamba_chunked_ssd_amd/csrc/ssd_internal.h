@@ -82,6 +82,16 @@ hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View 
                              const float *init, float *final_states, const void *B,
                              const void *C, float *CB, hipStream_t stream, const LaunchEvents &ev);
 
+// Stages 2 and 3 in one launch (bf16 inputs): per (batch, head, block of
+// plan.fused_cols dstate columns) the chunks in order, h_c stored as the hi/lo
+// bf16 planes of H, final = h_nchunks; no s_c.  When uses_cb_tiles(p), extra
+// blocks of the launch also write the C B^T tiles.  Needs nchunks > 0.
+bool state_fused_supported(const Problem &p, int cols);
+hipError_t launch_state_fused(const Problem &p, const Plan &plan, const void *x, const void *B,
+                              const float *W, G2View G2, const float *init, float *H,
+                              float *final_states, const void *C, float *CB, hipStream_t stream,
+                              const LaunchEvents &ev);
+
 // Stage 4: chunk output
 // y_i = exp2(G2_i) C_i h_c + sum_{j<=i} exp2(G2_i - G2_j) (C_i . B_j) DT_j x_j + D x_i.
 // CB: the C B^T tiles of stage 1 when uses_cb_tiles(p), else unused.

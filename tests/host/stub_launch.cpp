@@ -29,6 +29,15 @@ hipError_t launch_state_pass(const Problem &, const float *, float *, G2View, co
     g_launches[2]++;
     return hipSuccess;
 }
+bool state_fused_supported(const Problem &p, int cols) {
+    return p.bf16 && (cols == 32 || cols == 64) && p.dstate % cols == 0;
+}
+hipError_t launch_state_fused(const Problem &, const Plan &, const void *, const void *, const float *,
+                              G2View, const float *, float *, float *, const void *, float *, hipStream_t,
+                              const LaunchEvents &) {
+    g_launches[1]++;
+    return hipSuccess;
+}
 hipError_t launch_chunk_out(const Problem &, const Plan &, const void *, const void *, const void *,
                             const float *, G2View, const float *, const float *, const float *, void *,
                             hipStream_t, const LaunchEvents &) {

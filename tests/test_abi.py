@@ -51,16 +51,24 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_stage_launches(lib):
-    # every stage launches its own kernel when there are tokens
+    # every stage launches its own kernel when there are tokens (split state
+    # path); under the fused state path the chunk-state launch also carries
+    # the state, and the state-passing stage launches nothing
     s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
-    assert ssd.stage_launches(s, 256) == ssd.STAGES
+    assert ssd.default_plan(s, 256).state_path == ssd.SSD_STATE_FUSED
+    assert ssd.stage_launches(s, 256) == ("chunk_cumsum", "chunk_state", "chunk_out")
+    assert ssd.stage_launches(s, 256, ssd.make_plan("split", 5, 5)) == ssd.STAGES
+    assert ssd.stage_launches(s, 256, ssd.make_plan("fused", 5, 5, 32)) == (
+        "chunk_cumsum", "chunk_state", "chunk_out")
     s = ssd.make_shape(4, 16384, 64, 128, 256, 8, "f32")
     assert ssd.stage_launches(s, 128) == ssd.STAGES
     s = ssd.make_shape(1, 65536, 32, 64, 256, 1, "bf16")
     assert ssd.stage_launches(s, 256) == ssd.STAGES
-    # no tokens: only the state pass (initial state to final state) runs
+    # no tokens: only the state pass (initial state to final state) runs,
+    # whichever the state path
     s = ssd.make_shape(2, 0, 4, 64, 128, 1, "bf16")
     assert ssd.stage_launches(s, 256) == ("state_pass",)
+    assert ssd.stage_launches(s, 256, ssd.make_plan("fused", 1, 1, 64)) == ("state_pass",)
     s = ssd.make_shape(0, 100, 4, 64, 128, 1, "bf16")
     assert ssd.stage_launches(s, 256) == ()
     m = ctypes.c_uint32()
@@ -274,6 +282,7 @@ def test_default_plan_errors(lib):
 @pytest.mark.parametrize("bad", [
     dict(chunk_state_heads=0), dict(chunk_out_heads=0), dict(chunk_state_heads=81),
     dict(chunk_out_heads=81), dict(state_path=2), dict(state_path=-1),
+    dict(state_path=1, fused_cols=48), dict(state_path=1, fused_cols=256), dict(state_path=1, fused_cols=0),
 ])
 def test_invalid_plans_rejected(lib, bad):
     s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
@@ -328,3 +337,11 @@ def test_noalloc_checks_before_any_device_access(lib):
     # an empty batch touches no device
     assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(shape(batch=0)), *([None] * 6), 256, None, None,
                                           None, None) == 0
+
+
+def test_fused_path_unsupported_for_fp32(lib):
+    s = ssd.make_shape(4, 16384, 64, 128, 256, 8, "f32")
+    m = ctypes.c_uint32()
+    plan = ssd.make_plan("fused", 1, 1, 64)
+    assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 128, ctypes.byref(plan),
+                                                 ctypes.byref(m)) == 2

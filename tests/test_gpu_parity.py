@@ -404,3 +404,83 @@ def test_invalid_arguments_raise_before_launch():
         ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=64,
                            workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert ei.value.status == 4
+
+
+# ---------------------------------------------------------------------------
+# the fused state path (chunk states and carry in one launch, bf16 inputs)
+# ---------------------------------------------------------------------------
+
+def _fused_plan(shp, cols, k4h=1):
+    b, L, nh, p, n, g, T = shp
+    return ssd.make_plan("fused", 1, k4h, cols)
+
+
+def _fused_ok(shp, cols):
+    b, L, nh, p, n, g, T = shp
+    return n % cols == 0
+
+
+FUSED_CASES = [(shp, cols) for shp in STAGE_SHAPES for cols in (32, 64) if _fused_ok(shp, cols)] + [
+    ((2, 1000, 10, 64, 128, 2, 256), 32),   # several heads per group, two batches
+    ((1, 19200, 2, 32, 32, 1, 64), 32),     # 300 chunks: chunk decays reloaded past 256
+    ((1, 4096, 3, 128, 256, 1, 256), 64),   # 16 chunks of the long-sequence state size
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES,
+                         ids=lambda c: "b%d_L%d_h%d_p%d_n%d_g%d_T%d" % c[0] + "_cols%d" % c[1])
+def test_stage_parity_fused(case):
+    shp, cols = case
+    print("case fused", shp, cols, flush=True)
+    out = check_stages(_stage_inputs("bf16", shp), "bf16", shp[-1], plan=_fused_plan(shp, cols))
+    assert out["plan"].state_path == ssd.SSD_STATE_FUSED and "S" not in out
+
+
+@pytest.mark.parametrize("a_max", [0.0, 1e-3])
+def test_fused_slow_decay_long_carry(a_max):
+    w, inp = _inputs("bf16", seqlen=2048, chunk_size=64, nheads=4, ngroups=1)
+    inp["A"] = (-np.linspace(0.0, a_max, 4)).astype(np.float32)
+    out = run(inp, "bf16", 64, plan=ssd.make_plan("fused", 1, 1, 32))
+    y_ref, fin_ref, _ = _oracle_all(inp, 64)
+    assert nerr(out["y"], y_ref) < TOL["bf16"]
+    assert nerr(out["final"], fin_ref) < TOL["bf16"]
+
+
+def test_fused_without_final_state_and_initial_state():
+    w, inp = _inputs("bf16", init_std=0.0, seqlen=700, chunk_size=128)
+    plan = ssd.make_plan("fused", 1, 1, 32)
+    out = run(inp, "bf16", 128, final=False, plan=plan)
+    y_ref, _, _ = _oracle_all(inp, 128)
+    assert out["final"] is None and nerr(out["y"], y_ref) < TOL["bf16"]
+
+
+def test_fused_and_split_agree_and_are_deterministic():
+    w, inp = _inputs("bf16", seqlen=1000, nheads=8, ngroups=2, chunk_size=256)
+    f1 = run(inp, "bf16", 256, plan=ssd.make_plan("fused", 1, 2, 32))
+    f2 = run(inp, "bf16", 256, plan=ssd.make_plan("fused", 1, 2, 32))
+    sp = run(inp, "bf16", 256, plan=ssd.make_plan("split", 2, 2, 0))
+    assert np.array_equal(f1["y"], f2["y"]) and np.array_equal(f1["final"], f2["final"])
+    assert nerr(f1["y"], sp["y"]) < 1e-3 and nerr(f1["final"], sp["final"]) < 1e-3
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_workload_full_size_whole_tensor_fused(k):
+    """The bf16 workloads under the fused state path at full size, every
+    element of y and of the final state against the oracle."""
+    w = si.WORKLOADS[k]
+    shape = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype)
+    dp = ssd.default_plan(shape, w.chunk_size)
+    plan = ssd.make_plan("fused", dp.chunk_state_heads, dp.chunk_out_heads, 32 if w.headdim <= 64 else 64)
+    print("workload", w.name, plan, flush=True)
+    inp = si.generate(w)
+    t = to_device(inp, w.dtype)
+    y, fin = ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=w.chunk_size,
+                                initial_states=t["h0"], return_final_states=True, plan=plan)
+    torch.cuda.synchronize()
+    y, fin = y.cpu().numpy(), fin.cpu().numpy()
+    del t
+    torch.cuda.empty_cache()
+    yr, fr, _ = oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    ey, ef = nerr(y, yr), nerr(fin, fr)
+    print("  whole tensor: y err %.3e final err %.3e" % (ey, ef), flush=True)
+    assert ey < TOL[w.dtype] and ef < TOL[w.dtype]
