@@ -156,6 +156,46 @@ def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
     }
 
 
+def decode_bench(hip, w, batch, dev, steps=20, warmup=5) -> dict:
+    """The recurrent decode step (one token per sequence, fp32 state updated in
+    place) at the layer shape of workload ``w`` with ``batch`` sequences:
+    kernel time from the dispatch's own events, and its HBM roofline (the
+    state read and written once, plus x, dt, B, C in and y out)."""
+    import numpy as np
+    import torch
+
+    import mamba_chunked_ssd_amd as ssd
+    import ssd_inputs as si
+
+    dw = si.small(dtype=w.dtype, batch=batch, seqlen=1, nheads=w.nheads, headdim=w.headdim, dstate=w.dstate,
+                  ngroups=w.ngroups, chunk_size=64, dt_mu=w.dt_mu, init_std=0.1, seed=w.seed + 100)
+    inp = si.generate(dw)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k][:, 0] if k in ("x", "dt", "B", "C") else inp[k],
+                                                  np.float32)).to(dev) for k in ("x", "dt", "A", "B", "C", "D")}
+    for k in ("x", "dt", "B", "C"):
+        t[k] = t[k].to(tdt)
+    state = torch.from_numpy(inp["h0"]).to(dev)
+    y = torch.empty((batch, w.nheads, w.headdim), dtype=torch.float32, device=dev)
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    for i in range(warmup + steps):
+        ssd.decode_step(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], state, out=y,
+                        events=evs[i - warmup] if i >= warmup else None)
+    torch.cuda.synchronize()
+    us = float(np.median([hip.elapsed_ms(a, b) for a, b in evs])) * 1e3
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    e = 2 if w.dtype == "bf16" else 4
+    bh = batch * w.nheads
+    byts = 2 * 4 * bh * w.headdim * w.dstate + bh * w.headdim * (e + 4) + bh * e + 2 * batch * w.ngroups * w.dstate * e
+    gbs = byts / (us * 1e-6) / 1e9
+    return {"workload": "decode_step_%s_batch%d" % (w.name, batch), "batch": batch, "us": round(us, 3),
+            "tokens_per_s": round(batch / (us * 1e-6), 1), "GB_s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts}}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +214,8 @@ def main(argv=None):
                     help="launch plan: the library's default, or the split / fused state path")
     ap.add_argument("--fused-cols", type=int, default=0,
                     help="dstate columns per fused-state block (0: 32 for headdim <= 64, else 64)")
+    ap.add_argument("--decode-batch", type=int, default=128,
+                    help="batch of the recurrent decode-step measurement (0: skip it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy (for scaling rocprofv3 FETCH/WRITE counters)")
     a = ap.parse_args(argv)
@@ -339,6 +381,9 @@ def main(argv=None):
         out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES) if n not in skipped}
         out["cold_tokens_per_s"] = round(
             w.tokens / (sum(cold[j] for j, n in enumerate(STAGES) if n not in skipped) * 1e-3), 1)
+
+    if a.decode_batch > 0:
+        out["decode"] = decode_bench(hip, w, a.decode_batch, dev)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps, a.cpu_seconds)

@@ -223,6 +223,35 @@ ssd_status ssd_chunk_scan_fwd_ex(const ssd_shape *shape,
 ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chunk_size,
                                              const ssd_plan *plan, uint32_t *mask);
 
+/* One step of the recurrence for one new token per sequence, with the state
+ * kept by the caller between calls ("Accelerating Mamba-2 with
+ * High-Performance Forward Pass Kernels in NVIDIA CUDA Tile", section
+ * "Mamba-2 architecture": the recurrent form, suited to sequential
+ * inference).  For every batch b and head h, with g = h / (nheads / ngroups):
+ *     state[b,h] <- exp(A[h] dt[b,h]) state[b,h] + dt[b,h] x[b,h] B[b,g]^T
+ *     y[b,h]      = state[b,h] C[b,g] + D[h] x[b,h]        (readout after the update)
+ * with the state in the (headdim, dstate) orientation of initial_states.
+ *   shape            seqlen must be 1; flags must be 0; other fields as for
+ *                    ssd_chunk_scan_fwd (headdim 32/64/128, dstate a multiple
+ *                    of 16 up to 256, dtype of x/dt/B/C, y_dtype of y)
+ *   x                (batch, nheads, headdim)  dtype
+ *   dt               (batch, nheads)           dtype, >= 0
+ *   A, D             (nheads) fp32; D NULL => no skip term
+ *   B, C             (batch, ngroups, dstate)  dtype, 16-byte aligned
+ *   state            (batch, nheads, headdim, dstate) fp32, 16-byte aligned,
+ *                    read and updated in place
+ *   y                (batch, nheads, headdim)  y_dtype, out
+ *   stream           hipStream_t or NULL
+ *   events           NULL, or 2 valid hipEvent_t recorded by the kernel's own
+ *                    dispatch (start, stop)
+ * These are the layouts of ssd_chunk_scan_fwd with seqlen 1.  y must not
+ * overlap any input or the state, and the state must not overlap an input.
+ * All checks happen before the launch; on error nothing is enqueued and
+ * state and y are untouched. */
+ssd_status ssd_decode_step(const ssd_shape *shape, const void *x, const void *dt, const float *A,
+                           const void *B, const void *C, const float *D, float *state, void *y,
+                           void *stream, void *const *events);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
  * pass of ssd_chunk_scan_fwd (default plan) with no workspace argument.  The

@@ -47,6 +47,7 @@ EXPORTS = [
     "ssd_chunk_scan_fwd_default_plan",
     "ssd_chunk_scan_fwd_ex",
     "ssd_chunk_scan_fwd_noalloc",
+    "ssd_decode_step",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -155,6 +156,8 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_scan_fwd_ex.restype = ctypes.c_int
         lib.ssd_chunk_scan_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
         lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
+        lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_void_p)]
+        lib.ssd_decode_step.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []
@@ -327,4 +330,53 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
         raise SSDError(st, where)
     if return_final_states:
         return y, fin
+    return y
+
+
+def decode_step(x, dt, A, B, C, D, state, *, y_dtype=None, out=None, stream=None, events=None):
+    """One recurrent step for one new token per sequence (``ssd_decode_step``).
+
+    x (b, nh, p) and dt (b, nh), B/C (b, g, n): float32 or bfloat16, all the
+    same dtype; A (nh,), D (nh,) or None: float32; ``state`` (b, nh, p, n)
+    float32 is updated in place.  Returns y (b, nh, p) (``y_dtype``: float32,
+    the default, or the input dtype).  ``events``: 2 raw hipEvent_t handles
+    (start, stop) recorded by the kernel's own dispatch.
+    """
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be (batch, nheads, headdim) and B (batch, ngroups, dstate)")
+    b, nh, p = x.shape
+    g, n = B.shape[1], B.shape[2]
+    if x.dtype == torch.bfloat16:
+        dname = "bf16"
+    elif x.dtype == torch.float32:
+        dname = "f32"
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    _check(x, "x", x.dtype, (b, nh, p), dev)
+    _check(dt, "dt", x.dtype, (b, nh), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    _check(B, "B", x.dtype, (b, g, n), dev)
+    _check(C, "C", x.dtype, (b, g, n), dev)
+    if D is not None:
+        _check(D, "D", torch.float32, (nh,), dev)
+    _check(state, "state", torch.float32, (b, nh, p, n), dev)
+    ytype = torch.float32 if y_dtype is None else y_dtype
+    if ytype not in (torch.float32, x.dtype):
+        raise TypeError("y_dtype must be float32 or the input dtype")
+    y = out if out is not None else torch.empty((b, nh, p), dtype=ytype, device=dev)
+    _check(y, "out", ytype, (b, nh, p), dev)
+    shape = make_shape(b, 1, nh, p, n, g, dname, False, "bf16" if ytype == torch.bfloat16 else "f32")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    ev = None
+    if events is not None:
+        if len(events) != 2:
+            raise ValueError("events: one (start, stop) pair")
+        ev = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e) for e in events])
+    st = lib.ssd_decode_step(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             _ptr(state), _ptr(y), ctypes.c_void_p(s), ev)
+    if st != 0:
+        raise SSDError(st, "ssd_decode_step")
     return y

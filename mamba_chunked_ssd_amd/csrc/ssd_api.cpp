@@ -419,6 +419,43 @@ ssd_status ssd_chunk_scan_fwd_stage_launches(const ssd_shape *shape, int64_t chu
     return SSD_OK;
 }
 
+ssd_status ssd_decode_step(const ssd_shape *shape, const void *x, const void *dt, const float *A,
+                           const void *B, const void *C, const float *D, float *state, void *y,
+                           void *stream_handle, void *const *events) {
+    Problem p;
+    // the chunk size plays no part in a single step; any supported one validates the rest
+    const ssd_status st = check_shape(shape, 64, &p);
+    if (st != SSD_OK) return st;
+    if (p.seqlen != 1 || shape->flags != 0) return SSD_ERROR_INVALID_VALUE;
+    if (events != nullptr && (events[0] == nullptr || events[1] == nullptr)) return SSD_ERROR_INVALID_VALUE;
+    if (p.batch == 0) return SSD_OK;
+    if (x == nullptr || dt == nullptr || A == nullptr || B == nullptr || C == nullptr ||
+        state == nullptr || y == nullptr)
+        return SSD_ERROR_INVALID_VALUE;
+    const size_t esz = p.bf16 ? 2 : 4, ysz = p.y_bf16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(dt, esz) || !aligned(A, 4) || !aligned(D, 4) || !aligned(B, 16) ||
+        !aligned(C, 16) || !aligned(state, 16) || !aligned(y, ysz))
+        return SSD_ERROR_MISALIGNED;
+    const size_t bh = (size_t)p.batch * p.nheads;
+    const Range rx = range_of(x, bh * p.headdim * esz), rdt = range_of(dt, bh * esz),
+                rA = range_of(A, p.nheads * 4), rD = range_of(D, D ? p.nheads * 4 : 0),
+                rB = range_of(B, (size_t)p.batch * p.ngroups * p.dstate * esz),
+                rC = range_of(C, (size_t)p.batch * p.ngroups * p.dstate * esz),
+                rs = range_of(state, bh * p.headdim * p.dstate * 4), ry = range_of(y, bh * p.headdim * ysz);
+    for (const Range &r : {rx, rdt, rA, rD, rB, rC})
+        if (overlap(r, rs) || overlap(r, ry)) return SSD_ERROR_INVALID_VALUE;
+    if (overlap(rs, ry)) return SSD_ERROR_INVALID_VALUE;
+    LaunchEvents ev;
+    if (events != nullptr) {
+        ev.start = static_cast<hipEvent_t>(events[0]);
+        ev.stop = static_cast<hipEvent_t>(events[1]);
+    }
+    if (launch_decode_step(p, x, dt, A, B, C, D, state, y, static_cast<hipStream_t>(stream_handle), ev) !=
+        hipSuccess)
+        return SSD_ERROR_LAUNCH;
+    return SSD_OK;
+}
+
 const char *ssd_status_string(ssd_status s) {
     switch (s) {
         case SSD_OK: return "ok";

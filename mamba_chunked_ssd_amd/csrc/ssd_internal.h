@@ -92,6 +92,12 @@ hipError_t launch_state_fused(const Problem &p, const Plan &plan, const void *x,
                               float *final_states, const void *C, float *CB, hipStream_t stream,
                               const LaunchEvents &ev);
 
+// Recurrent decode step (seqlen 1): state <- exp(A dt) state + dt x B^T in
+// place, y = state C + D x.  Layouts as the forward pass with seqlen 1.
+hipError_t launch_decode_step(const Problem &p, const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, float *state, void *y, hipStream_t stream,
+                              const LaunchEvents &ev);
+
 // Stage 4: chunk output
 // y_i = exp2(G2_i) C_i h_c + sum_{j<=i} exp2(G2_i - G2_j) (C_i . B_j) DT_j x_j + D x_i.
 // CB: the C B^T tiles of stage 1 when uses_cb_tiles(p), else unused.

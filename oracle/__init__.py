@@ -24,6 +24,9 @@ Pass Kernels in NVIDIA CUDA Tile":
   quantity the fwd_pass_state section stores per chunk.
 * :func:`chunk_cb` -- the C B^T factor of the chunk output equation (section
   "Mamba-2 architecture"): every product C_i . B_j of two tokens of a chunk.
+* :func:`decode_step` -- one step of the recurrence for one new token per
+  sequence from a given state (the recurrent form the same section names for
+  sequential inference): :func:`scan` over a sequence of length 1.
 
 Inputs may be float32 or float64 numpy arrays; they are widened exactly to
 fp64.  bf16 data is passed as float32 arrays holding bf16-representable values
@@ -211,3 +214,16 @@ def chunk_cb(B, C, chunk_size: int):
     for gi in range(g):
         out[:, :, gi] = np.matmul(Cs[:, :, :, gi, :], Bs[:, :, :, gi, :].transpose(0, 1, 3, 2))
     return out
+
+
+def decode_step(x, dt, A, B, C, D, state):
+    """One step of the recurrence from ``state``, for one token per sequence.
+
+    Shapes: x (b, nh, p), dt (b, nh), B/C (b, g, n), A (nh,), D (nh,) or None,
+    state (b, nh, p, n).  Returns ``(y, new_state)``: y (b, nh, p) fp64 with
+    the readout after the update, new_state (b, nh, p, n) fp64.  This is
+    :func:`scan` with seqlen 1 and initial state ``state``.
+    """
+    x, dt, B, C = (_f64(v) for v in (x, dt, B, C))
+    y, hT, _ = scan(x[:, None], dt[:, None], A, B[:, None], C[:, None], D, state)
+    return y[:, 0], hT

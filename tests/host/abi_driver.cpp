@@ -11,7 +11,7 @@
 
 #include "../../include/ssd.h"
 
-extern std::atomic<long> g_launches[4];
+extern std::atomic<long> g_launches[5];
 extern std::atomic<long> g_event_records;
 
 static int g_fail = 0;
@@ -59,7 +59,9 @@ static ssd_status fwd(const ssd_shape &s, int64_t T, const Args &a, const ssd_pl
                                  plan, events);
 }
 
-static long launches() { return g_launches[0] + g_launches[1] + g_launches[2] + g_launches[3]; }
+static long launches() {
+    return g_launches[0] + g_launches[1] + g_launches[2] + g_launches[3] + g_launches[4];
+}
 
 static void validation_paths() {
     Fake f;
@@ -162,6 +164,31 @@ static void validation_paths() {
         Args a = args_for(big, 256, f);
         CHECK(ssd_chunk_scan_fwd_workspace_size(&big, 256) > (size_t)SSD_NOALLOC_SCRATCH_BYTES);
     }
+    // decode step: seqlen must be 1, pointers present, aligned, not aliased
+    {
+        const ssd_shape d1 = shape(4, 1, 8, 64, 128, 2, SSD_DTYPE_BF16);
+        void *x = f(), *dt = f(), *A = f(), *B = f(), *C = f(), *D = f(), *st = f(), *y = f();
+        auto dec = [&](const ssd_shape &s) {
+            return ssd_decode_step(&s, x, dt, (const float *)A, B, C, (const float *)D, (float *)st, y,
+                                   nullptr, nullptr);
+        };
+        CHECK(dec(shape(4, 2, 8, 64, 128, 2, SSD_DTYPE_BF16)) == SSD_ERROR_INVALID_VALUE);
+        CHECK(dec(shape(4, 1, 8, 48, 128, 2, SSD_DTYPE_BF16)) == SSD_ERROR_UNSUPPORTED);
+        CHECK(dec(shape(4, 1, 8, 64, 128, 2, SSD_DTYPE_BF16, 1)) == SSD_ERROR_INVALID_VALUE);
+        void *keep = st;
+        st = nullptr;
+        CHECK(dec(d1) == SSD_ERROR_INVALID_VALUE);
+        st = (char *)keep + 8;
+        CHECK(dec(d1) == SSD_ERROR_MISALIGNED);
+        st = keep;
+        void *keepy = y;
+        y = (char *)st + 64;  // y inside the state
+        CHECK(dec(d1) == SSD_ERROR_INVALID_VALUE);
+        y = keepy;
+        void *ev[2] = {f(), nullptr};
+        CHECK(ssd_decode_step(&d1, x, dt, (const float *)A, B, C, nullptr, (float *)st, y, nullptr, ev) ==
+              SSD_ERROR_INVALID_VALUE);
+    }
     CHECK(launches() == before);  // nothing was enqueued by any rejected call
 }
 
@@ -213,6 +240,14 @@ static void valid_calls() {
         Args a = args_for(s, 64, f);
         a.init = a.fin;
         CHECK(fwd(s, 64, a) == SSD_OK);
+    }
+    // a valid decode step: one launch
+    {
+        const ssd_shape d1 = shape(4, 1, 8, 64, 128, 2, SSD_DTYPE_F32);
+        const long c4 = g_launches[4];
+        CHECK(ssd_decode_step(&d1, f(), f(), (const float *)f(), f(), f(), nullptr, (float *)f(), f(), nullptr,
+                              nullptr) == SSD_OK);
+        CHECK(g_launches[4] == c4 + 1);
     }
     for (int st = 0; st <= 6; ++st) CHECK(std::strlen(ssd_status_string((ssd_status)st)) > 1);
     CHECK(ssd_version() >= 200);

@@ -8,7 +8,7 @@
 
 #include "../../mamba_chunked_ssd_amd/csrc/ssd_internal.h"
 
-std::atomic<long> g_launches[4];  // calls per stage
+std::atomic<long> g_launches[5];  // calls per stage (4: the decode step)
 std::atomic<long> g_event_records;
 
 namespace ssd {
@@ -36,6 +36,11 @@ hipError_t launch_state_fused(const Problem &, const Plan &, const void *, const
                               G2View, const float *, float *, float *, const void *, float *, hipStream_t,
                               const LaunchEvents &) {
     g_launches[1]++;
+    return hipSuccess;
+}
+hipError_t launch_decode_step(const Problem &, const void *, const void *, const float *, const void *,
+                              const void *, const float *, float *, void *, hipStream_t, const LaunchEvents &) {
+    g_launches[4]++;
     return hipSuccess;
 }
 hipError_t launch_chunk_out(const Problem &, const Plan &, const void *, const void *, const void *,

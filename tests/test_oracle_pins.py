@@ -252,3 +252,38 @@ def test_chunk_cb_brute_force_and_linear_attention():
             W = np.tril(cb1[bi, h // hpg]) * dt[bi, :, h][None, :]
             want = W @ x[bi, :, h] + D[h] * x[bi, :, h]
             assert np.max(np.abs(y[bi, :, h] - want)) < 1e-10
+
+
+def test_decode_step_single_token_closed_form():
+    # One step from a state s: s' = exp(A dt) s + dt x B^T (per head row p),
+    # y = s' C + D x -- written out with numpy einsum, from a random state.
+    rng = np.random.default_rng(71)
+    b, nh, p, n, g = 3, 4, 5, 6, 2
+    x = rng.standard_normal((b, nh, p))
+    dt = np.abs(rng.standard_normal((b, nh)))
+    A = -np.abs(rng.standard_normal(nh))
+    B = rng.standard_normal((b, g, n))
+    C = rng.standard_normal((b, g, n))
+    D = rng.standard_normal(nh)
+    s = rng.standard_normal((b, nh, p, n))
+    y, s1 = oracle.decode_step(x, dt, A, B, C, D, s)
+    hg = np.arange(nh) // (nh // g)
+    Bh, Ch = B[:, hg], C[:, hg]                       # (b, nh, n) per head
+    decay = np.exp(A[None, :] * dt)[..., None, None]  # (b, nh, 1, 1)
+    want_s = decay * s + (dt[..., None] * x)[..., None] * Bh[:, :, None, :]
+    want_y = np.einsum("bhpn,bhn->bhp", want_s, Ch) + D[None, :, None] * x
+    assert np.allclose(s1, want_s, rtol=1e-13, atol=1e-13)
+    assert np.allclose(y, want_y, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_steps_chain_to_the_scan():
+    # K single steps, each from the previous step's state, give the K-token
+    # scan's outputs and final state (state continuity through one token).
+    pr = pins.problem(73, b=2, L=9, nh=4, p=3, n=5, h0=True)
+    y_ref, h_ref, _ = oracle.scan(**pr)
+    s = pr["h0"]
+    for t in range(pr["x"].shape[1]):
+        y, s = oracle.decode_step(pr["x"][:, t], pr["dt"][:, t], pr["A"], pr["B"][:, t], pr["C"][:, t],
+                                  pr["D"], s)
+        assert np.allclose(y, y_ref[:, t], rtol=1e-12, atol=1e-12)
+    assert np.allclose(s, h_ref, rtol=1e-12, atol=1e-12)
