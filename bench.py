@@ -210,8 +210,9 @@ def main(argv=None):
                     help="repeat the oracle run until this much CPU time has passed")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps after a 1 GiB cache-flush write (reported separately)")
-    ap.add_argument("--plan", choices=["default", "split", "fused"], default="default",
-                    help="launch plan: the library's default, or the split / fused state path")
+    ap.add_argument("--plan", choices=["default", "split", "fused", "tuned"], default="default",
+                    help="launch plan: the library's default, the split / fused state path, or the "
+                         "plan ssd_chunk_scan_fwd_tune picks (tuned before the warm-up, untimed)")
     ap.add_argument("--fused-cols", type=int, default=0,
                     help="dstate columns per fused-state block (0: 32 for headdim <= 64, else 64)")
     ap.add_argument("--decode-batch", type=int, default=128,
@@ -254,7 +255,11 @@ def main(argv=None):
     hip = Hip()
     stream = torch.cuda.current_stream(dev)
     plan = ssd.default_plan(shape, w.chunk_size)
-    if a.plan != "default":
+    tuned_us = None
+    if a.plan == "tuned":
+        plan, tuned_us = ssd.tune(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], w.chunk_size, t["h0"],
+                                  reps=5, y_dtype=ydt, out=y, final_out=fin, workspace=ws)
+    elif a.plan != "default":
         cols = a.fused_cols or (32 if w.headdim <= 64 else 64)
         plan = ssd.make_plan(a.plan, plan.chunk_state_heads, plan.chunk_out_heads,
                              cols if a.plan == "fused" else 0)

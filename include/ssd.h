@@ -210,6 +210,27 @@ ssd_status ssd_chunk_scan_fwd_ex(const ssd_shape *shape,
                                  void *workspace, size_t workspace_bytes, void *stream,
                                  const ssd_plan *plan, void *const *stage_events);
 
+/* Per-shape autotuner ("Kernel shorts: Mamba-2 in cuTile, CompileIQ + Helion,
+ * Deepgram on Trainium2", TL;DR: per-shape tuning of the kernels' tile
+ * configurations).  Runs the caller's problem (same arguments and rules as
+ * ssd_chunk_scan_fwd; initial_states must not alias final_states here) under
+ * candidate plans on `stream` -- heads per block of the chunk-output launch,
+ * then the state path: split with each chunk-state heads per block, fused
+ * with 32 and 64 dstate columns where supported -- each once untimed and
+ * `reps` times (1..1000) with stage events, and writes the plan with the
+ * smallest median time to *best (and that time in microseconds, summed over
+ * the stages, to *best_us unless it is NULL).  Synchronizes `stream` after
+ * each timed run.  On return y and final_states hold the forward pass's
+ * result (computed under *best).  Creates and destroys its own events; the
+ * plan is plain data the caller keeps and passes to ssd_chunk_scan_fwd_ex. */
+ssd_status ssd_chunk_scan_fwd_tune(const ssd_shape *shape,
+                                   const void *x, const void *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   int64_t chunk_size, const float *initial_states,
+                                   void *y, float *final_states,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   int reps, ssd_plan *best, float *best_us);
+
 /* Which stages launch a kernel of their own for this problem (host only):
  * bit i of *mask is set for stage i (0 chunk cumsum, 1 chunk state, 2 state
  * passing, 3 chunk output).  Stages 0, 1 and 3 are clear when there are no

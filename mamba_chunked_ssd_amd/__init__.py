@@ -48,6 +48,7 @@ EXPORTS = [
     "ssd_chunk_scan_fwd_ex",
     "ssd_chunk_scan_fwd_noalloc",
     "ssd_decode_step",
+    "ssd_chunk_scan_fwd_tune",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -158,6 +159,8 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
         lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_void_p)]
         lib.ssd_decode_step.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_tune.argtypes = fwd_args + [ctypes.c_int, pp, ctypes.POINTER(ctypes.c_float)]
+        lib.ssd_chunk_scan_fwd_tune.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []
@@ -380,3 +383,40 @@ def decode_step(x, dt, A, B, C, D, state, *, y_dtype=None, out=None, stream=None
     if st != 0:
         raise SSDError(st, "ssd_decode_step")
     return y
+
+
+def tune(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states=None, *, reps: int = 5,
+         y_dtype=None, out=None, final_out=None, workspace=None, stream=None):
+    """Run ``ssd_chunk_scan_fwd_tune`` on these inputs: returns ``(plan, us)``,
+    the fastest launch plan found and its time in microseconds.  Pass the plan
+    to :func:`chunk_scan_fwd` (``plan=``) for later calls of the same shape."""
+    torch = _torch()
+    lib = load_library()
+    b, L, nh, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    dname = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    dev = x.device
+    ytype = torch.float32 if y_dtype is None else y_dtype
+    shape = make_shape(b, L, nh, p, n, g, dname, False, "bf16" if ytype == torch.bfloat16 else "f32")
+    for name, t, dtp, shp in (("x", x, x.dtype, (b, L, nh, p)), ("dt", dt, x.dtype, (b, L, nh)),
+                              ("A", A, torch.float32, (nh,)), ("B", B, x.dtype, (b, L, g, n)),
+                              ("C", C, x.dtype, (b, L, g, n))):
+        _check(t, name, dtp, shp, dev)
+    if D is not None:
+        _check(D, "D", torch.float32, (nh,), dev)
+    if initial_states is not None:
+        _check(initial_states, "initial_states", torch.float32, (b, nh, p, n), dev)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(shape, chunk_size), 1), dtype=torch.uint8, device=dev)
+    y = out if out is not None else torch.empty((b, L, nh, p), dtype=ytype, device=dev)
+    fin = final_out if final_out is not None else torch.empty((b, nh, p, n), dtype=torch.float32, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    plan = Plan()
+    us = ctypes.c_float()
+    st = lib.ssd_chunk_scan_fwd_tune(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                     int(chunk_size), _ptr(initial_states), _ptr(y), _ptr(fin), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), ctypes.c_void_p(s), int(reps),
+                                     ctypes.byref(plan), ctypes.byref(us))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_tune")
+    return plan, float(us.value)

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libssd.so")
-SOURCES = ["ssd_api.cpp", "k1_cumsum.hip", "k2_chunk_state.hip", "k3_state_pass.hip", "k23_state_fused.hip", "k5_decode_step.hip",
+SOURCES = ["ssd_api.cpp", "ssd_tune.cpp", "k1_cumsum.hip", "k2_chunk_state.hip", "k3_state_pass.hip", "k23_state_fused.hip", "k5_decode_step.hip",
            "k4_out_bf16_f32.hip", "k4_out_bf16_bf16.hip", "k4_out_f32.hip", "ssd_noalloc.hip"]
 HEADERS = ["ssd_device.h", "ssd_internal.h", "ssd_launch.h", "k_cb_tiles.h", "k4_chunk_out.h"]
 ARCH = "gfx950"

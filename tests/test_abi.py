@@ -345,3 +345,25 @@ def test_fused_path_unsupported_for_fp32(lib):
     plan = ssd.make_plan("fused", 1, 1, 64)
     assert lib.ssd_chunk_scan_fwd_stage_launches(ctypes.byref(s), 128, ctypes.byref(plan),
                                                  ctypes.byref(m)) == 2
+
+
+@no_gpu
+def test_tune_rejects_before_any_device_work(lib):
+    f = Fake()
+    v = lambda a: ctypes.c_void_p(a)  # noqa: E731
+    s = shape()
+    plan = ssd.Plan()
+    us = ctypes.c_float()
+
+    def tune(T=256, init=None, fin=None, reps=5, best=True):
+        fin = f() if fin is None else fin
+        return lib.ssd_chunk_scan_fwd_tune(ctypes.byref(s), v(f()), v(f()), v(f()), v(f()), v(f()), v(f()), T,
+                                           None if init is None else v(init), v(f()), v(fin), v(f()),
+                                           ssd.workspace_size(s, 256), None, reps,
+                                           ctypes.byref(plan) if best else None, ctypes.byref(us))
+    assert tune(best=False) == 1
+    assert tune(reps=0) == 1
+    assert tune(reps=1001) == 1
+    assert tune(T=96) == 2
+    h = f()
+    assert tune(init=h, fin=h) == 1   # the candidates would read each other's states
