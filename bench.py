@@ -38,17 +38,20 @@ STAGES = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_out"]
 # taken on, identified by a hash; any change to those sources reports null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    # (workload, y dtype, stage): (sources, sha256[:16], FETCH KiB, WRITE KiB)
-    ("mamba2_2p7b_layer_bf16", "f32", "chunk_out"): (
-        ("k4_chunk_out.h", "k4_out_bf16_f32.hip", "ssd_device.h"), "3a0b437ad6adcf63",
-        45013.19, 81947.85),
+    # (workload, y dtype, stage, state path): (sources, sha256[:16], FETCH KiB, WRITE KiB)
+    ("mamba2_2p7b_layer_bf16", "f32", "chunk_out", "fused"): (
+        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'e0b38472eef460b1', 45015.9, 81961.0),
+    ("mamba2_2p7b_layer_bf16", "f32", "chunk_out", "split"): (
+        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'e0b38472eef460b1', 45015.9, 81960.0),
+    ("mamba2_2p7b_layer_bf16", "f32", "chunk_state", "fused"): (
+        ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), 'd335e9eacd803fb6', 24143.0, 48386.0),
 }
 
 
-def measured_traffic(workload: str, y_dtype: str, stage: str):
+def measured_traffic(workload: str, y_dtype: str, stage: str, plan: dict | None = None):
     """HBM bytes per launch of ``stage`` if counters exist for its current sources."""
     import hashlib
-    ent = MEASURED_TRAFFIC.get((workload, y_dtype, stage))
+    ent = MEASURED_TRAFFIC.get((workload, y_dtype, stage, (plan or {}).get("state_path", "split")))
     if ent is None:
         return None
     files, digest, fetch_kib, write_kib = ent
@@ -146,14 +149,45 @@ def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
         times.append(time.perf_counter() - t0)
     med = float(sorted(times)[len(times) // 2])
     threads = int(os.environ.get("OMP_NUM_THREADS", ncores))
+    single = single_thread_oracle(w)
     return {
         "value": w.tokens / med,
         "unit": "tokens/s",
         "cores": min(threads, ncores),
         "kind": "oracle",
         "sample": "whole workload (%d tokens, all heads), fp64 sequential recurrence, median of %d runs "
-                  "(%.3f s each, %.1f s in all)" % (w.tokens, len(times), med, sum(times)),
+                  "(%.3f s each, %.1f s in all); oracle built with gcc -O2 -fopenmp, no -march=native "
+                  "(the same library runs on any x86-64 host)" % (w.tokens, len(times), med, sum(times)),
+        "single_thread": single,
     }
+
+
+def single_thread_oracle(w) -> dict:
+    """The oracle on one thread (OMP_NUM_THREADS=1, in a child process so the
+    OpenMP runtime starts with that setting) for the tiny workload and for
+    ``w``: tokens/s of one run each."""
+    import subprocess
+    out = {}
+    for name in dict.fromkeys(["tiny_f32", w.name]):
+        code = ("import sys, time; sys.path.insert(0, %r); import oracle, ssd_inputs as si; "
+                "w = si.BY_NAME[%r]; i = si.generate(w); oracle.scan(i['x'][:, :8], i['dt'][:, :8], i['A'], "
+                "i['B'][:, :8], i['C'][:, :8]); t = time.perf_counter(); "
+                "oracle.scan(i['x'], i['dt'], i['A'], i['B'], i['C'], i['D'], i['h0']); "
+                "print(time.perf_counter() - t)" % (ROOT, name))
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+        if r.returncode != 0:
+            out[name] = {"error": r.stderr[-300:]}
+            continue
+        sec = float(r.stdout.strip().splitlines()[-1])
+        tok = si_tokens(name)
+        out[name] = {"value": round(tok / sec, 1), "unit": "tokens/s", "seconds": round(sec, 4), "cores": 1}
+    return out
+
+
+def si_tokens(name: str) -> int:
+    import ssd_inputs as si
+    return si.BY_NAME[name].tokens
 
 
 def decode_bench(hip, w, batch, dev, steps=20, warmup=5) -> dict:
@@ -208,13 +242,13 @@ def main(argv=None):
     ap.add_argument("--cpu-reps", type=int, default=3, help="least number of oracle runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle run until this much CPU time has passed")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps after a 1 GiB cache-flush write (reported separately)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed after a 1 GiB cache-flush write each (per-stage cold times; 0: skip)")
     ap.add_argument("--plan", choices=["default", "split", "fused", "tuned"], default="default",
                     help="launch plan: the library's default, the split / fused state path, or the "
                          "plan ssd_chunk_scan_fwd_tune picks (tuned before the warm-up, untimed)")
-    ap.add_argument("--fused-cols", type=int, default=0,
-                    help="dstate columns per fused-state block (0: 32 for headdim <= 64, else 64)")
+    ap.add_argument("--fused-cols", type=int, default=64,
+                    help="dstate columns per fused-state block (32 or 64)")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="batch of the recurrent decode-step measurement (0: skip it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -260,9 +294,8 @@ def main(argv=None):
         plan, tuned_us = ssd.tune(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], w.chunk_size, t["h0"],
                                   reps=5, y_dtype=ydt, out=y, final_out=fin, workspace=ws)
     elif a.plan != "default":
-        cols = a.fused_cols or (32 if w.headdim <= 64 else 64)
         plan = ssd.make_plan(a.plan, plan.chunk_state_heads, plan.chunk_out_heads,
-                             cols if a.plan == "fused" else 0)
+                             a.fused_cols if a.plan == "fused" else 0)
 
     def step(events=None):
         ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=w.chunk_size,
@@ -271,15 +304,19 @@ def main(argv=None):
 
     if a.calibrate_copy:
         # a plain device copy of known size (1 GiB read + 1 GiB written) whose
-        # FETCH_SIZE / WRITE_SIZE give the counters' scale; the source is
-        # written first so the copy reads real data
+        # FETCH_SIZE / WRITE_SIZE give the counters' scale.  The source is
+        # written first (real data), then a second 1 GiB buffer is written so
+        # that neither L2 nor the 256 MB Infinity Cache still holds the
+        # source when the copy reads it.
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         src.fill_(1.0)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        flush.fill_(2.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, flush
 
     for _ in range(a.warmup):
         step()
@@ -338,8 +375,16 @@ def main(argv=None):
     else:
         roof = {"bound": "mfma", "achieved": round(dflops / t_dom / 1e12, 2), "peak": peak_tf,
                 "unit": "TFLOP/s", "frac": round(dflops / t_dom / 1e12 / peak_tf, 4)}
-    roof["traffic"] = measured_traffic(w.name, "f32" if ydt == torch.float32 else w.dtype, dom)
+    roof["traffic"] = measured_traffic(w.name, "f32" if ydt == torch.float32 else w.dtype, dom,
+                                       plan.as_dict())
     roof["kernel"] = dom
+    # the byte model behind `achieved`: algorithmic bytes of one launch of the
+    # dominant kernel (inputs in their dtype, fp32 intermediates, y at the
+    # y dtype's size -- fp32 by default, whose floor is larger than a bf16 y's)
+    roof["bytes"] = int(dbytes)
+    roof["flops"] = float(dflops)
+    roof["model"] = "algorithmic bytes per launch, y at %d bytes per element" % (
+        4 if ydt == torch.float32 else 2)
     e2e_bytes, e2e_flops = model["e2e"]
     e2e_t = ms_per_step * 1e-3
     e2e_floor = max(e2e_bytes / (PEAK_HBM_GBS * 1e9), e2e_flops / (peak_tf * 1e12))
@@ -371,10 +416,13 @@ def main(argv=None):
         "e2e_stage_sum_roofline_frac": round(sigma_floor / e2e_t, 4),
     }
 
-    if a.cold:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    if a.cold_steps > 0:
+        # per-stage times with cold caches: before each step a 1 GiB write
+        # (more than L2 plus the 256 MB Infinity Cache) evicts the inputs and
+        # the previous step's intermediates; the flush is outside the events
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         cold = []
-        for _ in range(min(a.steps, 20)):
+        for _ in range(a.cold_steps):
             flush.fill_(1.0)
             e = [hip.event() for _ in range(8)]
             step(e)
@@ -382,10 +430,25 @@ def main(argv=None):
             cold.append([hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(4)])
             for ev in e:
                 hip.destroy(ev)
-        cold = np.array(cold).mean(axis=0)
-        out["cold_stage_us"] = {n: round(cold[j] * 1e3, 3) for j, n in enumerate(STAGES) if n not in skipped}
-        out["cold_tokens_per_s"] = round(
-            w.tokens / (sum(cold[j] for j, n in enumerate(STAGES) if n not in skipped) * 1e-3), 1)
+        del flush
+        cold_ms = np.median(np.array(cold), axis=0)
+        cold_stages = {}
+        for j, name in enumerate(STAGES):
+            if name in skipped:
+                continue
+            byts, flops = model[name]
+            t_s = cold_ms[j] * 1e-3
+            floor = max(byts / (PEAK_HBM_GBS * 1e9), flops / (peak_tf * 1e12))
+            cold_stages[name] = {"us": round(cold_ms[j] * 1e3, 3), "roofline_frac": round(floor / t_s, 4)}
+        t_dom_c = cold_ms[dj] * 1e-3
+        out["cold"] = {
+            "steps": a.cold_steps,
+            "stages": cold_stages,
+            "stage_sum_us": round(sum(cold_ms[j] for j, n in enumerate(STAGES) if n not in skipped) * 1e3, 3),
+            "roofline": dict(roof, achieved=round((dbytes if roof["bound"] == "hbm" else dflops / 1e3)
+                                                  / t_dom_c / 1e9, 1),
+                             frac=round((hbm_t if roof["bound"] == "hbm" else mfma_t) / t_dom_c, 4)),
+        }
 
     if a.decode_batch > 0:
         out["decode"] = decode_bench(hip, w, a.decode_batch, dev)
