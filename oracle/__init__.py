@@ -27,6 +27,11 @@ Pass Kernels in NVIDIA CUDA Tile":
 * :func:`decode_step` -- one step of the recurrence for one new token per
   sequence from a given state (the recurrent form the same section names for
   sequential inference): :func:`scan` over a sequence of length 1.
+* :func:`scan_bwd` -- the gradients of <dy, y> + <dhT, h_final> with respect
+  to every input of :func:`scan`: the adjoint of the same recurrence, run in
+  reverse in fp64 (``ssd_oracle.c``).  The pages name the backward pass as
+  what training depends on and derive none; this is the chain rule applied to
+  each step of the recurrence, pinned by finite differences of :func:`scan`.
 
 Inputs may be float32 or float64 numpy arrays; they are widened exactly to
 fp64.  bf16 data is passed as float32 arrays holding bf16-representable values
@@ -71,6 +76,9 @@ def load_library(path: str):
     dp = ctypes.c_void_p
     f.argtypes = [i64] * 6 + [dp] * 9 + [i64, dp]
     f.restype = ctypes.c_int
+    g = lib.ssd_oracle_scan_bwd
+    g.argtypes = [i64] * 6 + [dp] * 16
+    g.restype = ctypes.c_int
     return lib
 
 
@@ -227,3 +235,51 @@ def decode_step(x, dt, A, B, C, D, state):
     x, dt, B, C = (_f64(v) for v in (x, dt, B, C))
     y, hT, _ = scan(x[:, None], dt[:, None], A, B[:, None], C[:, None], D, state)
     return y[:, 0], hT
+
+
+def scan_bwd(x, dt, A, B, C, D=None, h0=None, dy=None, dhT=None):
+    """Gradients of ``<dy, y> + <dhT, h_final>`` through :func:`scan`, fp64.
+
+    Same shapes as :func:`scan`; dy like y (None => 0), dhT like h_final
+    (None => 0).  Returns a dict with ``dx`` (b, L, nh, p), ``ddt`` (b, L, nh),
+    ``dA`` (nh,), ``dB`` and ``dC`` (b, L, g, n), ``dD`` (nh,) and ``dh0``
+    (b, nh, p, n).  dB and dC sum over the heads that share a group; dA and dD
+    over batch and tokens.
+    """
+    return scan_bwd_with(_load(), x, dt, A, B, C, D, h0, dy, dhT)
+
+
+def scan_bwd_with(lib, x, dt, A, B, C, D=None, h0=None, dy=None, dhT=None):
+    """:func:`scan_bwd` through a given library handle."""
+    x, dt, A, B, C = (_f64(v) for v in (x, dt, A, B, C))
+    D, h0, dy, dhT = _f64(D), _f64(h0), _f64(dy), _f64(dhT)
+    bsz, L, nh, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    if dt.shape != (bsz, L, nh) or A.shape != (nh,):
+        raise ValueError("dt/A shape mismatch")
+    if B.shape != (bsz, L, g, n) or C.shape != B.shape:
+        raise ValueError("B/C shape mismatch")
+    if D is not None and D.shape != (nh,):
+        raise ValueError("D shape mismatch")
+    if h0 is not None and h0.shape != (bsz, nh, p, n):
+        raise ValueError("h0 shape mismatch")
+    if dy is None:
+        dy = np.zeros(x.shape, np.float64)
+    if dy.shape != x.shape:
+        raise ValueError("dy shape mismatch")
+    if dhT is not None and dhT.shape != (bsz, nh, p, n):
+        raise ValueError("dhT shape mismatch")
+    out = {
+        "dx": np.zeros(x.shape), "ddt": np.zeros(dt.shape), "dA": np.zeros(nh),
+        "dB": np.zeros(B.shape), "dC": np.zeros(C.shape), "dD": np.zeros(nh),
+        "dh0": np.zeros((bsz, nh, p, n)),
+    }
+    rc = lib.ssd_oracle_scan_bwd(bsz, L, nh, p, n, g,
+                                 _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                 _ptr(h0), _ptr(dy), _ptr(dhT),
+                                 _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                                 _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                                 _ptr(out["dh0"]))
+    if rc != 0:
+        raise ValueError("ssd_oracle_scan_bwd rejected its arguments (rc=%d)" % rc)
+    return out

@@ -320,3 +320,191 @@ def pin_checkpoints(scan, tol=1e-11):
 ALL_PINS = [pin_bruteforce, pin_bruteforce_mp, pin_d_only, pin_decayed_initial_state,
             pin_linear_attention, pin_chunked, pin_split_continuity, pin_group_expansion,
             pin_linearity, pin_scalar_geometric, pin_dt_zero, pin_checkpoints]
+
+
+# ---------------------------------------------------------------------------
+# Pins of the backward pass (the gradients of <dy, y> + <dhT, h_final>).
+#
+# Every ``bpin_*`` takes ``scan_bwd`` with the signature of ``oracle.scan_bwd``
+# and ``scan`` with the forward oracle's signature (the pinned forward above),
+# and raises AssertionError on disagreement.  None of them restates the
+# adjoint recurrence: they come from the forward map itself (its Jacobian
+# columns, finite differences), from symmetries of the recurrence, and from
+# the chain rule through the group and sequence structure.
+# ---------------------------------------------------------------------------
+
+
+def bwd_problem(seed, b=1, L=7, nh=2, p=3, n=4, g=1, h0=True):
+    pr = problem(seed, b=b, L=L, nh=nh, p=p, n=n, g=g, h0=h0)
+    rng = np.random.default_rng(seed + 1000)
+    dy = rng.standard_normal(pr["x"].shape)
+    dhT = rng.standard_normal((b, nh, p, n))
+    return pr, dy, dhT
+
+
+def _objective(scan, pr, dy, dhT):
+    y, hT, _ = scan(**pr)
+    return float(np.sum(y * dy) + np.sum(hT * dhT))
+
+
+_GRAD_OF = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+
+
+def bpin_affine_jacobians(scan_bwd, scan, tol=1e-11):
+    # (y, h_final) is affine in each of x, B, C, D and h0 with the others
+    # fixed, so each Jacobian column is f(theta + e_k) - f(theta) exactly (up
+    # to rounding), and the gradient is the transposed Jacobian applied to
+    # (dy, dhT).  Every element of every one of these gradients is checked.
+    for seed, g, nh in ((201, 1, 2), (202, 2, 4)):
+        pr, dy, dhT = bwd_problem(seed, b=2, L=5, nh=nh, p=2, n=3, g=g)
+        gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+        base = _objective(scan, pr, dy, dhT)
+        for name in ("x", "B", "C", "D", "h0"):
+            v = pr[name]
+            want = np.zeros(v.size)
+            for k in range(v.size):
+                e = np.zeros(v.size)
+                e[k] = 1.0
+                q = dict(pr)
+                q[name] = v + e.reshape(v.shape)
+                want[k] = _objective(scan, q, dy, dhT) - base
+            got = gr[_GRAD_OF[name]].ravel()
+            assert rel_err(got, want) < tol, ("affine jacobian", name, seed)
+
+
+def bpin_finite_differences(scan_bwd, scan, tol=1e-7):
+    # dt and A enter through exp(A dt): central differences with Richardson
+    # extrapolation (error O(eps^4)) for every element of ddt and dA.
+    pr, dy, dhT = bwd_problem(211, b=2, L=6, nh=3, p=2, n=3, g=1)
+    gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+    for name in ("dt", "A"):
+        v = pr[name]
+        want = np.zeros(v.size)
+        for k in range(v.size):
+            e = np.zeros(v.size)
+            e[k] = 1.0
+            e = e.reshape(v.shape)
+
+            def f(s):
+                q = dict(pr)
+                q[name] = v + s * e
+                return _objective(scan, q, dy, dhT)
+
+            h = 1e-3
+            d1 = (f(h) - f(-h)) / (2 * h)
+            d2 = (f(h / 2) - f(-h / 2)) / h
+            want[k] = (4 * d2 - d1) / 3
+        assert rel_err(gr[_GRAD_OF[name]].ravel(), want) < tol, ("finite differences", name)
+
+
+def bpin_scaling_invariants(scan_bwd, scan, tol=1e-10):
+    # Three one-parameter symmetries of the forward map give Euler identities
+    # that tie different gradients together (d/ds of the objective at s = 1):
+    #  1. (dt, A, B) -> (s dt, A / s, B / s) leaves A dt and dt B, hence every
+    #     output, unchanged:    <dt, ddt> - <A, dA> - <B, dB> = 0 ;
+    #  2. (x, B, D) -> (s x, B / s, D / s) leaves dt B x^T and D x unchanged:
+    #                           <x, dx> - <B, dB> - <D, dD> = 0 ;
+    #  3. (C, B, h0) -> (s C, B / s, h0 / s) scales every state by 1 / s and
+    #     leaves y unchanged, so the objective changes by -<dhT, h_final>:
+    #                           <C, dC> - <B, dB> - <h0, dh0> + <dhT, h_final> = 0 .
+    for seed, g, nh in ((221, 1, 2), (222, 2, 4)):
+        pr, dy, dhT = bwd_problem(seed, b=2, L=9, nh=nh, p=3, n=4, g=g)
+        gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+        _, hT, _ = scan(**pr)
+
+        def dot(a, b):
+            return float(np.sum(np.asarray(a) * np.asarray(b)))
+
+        scale = sum(abs(dot(pr[k], gr[_GRAD_OF[k]])) for k in _GRAD_OF) + 1.0
+        i1 = dot(pr["dt"], gr["ddt"]) - dot(pr["A"], gr["dA"]) - dot(pr["B"], gr["dB"])
+        i2 = dot(pr["x"], gr["dx"]) - dot(pr["B"], gr["dB"]) - dot(pr["D"], gr["dD"])
+        i3 = dot(pr["C"], gr["dC"]) - dot(pr["B"], gr["dB"]) - dot(pr["h0"], gr["dh0"]) + dot(dhT, hT)
+        for name, v in (("dt-A-B", i1), ("x-B-D", i2), ("C-B-h0", i3)):
+            assert abs(v) / scale < tol, ("scaling invariant", name, v)
+
+
+def bpin_single_token(scan_bwd, scan, tol=1e-12):
+    # One token from a zero state: h = dt x B^T, y = dt (C . B) x + D x, so by
+    # hand (per head; B and C of the head's group)
+    #   dx  = dt (C . B) dy + D dy + dt dhT B      dD  = dy . x
+    #   dC  = dt (dy . x) B                        dB  = dt (dy . x) C + dt dhT^T x
+    #   ddt = (C . B)(dy . x) + x^T dhT B          dA  = 0
+    # and, through h = exp(A dt) h0 + ... with h0 = 0,  dh0 = exp(A dt)(dhT + dy C^T).
+    pr, dy, dhT = bwd_problem(231, b=2, L=1, nh=4, p=3, n=5, g=2, h0=False)
+    gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+    x, dt, A, B, C, D = (pr[k] for k in ("x", "dt", "A", "B", "C", "D"))
+    b, _, nh, p = x.shape
+    g = B.shape[2]
+    want = {k: np.zeros_like(gr[k]) for k in gr}
+    for bi in range(b):
+        for h in range(nh):
+            gi = _group(h, nh, g)
+            Bv, Cv, xv, dyv, d = B[bi, 0, gi], C[bi, 0, gi], x[bi, 0, h], dy[bi, 0, h], dt[bi, 0, h]
+            cb, yx = float(Cv @ Bv), float(dyv @ xv)
+            want["dx"][bi, 0, h] = d * cb * dyv + D[h] * dyv + d * (dhT[bi, h] @ Bv)
+            want["dD"][h] += yx
+            want["dC"][bi, 0, gi] += d * yx * Bv
+            want["dB"][bi, 0, gi] += d * yx * Cv + d * (dhT[bi, h].T @ xv)
+            want["ddt"][bi, 0, h] = cb * yx + float(xv @ dhT[bi, h] @ Bv)
+            want["dh0"][bi, h] = np.exp(A[h] * d) * (dhT[bi, h] + np.outer(dyv, Cv))
+    for k in want:
+        assert rel_err(gr[k], want[k]) < tol or np.max(np.abs(gr[k] - want[k])) < 1e-14, ("single token", k)
+
+
+def bpin_group_replication(scan_bwd, scan, tol=1e-12):
+    # Sharing one B/C row among a group's heads is replication: with the rows
+    # copied out to one group per head, the shared gradient is the sum of the
+    # per-head copies' gradients (the chain rule through the copy), and every
+    # other gradient is unchanged.
+    pr, dy, dhT = bwd_problem(241, b=2, L=6, nh=4, p=2, n=3, g=2)
+    gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+    hg = np.arange(4) // 2
+    ex = dict(pr)
+    ex["B"] = pr["B"][:, :, hg]
+    ex["C"] = pr["C"][:, :, hg]
+    ge = scan_bwd(**ex, dy=dy, dhT=dhT)
+    for k in ("dB", "dC"):
+        summed = np.stack([ge[k][:, :, hg == gi].sum(axis=2) for gi in range(2)], axis=2)
+        assert rel_err(gr[k], summed) < tol, ("group replication", k)
+    for k in ("dx", "ddt", "dA", "dD", "dh0"):
+        assert rel_err(gr[k], ge[k]) < tol, ("group replication", k)
+
+
+def bpin_split_continuity(scan_bwd, scan, tol=1e-12):
+    # The sequence split at m: the second part starts from the first part's
+    # final state, and the first part's backward receives the second part's
+    # dh0 as its dhT.  Per-token gradients concatenate, dA and dD add, and the
+    # whole sequence's dh0 is the first part's.
+    pr, dy, dhT = bwd_problem(251, b=2, L=10, nh=2, p=3, n=4, g=1)
+    gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+    m = 4
+    tok = ("x", "dt", "B", "C")
+    p1 = {k: (v[:, :m] if k in tok else v) for k, v in pr.items()}
+    _, h_m, _ = scan(**p1)
+    p2 = {k: (v[:, m:] if k in tok else v) for k, v in pr.items()}
+    p2["h0"] = h_m
+    g2 = scan_bwd(**p2, dy=dy[:, m:], dhT=dhT)
+    g1 = scan_bwd(**p1, dy=dy[:, :m], dhT=g2["dh0"])
+    for k in ("dx", "ddt", "dB", "dC"):
+        assert rel_err(gr[k], np.concatenate([g1[k], g2[k]], axis=1)) < tol, ("split", k)
+    for k in ("dA", "dD"):
+        assert rel_err(gr[k], g1[k] + g2[k]) < tol, ("split", k)
+    assert rel_err(gr["dh0"], g1["dh0"]) < tol, ("split", "dh0")
+
+
+def bpin_empty_and_zero(scan_bwd, scan):
+    # seqlen 0: the final state is h0, so dh0 = dhT and all else is zero.
+    # dy = 0 and dhT = 0: every gradient is exactly zero.
+    pr, dy, dhT = bwd_problem(261, b=1, L=0, nh=2, p=2, n=3)
+    gr = scan_bwd(**pr, dy=dy, dhT=dhT)
+    assert np.array_equal(gr["dh0"], dhT)
+    for k in ("dA", "dD"):
+        assert not np.any(gr[k])
+    pr, dy, dhT = bwd_problem(262, b=1, L=5, nh=2, p=2, n=3)
+    gr = scan_bwd(**pr, dy=np.zeros_like(dy), dhT=np.zeros_like(dhT))
+    for k, v in gr.items():
+        assert not np.any(v), ("zero cotangent", k)
+
+
+BWD_PINS = [bpin_affine_jacobians, bpin_finite_differences, bpin_scaling_invariants, bpin_single_token,
+            bpin_group_replication, bpin_split_continuity, bpin_empty_and_zero]

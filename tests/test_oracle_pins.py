@@ -183,12 +183,28 @@ MUTANTS = {
 }
 
 
-@pytest.fixture(scope="module")
-def mutant_libs(tmp_path_factory):
+# planted mistakes in the backward (adjoint) part of the oracle
+BWD_MUTANTS = {
+    "bwd_ddt_drops_decay_term": ("ddt[(b * seqlen + t) * nheads + h] = xLB + A[h] * alpha * inner;",
+                                 "ddt[(b * seqlen + t) * nheads + h] = xLB;"),
+    "bwd_carry_without_decay": ("lam[k] *= alpha;", "lam[k] *= 1.0;"),
+    "bwd_dC_from_previous_state": ("sc += ht[p * N + n] * dyt[p];", "sc += hprev[p * N + n] * dyt[p];"),
+    "bwd_dB_missing_dt": ("dBt[n] = dtv * sb;", "dBt[n] = sb;"),
+    "bwd_dx_missing_skip": ("dxt[p] = dtv * lb + d_skip * dyt[p];", "dxt[p] = dtv * lb;"),
+    "bwd_dA_missing_dt": ("dA_acc += dtv * alpha * inner;", "dA_acc += alpha * inner;"),
+    "bwd_adjoint_uses_B_not_C": ("lam[p * N + n] += dyt[p] * Ct[n];", "lam[p * N + n] += dyt[p] * Bt[n];"),
+    "bwd_group_sum_strided": ("for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {",
+                              "for (int64_t h = g; h < nheads; h += ngroups) {"),
+    "bwd_decay_inner_with_current_state": ("inner += lam[p * N + n] * hprev[p * N + n];",
+                                           "inner += lam[p * N + n] * ht[p * N + n];"),
+    "bwd_dD_uses_dx": ("dyx += dyt[p] * xt[p];", "dyx += dyt[p] * dxt[p];"),
+}
+
+
+def _compile_mutants(d, mutants):
     src = open(_SRC).read()
-    d = tmp_path_factory.mktemp("mutants")
     libs = {}
-    for name, (old, new) in MUTANTS.items():
+    for name, (old, new) in mutants.items():
         assert old in src, "mutation target vanished: %s" % name
         cpath = d / (name + ".c")
         cpath.write_text(src.replace(old, new, 1))
@@ -197,6 +213,16 @@ def mutant_libs(tmp_path_factory):
                         "-o", str(so), "-lm"], check=True)
         libs[name] = oracle.load_library(str(so))
     return libs
+
+
+@pytest.fixture(scope="module")
+def mutant_libs(tmp_path_factory):
+    return _compile_mutants(tmp_path_factory.mktemp("mutants"), MUTANTS)
+
+
+@pytest.fixture(scope="module")
+def bwd_mutant_libs(tmp_path_factory):
+    return _compile_mutants(tmp_path_factory.mktemp("bwd_mutants"), BWD_MUTANTS)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -287,3 +313,37 @@ def test_decode_steps_chain_to_the_scan():
                                   pr["D"], s)
         assert np.allclose(y, y_ref[:, t], rtol=1e-12, atol=1e-12)
     assert np.allclose(s, h_ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the backward pass
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("pin", pins.BWD_PINS, ids=lambda f: f.__name__)
+def test_oracle_backward_passes_pin(pin):
+    pin(oracle.scan_bwd, oracle.scan)
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_pins_catch_planted_mistake(name, bwd_mutant_libs):
+    lib = bwd_mutant_libs[name]
+
+    def scan_bwd(*a, **k):
+        return oracle.scan_bwd_with(lib, *a, **k)
+
+    failed = []
+    for pin in pins.BWD_PINS:
+        try:
+            pin(scan_bwd, oracle.scan)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, "no backward pin caught mutant %s" % name
+
+
+def test_backward_rejects_bad_arguments():
+    pr, dy, dhT = pins.bwd_problem(271)
+    with pytest.raises(ValueError):
+        oracle.scan_bwd(**pr, dy=dy[:, :-1], dhT=dhT)
+    with pytest.raises(ValueError):
+        oracle.scan_bwd(**pr, dy=dy, dhT=dhT[:, :1])
