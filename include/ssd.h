@@ -295,6 +295,69 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_shape *shape,
                                       int64_t chunk_size, const float *initial_states,
                                       void *y, float *final_states, void *stream);
 
+/* Backward pass: the gradients of a scalar loss L through ssd_chunk_scan_fwd.
+ *
+ * The pages name the backward pass as what training depends on
+ * ("Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+ * CUDA Tile", section "Mamba-2 architecture": the chunked form serves
+ * training and prefill) and derive none.  This computes the chain rule through
+ * the recurrence of that section, h_t = exp(A dt_t) h_{t-1} + dt_t B_t x_t^T,
+ * y_t = C_t^T h_t + D x_t, given dy = dL/dy and dL/dh_final, evaluated chunk
+ * by chunk: the chunk-start states are recomputed from the inputs (nothing of
+ * the forward call is kept), the gradient of the state is carried across the
+ * chunks in reverse, and per chunk the gradients take the form of the forward
+ * chunk output with the operands' roles exchanged (MFMA kernels).
+ *
+ *   shape, x, dt, A, B, C, D, chunk_size, initial_states
+ *                    exactly as passed to ssd_chunk_scan_fwd (same layouts,
+ *                    dtypes and supported sizes); flags must be 0, y_dtype
+ *                    plays no part
+ *   dy               dL/dy, (batch, seqlen, nheads, headdim) in dtype
+ *   d_final_states   dL/dh_final, (batch, nheads, headdim, dstate) fp32;
+ *                    NULL => 0
+ * Outputs, all fp32 and written (not accumulated):
+ *   dx               (batch, seqlen, nheads, headdim)
+ *   ddt              (batch, seqlen, nheads)
+ *   dA               (nheads)             summed over batch and tokens
+ *   dB, dC           (batch, seqlen, ngroups, dstate), summed over the heads
+ *                    of each group
+ *   dD               (nheads) or NULL => not written (computed as if D were
+ *                    given when D is NULL, i.e. the gradient at D = 0)
+ *   d_initial_states (batch, nheads, headdim, dstate) or NULL => not written
+ * Pointers: x, B, C, dy, the state tensors, dx, dB, dC 16-byte aligned;
+ * the workspace 256-byte aligned and at least
+ * ssd_chunk_scan_bwd_workspace_size bytes.  No output may overlap an input,
+ * the workspace or another output.  All checks happen before the first
+ * launch; on error nothing is enqueued and the outputs are untouched.  The
+ * call enqueues on `stream` and does not synchronise.  The result is
+ * deterministic (fixed reduction orders, no atomics). */
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_shape *shape, int64_t chunk_size);
+ssd_status ssd_chunk_scan_bwd(const ssd_shape *shape,
+                              const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              int64_t chunk_size, const float *initial_states,
+                              const void *dy, const float *d_final_states,
+                              float *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                              float *d_initial_states,
+                              void *workspace, size_t workspace_bytes, void *stream);
+/* As ssd_chunk_scan_bwd, with 2 * SSD_BWD_STAGES valid hipEvent_t recorded
+ * by the stages' own dispatches (start, stop per stage), stages in order:
+ * 0 cumsum, 1 chunk states, 2 state passing (the recomputed forward states),
+ * 3 adjoint chunk terms, 4 reverse carry, 5 score tiles, 6 dx pass, 7 dB
+ * pass, 8 dC pass, 9 the sums of the decay-gradient matrix, 10 per-token
+ * finish (ddt), 11 reductions (dB, dC, dA, dD).  A stage with nothing to do
+ * records both its events back to back. */
+#define SSD_BWD_STAGES 12
+ssd_status ssd_chunk_scan_bwd_profiled(const ssd_shape *shape,
+                                       const void *x, const void *dt, const float *A,
+                                       const void *B, const void *C, const float *D,
+                                       int64_t chunk_size, const float *initial_states,
+                                       const void *dy, const float *d_final_states,
+                                       float *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                                       float *d_initial_states,
+                                       void *workspace, size_t workspace_bytes, void *stream,
+                                       void *const *stage_events);
+
 /* Static, human-readable description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

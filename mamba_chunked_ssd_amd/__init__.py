@@ -49,6 +49,9 @@ EXPORTS = [
     "ssd_chunk_scan_fwd_noalloc",
     "ssd_decode_step",
     "ssd_chunk_scan_fwd_tune",
+    "ssd_chunk_scan_bwd_workspace_size",
+    "ssd_chunk_scan_bwd",
+    "ssd_chunk_scan_bwd_profiled",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -161,6 +164,13 @@ def load_library(path: str | None = None):
         lib.ssd_decode_step.restype = ctypes.c_int
         lib.ssd_chunk_scan_fwd_tune.argtypes = fwd_args + [ctypes.c_int, pp, ctypes.POINTER(ctypes.c_float)]
         lib.ssd_chunk_scan_fwd_tune.restype = ctypes.c_int
+        lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [sp, i64]
+        lib.ssd_chunk_scan_bwd_workspace_size.restype = sz
+        bwd_args = [sp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ssd_chunk_scan_bwd.argtypes = bwd_args
+        lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
+        lib.ssd_chunk_scan_bwd_profiled.argtypes = bwd_args + [ctypes.POINTER(ctypes.c_void_p)]
+        lib.ssd_chunk_scan_bwd_profiled.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []
@@ -334,6 +344,87 @@ def chunk_scan_fwd(x, dt, A, B, C, D=None, chunk_size: int = 256, initial_states
     if return_final_states:
         return y, fin
     return y
+
+
+BWD_STAGES = ("chunk_cumsum", "chunk_state", "state_pass", "adjoint_chunk_state", "adjoint_carry",
+              "score_tiles", "dx_pass", "dB_pass", "dC_pass", "w_sums", "token_finish", "reduce")
+
+
+def bwd_workspace_size(shape: Shape, chunk_size: int) -> int:
+    return int(load_library().ssd_chunk_scan_bwd_workspace_size(ctypes.byref(shape), chunk_size))
+
+
+def chunk_scan_bwd(x, dt, A, B, C, D, dy, chunk_size: int = 256, initial_states=None,
+                   d_final_states=None, *, want_dD: bool = True, want_d_initial: bool = True,
+                   workspace=None, stream=None, events=None):
+    """Gradients through :func:`chunk_scan_fwd` (``ssd_chunk_scan_bwd``).
+
+    Inputs as passed to :func:`chunk_scan_fwd`, plus ``dy`` (dL/dy, the input
+    dtype), and optionally
+    ``d_final_states`` (dL/dh_final, float32).  Returns a dict of float32
+    tensors ``dx, ddt, dA, dB, dC`` and, when requested, ``dD`` and
+    ``d_initial_states``.  ``events``: 22 raw hipEvent_t handles (a start and
+    stop per stage of :data:`BWD_STAGES`).
+    """
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x and B must be 4-D")
+    b, L, nh, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    if x.dtype == torch.bfloat16:
+        dname = "bf16"
+    elif x.dtype == torch.float32:
+        dname = "f32"
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a ROCm device (got %s)" % dev)
+    _check(x, "x", x.dtype, (b, L, nh, p), dev)
+    _check(dt, "dt", x.dtype, (b, L, nh), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    _check(B, "B", x.dtype, (b, L, g, n), dev)
+    _check(C, "C", x.dtype, (b, L, g, n), dev)
+    if D is not None:
+        _check(D, "D", torch.float32, (nh,), dev)
+    if initial_states is not None:
+        _check(initial_states, "initial_states", torch.float32, (b, nh, p, n), dev)
+    _check(dy, "dy", x.dtype, (b, L, nh, p), dev)
+    if d_final_states is not None:
+        _check(d_final_states, "d_final_states", torch.float32, (b, nh, p, n), dev)
+    shape = make_shape(b, L, nh, p, n, g, dname)
+    need = bwd_workspace_size(shape, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {
+        "dx": torch.empty((b, L, nh, p), **f32), "ddt": torch.empty((b, L, nh), **f32),
+        "dA": torch.empty((nh,), **f32), "dB": torch.empty((b, L, g, n), **f32),
+        "dC": torch.empty((b, L, g, n), **f32),
+    }
+    if want_dD:
+        out["dD"] = torch.empty((nh,), **f32)
+    if want_d_initial:
+        out["d_initial_states"] = torch.empty((b, nh, p, n), **f32)
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    args = [ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
+            _ptr(initial_states), _ptr(dy), _ptr(d_final_states), _ptr(out["dx"]), _ptr(out["ddt"]),
+            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
+            _ptr(out.get("d_initial_states")), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(s)]
+    if events is None:
+        st = lib.ssd_chunk_scan_bwd(*args)
+        where = "ssd_chunk_scan_bwd"
+    else:
+        if len(events) != 2 * len(BWD_STAGES):
+            raise ValueError("events: a (start, stop) pair for each of the %d stages" % len(BWD_STAGES))
+        ev = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
+        st = lib.ssd_chunk_scan_bwd_profiled(*args, ev)
+        where = "ssd_chunk_scan_bwd_profiled"
+    if st != 0:
+        raise SSDError(st, where)
+    return out
 
 
 def decode_step(x, dt, A, B, C, D, state, *, y_dtype=None, out=None, stream=None, events=None):

@@ -18,9 +18,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libssd.so")
-SOURCES = ["ssd_api.cpp", "ssd_tune.cpp", "k1_cumsum.hip", "k2_chunk_state.hip", "k3_state_pass.hip", "k23_state_fused.hip", "k5_decode_step.hip",
-           "k4_out_bf16_f32.hip", "k4_out_bf16_bf16.hip", "k4_out_f32.hip", "ssd_noalloc.hip"]
-HEADERS = ["ssd_device.h", "ssd_internal.h", "ssd_launch.h", "k_cb_tiles.h", "k4_chunk_out.h"]
+SOURCES = ["ssd_api.cpp", "ssd_tune.cpp", "ssd_bwd.cpp", "k1_cumsum.hip", "k2_chunk_state.hip", "k3_state_pass.hip",
+           "k23_state_fused.hip", "k5_decode_step.hip", "k4_out_bf16_f32.hip", "k4_out_bf16_bf16.hip",
+           "k4_out_f32.hip", "ssd_noalloc.hip", "kb_aux.hip", "kb_pass_q.hip", "kb_pass_b.hip", "kb_pass_c.hip"]
+HEADERS = ["ssd_device.h", "ssd_internal.h", "ssd_host.h", "ssd_launch.h", "k_cb_tiles.h", "k4_chunk_out.h",
+           "kb_pass.h", "kb_pass_inst.h"]
 ARCH = "gfx950"
 
 

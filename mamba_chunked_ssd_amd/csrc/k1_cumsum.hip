@@ -23,7 +23,10 @@
 // the same page's section "Mamba-2 architecture"),
 //     W_t = exp2(G2_last - G2_t) dt_t ,
 // whose exponent is formed exactly in fp64 before the fp32 exp2.  Tokens past
-// seqlen are treated as dt = 0: G2 stays flat and DT, W are 0.
+// seqlen are treated as dt = 0: G2 stays flat and DT, W are 0.  On request
+// (the backward pass) it also writes exp2(G2_t), the weight with which the
+// output gradient at token t enters the adjoint of its chunk's starting
+// state (0 past seqlen).
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -42,8 +45,8 @@ __device__ __forceinline__ float load_dt<uint16_t>(const uint16_t *p) { return b
 template <typename Tin, int T>
 __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
     const Tin *__restrict__ dt, const float *__restrict__ A, float *__restrict__ G2hi,
-    float *__restrict__ G2lo, float *__restrict__ DT, float *__restrict__ W, int64_t seqlen,
-    int nheads, int64_t Lp) {
+    float *__restrict__ G2lo, float *__restrict__ DT, float *__restrict__ W, float *__restrict__ Wb,
+    int64_t seqlen, int nheads, int64_t Lp) {
     constexpr int E = T / 64;  // tokens per lane
     const int c = blockIdx.x;
     const int h = blockIdx.y * kHeadsPerBlock + (threadIdx.x >> 6);
@@ -63,25 +66,31 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
     store_vec<E>(G2lo + base, lo);
     store_vec<E>(DT + base, d);
     store_vec<E>(W + base, wt);
+    if (Wb != nullptr) {
+        float eg[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) eg[e] = (t0 + e < seqlen) ? fast_exp2(hi[e]) * fast_exp2(lo[e]) : 0.f;
+        store_vec<E>(Wb + base, eg);
+    }
 }
 
 template <typename Tin, int T>
 hipError_t launch_t(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
-                    float *W, hipStream_t stream, const LaunchEvents &ev) {
+                    float *W, float *Wb, hipStream_t stream, const LaunchEvents &ev) {
     dim3 grid((unsigned)p.nchunks, (unsigned)((p.nheads + kHeadsPerBlock - 1) / kHeadsPerBlock),
               (unsigned)p.batch);
     launch_kernel((k1_cumsum<Tin, T>), grid, dim3(64 * kHeadsPerBlock), 0, stream, ev, dt, A,
-                  G2.hi, G2.lo, DT, W, p.seqlen, (int)p.nheads, p.padded_len);
+                  G2.hi, G2.lo, DT, W, Wb, p.seqlen, (int)p.nheads, p.padded_len);
     return hipGetLastError();
 }
 
 template <typename Tin>
 hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, G2Pair G2, float *DT,
-                        float *W, hipStream_t stream, const LaunchEvents &ev) {
+                        float *W, float *Wb, hipStream_t stream, const LaunchEvents &ev) {
     switch (p.chunk) {
-        case 64: return launch_t<Tin, 64>(p, dt, A, G2, DT, W, stream, ev);
-        case 128: return launch_t<Tin, 128>(p, dt, A, G2, DT, W, stream, ev);
-        case 256: return launch_t<Tin, 256>(p, dt, A, G2, DT, W, stream, ev);
+        case 64: return launch_t<Tin, 64>(p, dt, A, G2, DT, W, Wb, stream, ev);
+        case 128: return launch_t<Tin, 128>(p, dt, A, G2, DT, W, Wb, stream, ev);
+        case 256: return launch_t<Tin, 256>(p, dt, A, G2, DT, W, Wb, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
@@ -89,9 +98,9 @@ hipError_t launch_dtype(const Problem &p, const Tin *dt, const float *A, G2Pair 
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
-                               float *DT, float *W, hipStream_t stream, const LaunchEvents &ev) {
-    if (p.bf16) return launch_dtype(p, static_cast<const uint16_t *>(dt), A, G2, DT, W, stream, ev);
-    return launch_dtype(p, static_cast<const float *>(dt), A, G2, DT, W, stream, ev);
+                               float *DT, float *W, hipStream_t stream, const LaunchEvents &ev, float *Wb) {
+    if (p.bf16) return launch_dtype(p, static_cast<const uint16_t *>(dt), A, G2, DT, W, Wb, stream, ev);
+    return launch_dtype(p, static_cast<const float *>(dt), A, G2, DT, W, Wb, stream, ev);
 }
 
 }  // namespace ssd

@@ -131,7 +131,7 @@ hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View 
     // 16.9 -> 15.4 us, grouped fp32 workload 1.94 -> 1.84 ms), 16 beyond
     constexpr int kShallow = 4, kDeep = 16;
     const bool deep = p.nchunks > 128;
-    const int64_t ntiles = uses_cb_tiles(p) ? p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) : 0;
+    const int64_t ntiles = (uses_cb_tiles(p) && CB != nullptr) ? p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) : 0;
     if (ntiles > 0) {
         const int64_t ncb = (ntiles + 4 * kCbPerWave - 1) / (4 * kCbPerWave);
         if (blocks + ncb > INT_MAX) return hipErrorInvalidValue;

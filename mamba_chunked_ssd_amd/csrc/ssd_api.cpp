@@ -15,15 +15,13 @@
 #include <limits>
 
 #include "../../include/ssd.h"
+#include "ssd_host.h"
 #include "ssd_internal.h"
 
 namespace ssd {
 namespace {
 
-constexpr size_t kAlign = 256;
 constexpr int64_t kMaxI32 = std::numeric_limits<int32_t>::max();
-
-size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out) {
     if (a < 0 || b < 0) return false;
@@ -36,7 +34,11 @@ bool chunk_supported(int64_t t) { return t == 64 || t == 128 || t == 256; }
 bool headdim_supported(int64_t p) { return p == 32 || p == 64 || p == 128; }
 bool dstate_supported(int64_t n) { return n >= 16 && n <= 256 && n % 16 == 0; }
 
-// Shape checks shared by the size query and the forward call.
+}  // namespace
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Shape checks shared by the size queries, the forward and the backward call.
 ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
     if (s == nullptr) return SSD_ERROR_INVALID_VALUE;
     if (s->batch < 0 || s->seqlen < 0 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
@@ -89,6 +91,8 @@ ssd_status check_shape(const ssd_shape *s, int64_t chunk, Problem *p) {
     return SSD_OK;
 }
 
+namespace {
+
 ssd_workspace_layout layout_for(const Problem &p, bool keep) {
     ssd_workspace_layout l;
     std::memset(&l, 0, sizeof(l));
@@ -120,18 +124,6 @@ ssd_workspace_layout layout_for(const Problem &p, bool keep) {
     return l;
 }
 
-bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
-
-struct Range {
-    uintptr_t lo, hi;  // [lo, hi)
-};
-Range range_of(const void *ptr, size_t bytes) {
-    return Range{(uintptr_t)ptr, (uintptr_t)ptr + bytes};
-}
-bool overlap(Range a, Range b) {
-    if (a.lo == a.hi || b.lo == b.hi) return false;
-    return a.lo < b.hi && b.lo < a.hi;
-}
 
 // Pick heads-per-block for a stage whose blocks each handle one (batch, chunk,
 // group) and a run of heads: each block pays a fixed set-up cost (staging the

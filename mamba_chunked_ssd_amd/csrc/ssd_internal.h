@@ -64,8 +64,11 @@ struct LaunchEvents {
 
 // Stage 1: G2 (hi/lo), dt widened to fp32 -> DT and the chunk-state weights
 // W_t = exp2(G2_last - G2_t) DT_t, all head-major.
+// With Wb non-null it also writes exp2(G2_t) (0 past seqlen), the backward
+// pass's weights for the adjoint chunk terms.
 hipError_t launch_chunk_cumsum(const Problem &p, const void *dt, const float *A, G2Pair G2,
-                               float *DT, float *W, hipStream_t stream, const LaunchEvents &ev);
+                               float *DT, float *W, hipStream_t stream, const LaunchEvents &ev,
+                               float *Wb = nullptr);
 
 // Stage 2: per-chunk input state s_c = sum_t W_t x_t B_t^T,
 // written as (batch, nheads, nchunks, headdim, dstate) fp32.
@@ -105,5 +108,62 @@ hipError_t launch_chunk_out(const Problem &p, const Plan &plan, const void *x, c
                             const void *C, const float *CB, G2View G2, const float *DT,
                             const float *D, const float *H, void *y, hipStream_t stream,
                             const LaunchEvents &ev);
+
+// ---------------------------------------------------------------------------
+// Backward pass (ssd_chunk_scan_bwd)
+// ---------------------------------------------------------------------------
+
+// Score tiles B_r . C_s of every (batch, chunk, group), the 16 x 16 blocks on
+// and above the diagonal, in the layout the dx pass reads.
+hipError_t launch_bwd_scores(const Problem &p, const void *B, const void *C, float *ST, hipStream_t stream,
+                             const LaunchEvents &ev);
+// Reverse carry of the adjoint state: E (per (b, h, c): hi/lo bf16 planes for
+// bf16 problems, fp32 for fp32 problems), per-wave partials of
+// exp(G_last) <E_c, h_c> (headdim * dstate / 256 per chunk) and the gradient
+// of the initial state (dinit may be null).
+hipError_t launch_bwd_carry(const Problem &p, const float *U, const void *H, G2View G2, const float *dfinal,
+                            void *E, float *Zp, float *dinit, hipStream_t stream, const LaunchEvents &ev);
+
+// One of the MFMA passes (kb_pass.h): 0 = dx and the per-token dot products,
+// 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16).
+struct BwdPassLaunch {
+    int pass;
+    const void *x, *dy, *B, *C;
+    G2View G2;
+    const float *DT;
+    const void *E;
+    const void *H;
+    const float *ST;
+    const float *D;
+    float *out;
+    float *xq, *xqi, *dyx, *cdi;  // per-token partial sums (kb_pass.h)
+    double *wcol, *wrow;
+    int dv;      // columns per block (16, 32 or 64)
+    int hb;      // heads per block
+    int lds_pad; // LDS row padding in elements (0 or 8)
+};
+// Column tiles of the dB and dC passes that their registers hold without
+// spilling (the rule of kb_pass_inst.h's bc_dv_ok).
+inline bool bwd_dv_ok(bool bf16, int64_t P, int dv) {
+    return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
+}
+// LDS bytes a pass block needs; 0 if it does not fit one CU.
+size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad);
+hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t stream, const LaunchEvents &ev);
+
+// The per-token partial sums the passes leave, (batch, nheads, Lp, parts).
+struct BwdTokens {
+    const float *xq, *xqi, *dyx;  // dx pass: nq parts (its column tiles)
+    const float *cdi;             // dC pass: nc parts
+    const double *wcol;           // dB pass: 1 part
+    const double *wrow;           // dB pass: nw = chunk / 32 parts
+    int nq, nc, nw;
+};
+hipError_t launch_bwd_tokens(const Problem &p, const BwdTokens &tk, const float *DT, const float *Zp,
+                             const float *A, float *ddt, float *dap, float *ddp, hipStream_t stream,
+                             const LaunchEvents &ev);
+hipError_t launch_bwd_reduce(const Problem &p, const float *dbp, const float *dcp, int nhb, float *dB, float *dC,
+                             const float *dap, const float *ddp, float *dA, float *dD, hipStream_t stream,
+                             const LaunchEvents &ev);
 
 }  // namespace ssd

@@ -123,3 +123,17 @@ def small(name: str = "small", dtype: str = "f32", batch=1, seqlen=64, nheads=2,
     """A small workload for tests (same distributions, any shape)."""
     return Workload(name, dtype, batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
                     dt_mu=dt_mu, init_std=init_std, seed=seed)
+
+
+def cotangents(w: Workload, seed: int | None = None, final: bool = True) -> dict:
+    """Seeded upstream gradients for the backward pass of workload ``w``:
+    dy ~ N(0, 1) (b, L, nh, p) in the workload's storage dtype (bf16-rounded
+    for bf16 workloads) and, when ``final``, dfinal ~ N(0, 1) (b, nh, p, n)
+    float32.  Drawn from ``default_rng(seed or w.seed + 500)`` in that order."""
+    rng = np.random.default_rng(w.seed + 500 if seed is None else seed)
+    b, L, nh, p, n = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    dy = rng.standard_normal((b, L, nh, p), dtype=np.float32)
+    if w.dtype == "bf16":
+        dy = round_bf16(dy)
+    dfin = rng.standard_normal((b, nh, p, n), dtype=np.float32) if final else None
+    return dict(dy=dy, dfinal=dfin)

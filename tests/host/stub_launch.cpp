@@ -9,12 +9,13 @@
 #include "../../mamba_chunked_ssd_amd/csrc/ssd_internal.h"
 
 std::atomic<long> g_launches[5];  // calls per stage (4: the decode step)
+std::atomic<long> g_bwd_launches;  // backward-only kernels
 std::atomic<long> g_event_records;
 
 namespace ssd {
 
 hipError_t launch_chunk_cumsum(const Problem &, const void *, const float *, G2Pair, float *, float *,
-                               hipStream_t, const LaunchEvents &) {
+                               hipStream_t, const LaunchEvents &, float *) {
     g_launches[0]++;
     return hipSuccess;
 }
@@ -47,6 +48,42 @@ hipError_t launch_chunk_out(const Problem &, const Plan &, const void *, const v
                             const float *, G2View, const float *, const float *, const float *, void *,
                             hipStream_t, const LaunchEvents &) {
     g_launches[3]++;
+    return hipSuccess;
+}
+
+hipError_t launch_bwd_scores(const Problem &, const void *, const void *, float *, hipStream_t,
+                             const LaunchEvents &) {
+    g_bwd_launches++;
+    return hipSuccess;
+}
+hipError_t launch_bwd_carry(const Problem &, const float *, const void *, G2View, const float *, void *, float *,
+                            float *, hipStream_t, const LaunchEvents &) {
+    g_bwd_launches++;
+    return hipSuccess;
+}
+// the LDS rule of the pass kernels: tables, K (passes 1, 2), V, state tile
+size_t bwd_pass_lds(const Problem &p, int pass, int dv, int pad) {
+    const int64_t esz = p.bf16 ? 2 : 4;
+    const int64_t T = p.chunk, P = p.headdim;
+    int64_t bytes = 12 * T;
+    if (pass != 0) bytes += T * (P + pad) * esz;
+    bytes += T * (dv + pad) * esz;
+    const int64_t erow = pass == 0 ? (p.dstate + 31) / 32 * 32 + pad : dv + pad;
+    bytes += (pass == 0 ? dv : P) * erow * 4;
+    return bytes <= (int64_t)kLdsPerCu ? (size_t)bytes : 0;
+}
+hipError_t launch_bwd_pass(const Problem &, const BwdPassLaunch &, hipStream_t, const LaunchEvents &) {
+    g_bwd_launches++;
+    return hipSuccess;
+}
+hipError_t launch_bwd_tokens(const Problem &, const BwdTokens &, const float *, const float *, const float *, float *,
+                             float *, float *, hipStream_t, const LaunchEvents &) {
+    g_bwd_launches++;
+    return hipSuccess;
+}
+hipError_t launch_bwd_reduce(const Problem &, const float *, const float *, int, float *, float *, const float *,
+                             const float *, float *, float *, hipStream_t, const LaunchEvents &) {
+    g_bwd_launches++;
     return hipSuccess;
 }
 

@@ -1,5 +1,5 @@
-"""The C ABI's host code (ssd_api.cpp: validation, workspace layout, launch
-plans, stage order) built with AddressSanitizer + UndefinedBehaviorSanitizer
+"""The C ABI's host code (ssd_api.cpp and ssd_bwd.cpp: validation, workspace
+layout, launch plans, stage order) built with AddressSanitizer + UndefinedBehaviorSanitizer
 and, separately, with ThreadSanitizer, against stub launchers that enqueue
 nothing (tests/host/stub_launch.cpp), and driven through every validation
 path and from eight threads at once (tests/host/abi_driver.cpp).  Plain g++,
@@ -14,6 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = [os.path.join(ROOT, "mamba_chunked_ssd_amd", "csrc", "ssd_api.cpp"),
+           os.path.join(ROOT, "mamba_chunked_ssd_amd", "csrc", "ssd_bwd.cpp"),
            os.path.join(ROOT, "tests", "host", "stub_launch.cpp"),
            os.path.join(ROOT, "tests", "host", "abi_driver.cpp")]
 ROCM_INCLUDE = "/opt/rocm/include"
