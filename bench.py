@@ -11,7 +11,10 @@ Prints ONE JSON line: tokens/s over K back-to-back steps (nothing else on the
 stream), per-stage kernel times from a second run of K steps in which every
 kernel's dispatch records a (start, stop) HIP event pair, the roofline of the
 dominant kernel, and the fp64 CPU oracle timed on this host as a reference
-baseline.
+baseline.  Beside the forward's figures the line carries the recurrent decode
+step ("decode") and the backward pass ("backward": ssd_chunk_scan_bwd on the
+same workload with seeded upstream gradients, its stages and the roofline of
+its slowest stage).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -230,6 +233,118 @@ def decode_bench(hip, w, batch, dev, steps=20, warmup=5) -> dict:
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts}}
 
 
+def bwd_stage_model(w) -> dict:
+    """Algorithmic (HBM bytes, flops) of each backward stage at workload ``w``:
+    each input read once, each output and intermediate written once and read
+    once by the stage that consumes it; MFMA flops of the contractions the
+    method needs (the masked triangles counted as T (T + 16) / 2 of T x T, the
+    16 x 16 blocks on the diagonal included), not of the bf16 term splits."""
+    B, L, NH, P, N, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    e = 2 if w.dtype == "bf16" else 4
+    NC = -(-L // T)
+    Lp = NC * T
+    tok_h = B * L * NH
+    seq = 4 * B * NH * Lp
+    states = 4 * B * NH * NC * P * N
+    tri = T * (T + 16) / 2
+    units = B * NC * NH
+    bc = B * L * G * N * e
+    x = tok_h * P * e
+    init = 4 * B * NH * P * N if w.init_std > 0 else 0
+    ntile = (T // 16) * (T // 16 + 1) // 2
+    st = 4 * B * NC * G * ntile * 256
+    m = {}
+    m["chunk_cumsum"] = (tok_h * e + 5 * seq, 0.0)
+    m["chunk_state"] = (x + bc + seq + states, 2.0 * B * L * NH * N * P)
+    m["state_pass"] = (2 * states + seq / T + init, 0.0)
+    m["adjoint_chunk_state"] = (x + bc + seq + states, 2.0 * B * L * NH * N * P)
+    m["adjoint_carry"] = (3 * states + 4 * B * NH * P * N, 0.0)
+    m["score_tiles"] = (2 * bc + st, 2.0 * B * NC * G * tri * N)
+    m["dx_pass"] = (st + 2 * x + bc + states + 4 * tok_h * P + 3 * 4 * tok_h, 2.0 * units * (tri * P + T * N * P))
+    bwd_bc = 2.0 * units * (tri * P + tri * N + T * P * N)
+    m["dB_pass"] = (2 * x + bc + states + 4 * B * L * G * N, bwd_bc)
+    m["dC_pass"] = (2 * x + 2 * bc + states + 4 * B * L * G * N + 4 * tok_h, bwd_bc)
+    m["w_sums"] = (2 * x + st + 8 * tok_h * (1 + T // 32), 2.0 * units * tri * P)
+    m["token_finish"] = (4 * 4 * tok_h + 8 * tok_h * (1 + T // 32) + 4 * tok_h, 0.0)
+    m["reduce"] = (2 * 4 * B * L * G * N * 2, 0.0)
+    return m
+
+
+def backward_bench(hip, w, inp, t, dev, steps=10, warmup=3) -> dict:
+    """ssd_chunk_scan_bwd at workload ``w`` with seeded upstream gradients:
+    the whole call timed back to back (tokens/s), each stage from its kernel's
+    own events (median over the steps), and the roofline of the slowest
+    stage against the algorithmic model of ``bwd_stage_model``."""
+    import numpy as np
+    import torch
+
+    import mamba_chunked_ssd_amd as ssd
+    import ssd_inputs as si
+
+    cot = si.cotangents(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dy = torch.from_numpy(cot["dy"]).to(dev).to(tdt)
+    dfin = torch.from_numpy(cot["dfinal"]).to(dev)
+    shape = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype)
+    ws = torch.empty(ssd.bwd_workspace_size(shape, w.chunk_size), dtype=torch.uint8, device=dev)
+    names = ssd.BWD_STAGES
+
+    def call(events=None):
+        return ssd.chunk_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], dy, chunk_size=w.chunk_size,
+                                  initial_states=t["h0"], d_final_states=dfin, workspace=ws, events=events)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    for _ in range(steps):
+        call()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    hip.lib.hipEventSynchronize(ctypes.c_void_p(e1))
+    total_us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    evs = [[hip.event() for _ in range(2 * len(names))] for _ in range(steps)]
+    for k in range(steps):
+        call(evs[k])
+    torch.cuda.synchronize()
+    per = {n: float(np.median([hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for ev in evs])) * 1e3
+           for i, n in enumerate(names)}
+    for ev in evs:
+        for e_ in ev:
+            hip.destroy(e_)
+    model = bwd_stage_model(w)
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    stages = {}
+    for n in names:
+        byts, flops = model[n]
+        us = per[n]
+        floor = max(byts / (PEAK_HBM_GBS * 1e9), flops / (peak_tf * 1e12))
+        stages[n] = {"us": round(us, 2), "roofline_frac": round(floor / (us * 1e-6), 4) if us > 0 else None}
+    dom = max(names, key=lambda n: per[n])
+    byts, flops = model[dom]
+    hbm_t, mfma_t = byts / (PEAK_HBM_GBS * 1e9), flops / (peak_tf * 1e12)
+    bound = "mfma" if mfma_t >= hbm_t else "hbm"
+    t_dom = per[dom] * 1e-6
+    achieved = flops / t_dom / 1e12 if bound == "mfma" else byts / t_dom / 1e9
+    peak = peak_tf if bound == "mfma" else PEAK_HBM_GBS
+    return {
+        "workload": w.name,
+        "metric": "SSD bwd tokens/s at 1 MI355X",
+        "value": round(w.tokens / (total_us * 1e-6), 1),
+        "unit": "tokens/s",
+        "us_per_step": round(total_us, 2),
+        "steps": steps,
+        "stages": stages,
+        "dominant": dom,
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(achieved / peak, 4),
+                     "flops": flops, "bytes": byts, "traffic": None,
+                     "model": "bwd_stage_model: algorithmic flops of the dominant stage's contractions"},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +364,8 @@ def main(argv=None):
                          "plan ssd_chunk_scan_fwd_tune picks (tuned before the warm-up, untimed)")
     ap.add_argument("--fused-cols", type=int, default=64,
                     help="dstate columns per fused-state block (32 or 64)")
+    ap.add_argument("--bwd-steps", type=int, default=10,
+                    help="timed steps of the backward pass (0: skip it)")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="batch of the recurrent decode-step measurement (0: skip it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -452,6 +569,9 @@ def main(argv=None):
 
     if a.decode_batch > 0:
         out["decode"] = decode_bench(hip, w, a.decode_batch, dev)
+
+    if a.bwd_steps > 0:
+        out["backward"] = backward_bench(hip, w, inp, t, dev, steps=a.bwd_steps)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps, a.cpu_seconds)
