@@ -51,7 +51,11 @@
 // stages K, V and the state Hm into LDS; Q fragments come straight from
 // memory into registers.  For a strip and a pair of key strips the scores
 // arrive in the MFMA output layout (lane = row, four keys per lane), are
-// decayed, masked (select before exp2) and split into bf16 terms, and feed the
+// decayed (on the diagonal tile from exact exponents, masked by a select
+// before exp2; off it as a product of three factors, each at most 1: the
+// row's decay to its strip's end, the decay between the two strips' near
+// ends, and the key's decay to its strip's end, a per-head table) and split
+// into bf16 terms, and feed the
 // next MFMA directly as its A operand, with the k index relabelled to match:
 // the V rows for that relabelling come from transposing LDS reads.  The state
 // term is one more MFMA chain per strip.
@@ -99,12 +103,12 @@ struct PassArgs {
     int krow, vrow, erow;           // LDS row strides (elements)
 };
 
-// LDS bytes of one block: tables (G2 hi, G2 lo, dt), K (passes B and C) and V
+// LDS bytes of one block: tables (G2 hi, G2 lo, dt, key factors), K (passes B and C) and V
 // in the input element type, the state tile as two bf16 planes or one fp32.
 __host__ __device__ inline int kb_lds_bytes(int pass, bool f32_in, int T, int P, int N, int DV, int krow,
                                             int vrow, int erow) {
     const int esz = f32_in ? 4 : 2;
-    int bytes = 12 * T;
+    int bytes = 16 * T;  // G2 hi, G2 lo, dt, key factors
     if (pass != kPassQ) bytes += T * krow * esz;
     if (pass == kPassW) return bytes;
     bytes += T * vrow * esz;
@@ -119,7 +123,7 @@ struct Frag {
     u32x4 t[NT];
 };
 
-// split 8 floats into NT (2 or 3) bf16 terms
+// split 8 floats into NT (1, 2 or 3) bf16 terms
 template <int NT>
 __device__ __forceinline__ Frag<NT> split8(const float (&v)[8]) {
     Frag<NT> f;
@@ -173,7 +177,9 @@ struct Io;
 template <>
 struct Io<uint16_t> {
     static constexpr int NI = 1;  // terms of an input value (exact)
-    static constexpr int NF = 2;  // terms of an fp32-valued operand
+    static constexpr int NF = 2;  // terms of an fp32-valued state operand
+    static constexpr int NP = 2;  // terms of a decayed score (one bf16 term gives dx errors of several
+                                  // per cent of its rms: too coarse)
     typedef uint16_t Lds;
     // 8 consecutive inputs from memory
     __device__ static Frag<1> load8(const uint16_t *p) { return Frag<1>{{*reinterpret_cast<const u32x4 *>(p)}}; }
@@ -201,6 +207,7 @@ template <>
 struct Io<float> {
     static constexpr int NI = 3;
     static constexpr int NF = 3;
+    static constexpr int NP = 3;
     typedef float Lds;
     __device__ static Frag<3> load8(const float *p) {
         const floatx4 a = *reinterpret_cast<const floatx4 *>(p), b = *reinterpret_cast<const floatx4 *>(p + 4);
@@ -229,6 +236,25 @@ struct Io<float> {
         return split8<3>(v);
     }
 };
+
+// Sum over the 16 lanes of each row of the wave (lanes 16 q .. 16 q + 15),
+// every lane receiving its row's sum, with DPP lane moves (VALU) rather than
+// LDS-crossbar shuffles: row mirror, half-row mirror, then the two quad
+// exchanges reach all 16 lanes.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // row_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    return v;
+}
+__device__ __forceinline__ double row16_sum(double v) {
+    v += dpp_move_f64<0x140, 0xf>(v);
+    v += dpp_move_f64<0x141, 0xf>(v);
+    v += dpp_move_f64<0xb1, 0xf>(v);
+    v += dpp_move_f64<0x4e, 0xf>(v);
+    return v;
+}
 
 // rows [0, nrows) x cols [0, ncols) (ncols % 8 == 0) of a row-major source
 // (row stride src_ld elements) into an LDS array of row stride `ld`, element
@@ -267,12 +293,13 @@ template <typename In, int NKQ, int DV, int PASS>
 __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
     typedef Io<In> IO;
     typedef typename IO::Lds L;
-    constexpr int NI = IO::NI, NF = IO::NF;
+    constexpr int NI = IO::NI, NF = IO::NF, NP = IO::NP;
     constexpr int NCT = DV / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     const int T = a.T, n = T / 16;
     const int tid = threadIdx.x, nthr = 2 * T;
-    const int w = tid >> 6, l = tid & 63, g4 = l >> 4, l16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so strip logic stays scalar
+    const int l = tid & 63, g4 = l >> 4, l16 = l & 15;
 
     int64_t u = blockIdx.x;
     const int vt = (int)(u % a.nvt);
@@ -291,7 +318,8 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
     float *g2h = reinterpret_cast<float *>(lds);
     float *g2l = g2h + T;
     float *dtt = g2l + T;
-    L *KS = reinterpret_cast<L *>(dtt + T);
+    float *kft = dtt + T;  // key factors of the off-diagonal tiles (see below)
+    L *KS = reinterpret_cast<L *>(kft + T);
     L *VS = KS + (PASS == kPassQ ? 0 : T * a.krow);
     unsigned char *ES = reinterpret_cast<unsigned char *>(VS + T * a.vrow);
     const int erows = PASS == kPassQ ? DV : a.P;
@@ -324,9 +352,20 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
         __syncthreads();  // the previous head's reads of LDS are done
         for (int t = tid; t < T; t += nthr) {
             const int64_t gi = bh * a.Lp + t0 + t;
-            g2h[t] = a.G2hi[gi];
-            g2l[t] = a.G2lo[gi];
-            dtt[t] = a.DT[gi];
+            const float gh = a.G2hi[gi], gl = a.G2lo[gi], d = a.DT[gi];
+            g2h[t] = gh;
+            g2l[t] = gl;
+            dtt[t] = d;
+            // decay between token t and the near end of its 16-token strip:
+            // exp2(G2_t - G2_start) for the passes whose keys follow the row,
+            // exp2(G2_end - G2_t) dt_t for pass C, whose keys precede it (<= 1)
+            if constexpr (PASS == kPassC) {
+                const int64_t ai = gi - (t & 15) + 15;
+                kft[t] = fast_exp2((a.G2hi[ai] - gh) + (a.G2lo[ai] - gl)) * d;
+            } else {
+                const int64_t ai = gi - (t & 15);
+                kft[t] = fast_exp2((gh - a.G2hi[ai]) + (gl - a.G2lo[ai]));
+            }
         }
         const int64_t rowbase = ((int64_t)b * a.seqlen + t0) * NHP + (int64_t)h * a.P;  // token t0, head h
         const unsigned char *sbase =
@@ -349,25 +388,31 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
         // pass W: sums of W[s][r] over this wave's rows r, for the keys
         // s = 16 J + 4 g4 + i of key strip J = l16
         double colacc[4] = {0.0, 0.0, 0.0, 0.0};
+
+        // 1. per strip: Q fragments (rows 16 I + l16, 32 kk + 8 g4 ..), the
+        //    row's decay tables, and the state term, which starts O
+        Frag<NI> qf[2][NKQ];
+        floatx4 O[2][NCT];  // the state term first, then the chunk's own tokens on top
+        float grh[2], grl[2], rfac[2];
+        double rowacc[2] = {0.0, 0.0};  // pass W: sums over this lane's keys s of W[s][r]
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int I = strips[k];
             const int r = 16 * I + l16;  // this lane's row for the score / A-operand layout
-            // Q fragments of the strip (passes B, C): rows 16 I + l16, 32 kk + 8 g4 ..
-            Frag<NI> qf[NKQ];
             if constexpr (PASS != kPassQ) {
                 const In *qsrc = (PASS == kPassC ? dyin : xin) + rowbase + (int64_t)r * NHP + 8 * g4;
 #pragma unroll
                 for (int kk = 0; kk < NKQ; ++kk) {
 #pragma unroll
-                    for (int j = 0; j < NI; ++j) qf[kk].t[j] = u32x4{0u, 0u, 0u, 0u};
-                    if (r < vrows) qf[kk] = IO::load8(qsrc + 32 * kk);
+                    for (int j = 0; j < NI; ++j) qf[k][kk].t[j] = u32x4{0u, 0u, 0u, 0u};
+                    if (r < vrows) qf[k][kk] = IO::load8(qsrc + 32 * kk);
                 }
             }
-            floatx4 O[NCT];  // the state term first, then the chunk's own tokens on top
-            const float grh = g2h[r], grl = g2l[r];
-            double rowacc = 0.0;  // pass W: sum over this lane's keys s of W[s][r]
-
+            grh[k] = g2h[r];
+            grl[k] = g2l[r];
+            // decay between this lane's row and the near end of its strip (<= 1)
+            rfac[k] = PASS == kPassC ? fast_exp2((grh[k] - g2h[16 * I]) + (grl[k] - g2l[16 * I]))
+                                     : fast_exp2((g2h[16 * I + 15] - grh[k]) + (g2l[16 * I + 15] - grl[k]));
             if constexpr (PASS != kPassW) {
                 // state term: Oi = Q Hm^T, scaled per row by exp2(e_r)
                 floatx4 Oi[NCT];
@@ -393,7 +438,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
 #pragma unroll
                         for (int ct = 0; ct < NCT; ++ct) {
                             const Frag<NF> ef = IO::scol8(ES, a.erow, erows, 32 * kk, 16 * ct, g4, l16);
-                            Oi[ct] = mmf<NI, NF>(qf[kk], ef, Oi[ct]);
+                            Oi[ct] = mmf<NI, NF>(qf[k][kk], ef, Oi[ct]);
                         }
                     }
                 }
@@ -410,7 +455,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) O[ct][i] = rf[i] * Oi[ct][i];
+                    for (int i = 0; i < 4; ++i) O[k][ct][i] = rf[i] * Oi[ct][i];
                 if constexpr (PASS == kPassQ) {
                     // x_r . (state term of q_r) over this tile's columns
                     float xs[4];
@@ -421,11 +466,10 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                         if (ro < vrows) {
 #pragma unroll
                             for (int ct = 0; ct < NCT; ++ct)
-                                xs[i] = fmaf(IO::load1(xin + rowbase + (int64_t)ro * NHP + vt * DV + 16 * ct + l16), O[ct][i],
+                                xs[i] = fmaf(IO::load1(xin + rowbase + (int64_t)ro * NHP + vt * DV + 16 * ct + l16), O[k][ct][i],
                                              xs[i]);
                         }
-#pragma unroll
-                        for (int off = 8; off > 0; off >>= 1) xs[i] += __shfl_xor(xs[i], off, 16);
+                        xs[i] = row16_sum(xs[i]);
                     }
                     if (l16 == 0) {
 #pragma unroll
@@ -442,10 +486,9 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                         if (ro < vrows) {
                             const In *crow = Cin + (((int64_t)b * a.seqlen + t0 + ro) * a.G + g) * a.N + vt * DV + l16;
 #pragma unroll
-                            for (int ct = 0; ct < NCT; ++ct) cd[i] = fmaf(IO::load1(crow + 16 * ct), O[ct][i], cd[i]);
+                            for (int ct = 0; ct < NCT; ++ct) cd[i] = fmaf(IO::load1(crow + 16 * ct), O[k][ct][i], cd[i]);
                         }
-#pragma unroll
-                        for (int off = 8; off > 0; off >>= 1) cd[i] += __shfl_xor(cd[i], off, 16);
+                        cd[i] = row16_sum(cd[i]);
                     }
                     if (l16 == 0) {
 #pragma unroll
@@ -453,9 +496,35 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                     }
                 }
             }
-            const int jlo = PASS == kPassC ? 0 : (I & ~1);
-            const int jhi = PASS == kPassC ? (I & ~1) : n - 2;  // inclusive, even
-            for (int J0 = jlo; J0 <= jhi; J0 += 2) {
+        }
+
+        // 2. the key-strip pairs, each pair's K and V fragments read once for
+        //    both row strips of the wave
+        const int I0 = strips[0], I1 = strips[1];  // I0 < I1
+        const int jlo = PASS == kPassC ? 0 : (I0 & ~1);
+        const int jhi = PASS == kPassC ? (I1 & ~1) : n - 2;  // inclusive, even
+        const int64_t stb = (((int64_t)b * a.NC + c) * a.G + g) * (int64_t)(n * (n + 1) / 2);
+        for (int J0 = jlo; J0 <= jhi; J0 += 2) {
+            // the pair's V fragments and (bf16) K fragments of its two key
+            // strips, read once for both strips of the wave
+            Frag<NI> vf[NCT];
+            if constexpr (PASS != kPassW) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) vf[ct] = IO::col8(VS, a.vrow, 16 * J0, 16 * J0 + 16, 16 * ct, g4, l16);
+            }
+            Frag<NI> kfr[2][NKQ];
+            if constexpr (PASS != kPassQ && NI == 1) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int kk = 0; kk < NKQ; ++kk)
+                        kfr[jj][kk] = IO::row8(KS + (16 * (J0 + jj) + l16) * a.krow + 32 * kk + 8 * g4);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int I = strips[k];
+                if (PASS == kPassC ? (J0 > (I & ~1)) : (J0 + 1 < I)) continue;  // no live key strip
+                const int r = 16 * I + l16;
                 float pv[8];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
@@ -465,78 +534,99 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                     if (live) {
                         if constexpr (PASS == kPassQ) {
                             const int tile = I * n - (I * (I - 1)) / 2 + (J - I);
-                            const int64_t tb = (((int64_t)b * a.NC + c) * a.G + g) * (int64_t)(n * (n + 1) / 2) + tile;
-                            S = *reinterpret_cast<const floatx4 *>(a.ST + (tb * 64 + l) * 4);
+                            S = *reinterpret_cast<const floatx4 *>(a.ST + ((stb + tile) * 64 + l) * 4);
                         } else {
 #pragma unroll
                             for (int kk = 0; kk < NKQ; ++kk) {
-                                const Frag<NI> kf = IO::row8(KS + (16 * J + l16) * a.krow + 32 * kk + 8 * g4);
-                                S = mmf<NI, NI>(kf, qf[kk], S);
+                                if constexpr (NI == 1) {
+                                    S = mmf<NI, NI>(kfr[jj][kk], qf[k][kk], S);
+                                } else {
+                                    const Frag<NI> kf = IO::row8(KS + (16 * J + l16) * a.krow + 32 * kk + 8 * g4);
+                                    S = mmf<NI, NI>(kf, qf[k][kk], S);
+                                }
                             }
                         }
                     }
+                    if (J == I) {
+                        // the diagonal tile: exact exponents, masked (select before exp2)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * J + 4 * g4 + i;
-                        float e;
-                        bool ok;
-                        if constexpr (PASS == kPassC) {
-                            ok = live && s <= r;
-                            e = (grh - g2h[s]) + (grl - g2l[s]);
-                        } else {
-                            ok = live && s >= r;
-                            e = (g2h[s] - grh) + (g2l[s] - grl);
+                        for (int i = 0; i < 4; ++i) {
+                            const int s_ = 16 * J + 4 * g4 + i;
+                            float e;
+                            bool ok;
+                            if constexpr (PASS == kPassC) {
+                                ok = s_ <= r;
+                                e = (grh[k] - g2h[s_]) + (grl[k] - g2l[s_]);
+                            } else {
+                                ok = s_ >= r;
+                                e = (g2h[s_] - grh[k]) + (g2l[s_] - grl[k]);
+                            }
+                            float v = S[i] * fast_exp2(ok ? e : -INFINITY);
+                            if constexpr (PASS == kPassC) v *= dtt[s_];
+                            pv[4 * jj + i] = v;
                         }
-                        float v = S[i] * fast_exp2(ok ? e : -INFINITY);
-                        if constexpr (PASS == kPassC) v *= dtt[s];
-                        pv[4 * jj + i] = v;
+                    } else if (live) {
+                        // off the diagonal every key is live and the decay factors
+                        // through the strips' near ends, each factor <= 1: the row's
+                        // to its strip end, strip end to strip end, and the key's
+                        // (table) -- two products per entry
+                        float se;
+                        if constexpr (PASS == kPassC)
+                            se = (g2h[16 * I] - g2h[16 * J + 15]) + (g2l[16 * I] - g2l[16 * J + 15]);
+                        else
+                            se = (g2h[16 * J] - g2h[16 * I + 15]) + (g2l[16 * J] - g2l[16 * I + 15]);
+                        const float rowj = rfac[k] * fast_exp2(se);
+                        const floatx4 kv = *reinterpret_cast<const floatx4 *>(kft + 16 * J + 4 * g4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pv[4 * jj + i] = S[i] * rowj * kv[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pv[4 * jj + i] = 0.f;
                     }
                     if constexpr (PASS == kPassW) {
                         if (live) {
                             // W[s][r] = (x_r . dy_s) exp2(G2_s - G2_r) (B_r . C_s) dt_r for this
                             // lane's row r and keys s = 16 J + 4 g4 + i: sums over s stay in
                             // the lane, sums over the strip's 16 rows go to lane l16 = J
-                            const int tile = I * n - (I * (I - 1)) / 2 + (J - I);
-                            const int64_t tb =
-                                (((int64_t)b * a.NC + c) * a.G + g) * (int64_t)(n * (n + 1) / 2) + tile;
-                            const floatx4 sc = *reinterpret_cast<const floatx4 *>(a.ST + (tb * 64 + l) * 4);
                             // (entries in fp32, their sums in fp64: the row and column
                             // sums are differenced later, where fp32 sums lose digits)
+                            const int tile = I * n - (I * (I - 1)) / 2 + (J - I);
+                            const floatx4 sc = *reinterpret_cast<const floatx4 *>(a.ST + ((stb + tile) * 64 + l) * 4);
                             const float dtr = dtt[r];
                             double wv[4];
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 wv[i] = (double)(pv[4 * jj + i] * sc[i] * dtr);
-                                rowacc += wv[i];
+                                rowacc[k] += wv[i];
                             }
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                                for (int off = 8; off > 0; off >>= 1) wv[i] += __shfl_xor(wv[i], off, 16);
+                            for (int i = 0; i < 4; ++i) wv[i] = row16_sum(wv[i]);
 #pragma unroll
                             for (int i = 0; i < 4; ++i) colacc[i] += (l16 == J) ? wv[i] : 0.0;
                         }
                     }
                 }
                 if constexpr (PASS != kPassW) {
-                    const Frag<NF> pf = split8<NF>(pv);
+                    const Frag<NP> pf = split8<NP>(pv);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        const Frag<NI> vf = IO::col8(VS, a.vrow, 16 * J0, 16 * J0 + 16, 16 * ct, g4, l16);
-                        O[ct] = mmf<NF, NI>(pf, vf, O[ct]);
-                    }
+                    for (int ct = 0; ct < NCT; ++ct) O[k][ct] = mmf<NP, NI>(pf, vf[ct], O[k][ct]);
                 }
             }
+        }
+
+        // 3. per strip: outputs
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int I = strips[k];
+            const int r = 16 * I + l16;
             if constexpr (PASS == kPassW) {
                 // sum over s of W[s][r] (W's column r): this lane's keys, then
                 // the 4 lane groups
-                rowacc += __shfl_xor(rowacc, 16, 64);
-                rowacc += __shfl_xor(rowacc, 32, 64);
-                if (g4 == 0) a.wcol[bh * a.Lp + t0 + r] = rowacc;
-                continue;
-            }
-
-            if constexpr (PASS == kPassQ) {
+                double ra = rowacc[k];
+                ra += __shfl_xor(ra, 16, 64);
+                ra += __shfl_xor(ra, 32, 64);
+                if (g4 == 0) a.wcol[bh * a.Lp + t0 + r] = ra;
+            } else if constexpr (PASS == kPassQ) {
                 float xq[4], dyx[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -548,7 +638,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
 #pragma unroll
                         for (int ct = 0; ct < NCT; ++ct) {
                             const int64_t e = rowbase + (int64_t)ro * NHP + vt * DV + 16 * ct + l16;
-                            const float q = O[ct][i];
+                            const float q = O[k][ct][i];
                             const float xv = IO::load1(xin + e), dv = IO::load1(dyin + e);
                             a.out[e] = fmaf(dtv, q, Dh * dv);
                             xq[i] = fmaf(xv, q, xq[i]);
@@ -558,11 +648,8 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                    for (int off = 8; off > 0; off >>= 1) {
-                        xq[i] += __shfl_xor(xq[i], off, 16);
-                        dyx[i] += __shfl_xor(dyx[i], off, 16);
-                    }
+                    xq[i] = row16_sum(xq[i]);
+                    dyx[i] = row16_sum(dyx[i]);
                 }
                 if (l16 == 0) {
 #pragma unroll
@@ -578,7 +665,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const float sc = PASS == kPassB ? dtt[16 * I + 4 * g4 + i] : 1.f;
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) acc[k][ct][i] = fmaf(sc, O[ct][i], acc[k][ct][i]);
+                    for (int ct = 0; ct < NCT; ++ct) acc[k][ct][i] = fmaf(sc, O[k][ct][i], acc[k][ct][i]);
                 }
             }
         }
