@@ -177,15 +177,25 @@ struct TokParts {
     int nq, nc, nw;
 };
 
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ double wave_prefix(double v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
+// inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (the
+// pattern of the cumsum's wave scan): shifts by 1, 2, 4, 8 within rows, then
+// row 0's total into rows 1 and 3... by the two row broadcasts
+__device__ __forceinline__ double wave_prefix(double v) {
+    v += dpp_move_f64<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_move_f64<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_move_f64<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_move_f64<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_move_f64<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+    v += dpp_move_f64<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
     return v;
 }
+__device__ __forceinline__ double lane63(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum(double v) { return lane63(wave_prefix(v)); }
 
 template <int E>
 __global__ __launch_bounds__(256) void kb_tokens(TokParts tp, const float *__restrict__ DT,
@@ -229,12 +239,11 @@ __global__ __launch_bounds__(256) void kb_tokens(TokParts tp, const float *__res
         lpre += pre[e];
     }
     // sums over the lanes after (suffix terms) and before (prefix terms) this one
-    const double isuf = wave_prefix(lsuf, lane), ipre = wave_prefix(lpre, lane);
-    const double tsuf = __shfl(isuf, 63, 64);
+    const double isuf = wave_prefix(lsuf), ipre = wave_prefix(lpre);
+    const double tsuf = lane63(isuf);
     double z = 0.0;
     for (int k = lane; k < nzw; k += 64) z += (double)Zp[(bh * NC + c) * nzw + k];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+    z = wave_sum(z);
     double sacc = tsuf - isuf;  // suffix from the later lanes
     double pacc = ipre - lpre;  // prefix from the earlier lanes
     double da[E];
@@ -256,11 +265,8 @@ __global__ __launch_bounds__(256) void kb_tokens(TokParts tp, const float *__res
         if (t < seqlen) ddt[(b * seqlen + t) * NH + h] = (float)(xqv[e] + (double)Ah * da[e]);
         da_sum += dtv[e] * da[e];
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        da_sum += __shfl_xor(da_sum, off, 64);
-        dyx += __shfl_xor(dyx, off, 64);
-    }
+    da_sum = wave_sum(da_sum);
+    dyx = wave_sum(dyx);
     if (lane == 0) {
         dap[wv] = (float)da_sum;
         ddp[wv] = (float)dyx;
