@@ -101,12 +101,14 @@ struct PassArgs {
     int64_t seqlen, Lp;
     int batch, NH, P, N, G, HPG, T, NC, hb, nhb, nvt;
     int krow, vrow, erow;           // LDS row strides (elements)
+    int xt_lds;                     // pass Q: x tile, pass C: C tile staged in LDS (else read from memory)
 };
 
 // LDS bytes of one block: tables (G2 hi, G2 lo, dt, key factors), K (passes B and C) and V
-// in the input element type, the state tile as two bf16 planes or one fp32.
+// in the input element type, the state tile as two bf16 planes or one fp32, and
+// (where it fits) the tile the epilogue reads beside O: x for pass Q, C for pass C.
 __host__ __device__ inline int kb_lds_bytes(int pass, bool f32_in, int T, int P, int N, int DV, int krow,
-                                            int vrow, int erow) {
+                                            int vrow, int erow, bool xt) {
     const int esz = f32_in ? 4 : 2;
     int bytes = 16 * T;  // G2 hi, G2 lo, dt, key factors
     if (pass != kPassQ) bytes += T * krow * esz;
@@ -114,6 +116,7 @@ __host__ __device__ inline int kb_lds_bytes(int pass, bool f32_in, int T, int P,
     bytes += T * vrow * esz;
     const int erows = pass == kPassQ ? DV : P;
     bytes += erows * erow * 4;
+    if (xt && (pass == kPassQ || pass == kPassC)) bytes += T * vrow * esz;  // the epilogue's x or C tile
     return bytes;
 }
 
@@ -289,6 +292,9 @@ __device__ __forceinline__ void stage_state(unsigned char *st, int ld, const voi
     }
 }
 
+__device__ __forceinline__ float lds1(const uint16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float lds1(const float *p) { return *p; }
+
 template <typename In, int NKQ, int DV, int PASS>
 __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
     typedef Io<In> IO;
@@ -323,6 +329,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
     L *VS = KS + (PASS == kPassQ ? 0 : T * a.krow);
     unsigned char *ES = reinterpret_cast<unsigned char *>(VS + T * a.vrow);
     const int erows = PASS == kPassQ ? DV : a.P;
+    L *XS = reinterpret_cast<L *>(ES + erows * a.erow * 4);  // x (pass Q) or C (pass C) tile, if staged
 
     const In *xin = static_cast<const In *>(a.x);
     const In *dyin = static_cast<const In *>(a.dy);
@@ -337,6 +344,10 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
         const In *vsrc = (PASS == kPassB ? Cin : Bin) + ((int64_t)b * a.seqlen + t0) * GN + (int64_t)g * a.N +
                          (int64_t)vt * DV;
         stage_rows<L>(VS, a.vrow, reinterpret_cast<const L *>(vsrc), GN, T, vrows, DV, DV, tid, nthr);
+        if (PASS == kPassC && a.xt_lds) {
+            const In *csrc = Cin + ((int64_t)b * a.seqlen + t0) * GN + (int64_t)g * a.N + (int64_t)vt * DV;
+            stage_rows<L>(XS, a.vrow, reinterpret_cast<const L *>(csrc), GN, T, vrows, DV, DV, tid, nthr);
+        }
     }
 
     // strips of this wave and their (pass B, C) accumulators over the heads
@@ -373,6 +384,9 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
         if constexpr (PASS == kPassQ) {
             stage_rows<L>(VS, a.vrow, reinterpret_cast<const L *>(dyin + rowbase + vt * DV), NHP, T, vrows, DV, DV,
                           tid, nthr);
+            if (a.xt_lds)
+                stage_rows<L>(XS, a.vrow, reinterpret_cast<const L *>(xin + rowbase + vt * DV), NHP, T, vrows, DV, DV,
+                              tid, nthr);
             // E_c rows p of this dv-tile, all dstate columns (zero past dstate)
             stage_state<In>(ES, a.erow, sbase, a.P, a.N, vt * DV, DV, 0, (a.N + 31) & ~31, a.N, tid, nthr);
         } else {
@@ -466,7 +480,9 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                         if (ro < vrows) {
 #pragma unroll
                             for (int ct = 0; ct < NCT; ++ct)
-                                xs[i] = fmaf(IO::load1(xin + rowbase + (int64_t)ro * NHP + vt * DV + 16 * ct + l16), O[k][ct][i],
+                                xs[i] = fmaf(a.xt_lds ? lds1(XS + ro * a.vrow + 16 * ct + l16)
+                                                      : IO::load1(xin + rowbase + (int64_t)ro * NHP + vt * DV + 16 * ct + l16),
+                                             O[k][ct][i],
                                              xs[i]);
                         }
                         xs[i] = row16_sum(xs[i]);
@@ -486,7 +502,9 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                         if (ro < vrows) {
                             const In *crow = Cin + (((int64_t)b * a.seqlen + t0 + ro) * a.G + g) * a.N + vt * DV + l16;
 #pragma unroll
-                            for (int ct = 0; ct < NCT; ++ct) cd[i] = fmaf(IO::load1(crow + 16 * ct), O[k][ct][i], cd[i]);
+                            for (int ct = 0; ct < NCT; ++ct)
+                                cd[i] = fmaf(a.xt_lds ? lds1(XS + ro * a.vrow + 16 * ct + l16) : IO::load1(crow + 16 * ct),
+                                             O[k][ct][i], cd[i]);
                         }
                         cd[i] = row16_sum(cd[i]);
                     }
@@ -520,18 +538,18 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                     for (int kk = 0; kk < NKQ; ++kk)
                         kfr[jj][kk] = IO::row8(KS + (16 * (J0 + jj) + l16) * a.krow + 32 * kk + 8 * g4);
             }
+            // the scores of both strips first (or their tiles' loads, pass Q),
+            // so that one strip's MFMA latency hides behind the other's VALU work
+            floatx4 Sall[2][2];
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int I = strips[k];
-                if (PASS == kPassC ? (J0 > (I & ~1)) : (J0 + 1 < I)) continue;  // no live key strip
-                const int r = 16 * I + l16;
-                float pv[8];
+                const bool act = !(PASS == kPassC ? (J0 > (I & ~1)) : (J0 + 1 < I));
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     const int J = J0 + jj;
                     floatx4 S = zero4();
-                    const bool live = PASS == kPassC ? (J <= I) : (J >= I);
-                    if (live) {
+                    if (act && (PASS == kPassC ? (J <= I) : (J >= I))) {
                         if constexpr (PASS == kPassQ) {
                             const int tile = I * n - (I * (I - 1)) / 2 + (J - I);
                             S = *reinterpret_cast<const floatx4 *>(a.ST + ((stb + tile) * 64 + l) * 4);
@@ -547,6 +565,20 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                             }
                         }
                     }
+                    Sall[k][jj] = S;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int I = strips[k];
+                if (PASS == kPassC ? (J0 > (I & ~1)) : (J0 + 1 < I)) continue;  // no live key strip
+                const int r = 16 * I + l16;
+                float pv[8];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int J = J0 + jj;
+                    const floatx4 S = Sall[k][jj];
+                    const bool live = PASS == kPassC ? (J <= I) : (J >= I);
                     if (J == I) {
                         // the diagonal tile: exact exponents, masked (select before exp2)
 #pragma unroll
@@ -639,7 +671,8 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                         for (int ct = 0; ct < NCT; ++ct) {
                             const int64_t e = rowbase + (int64_t)ro * NHP + vt * DV + 16 * ct + l16;
                             const float q = O[k][ct][i];
-                            const float xv = IO::load1(xin + e), dv = IO::load1(dyin + e);
+                            const float xv = a.xt_lds ? lds1(XS + ro * a.vrow + 16 * ct + l16) : IO::load1(xin + e);
+                            const float dv = lds1(VS + ro * a.vrow + 16 * ct + l16);  // dy: pass Q's V tile
                             a.out[e] = fmaf(dtv, q, Dh * dv);
                             xq[i] = fmaf(xv, q, xq[i]);
                             dyx[i] = fmaf(dv, xv, dyx[i]);

@@ -27,17 +27,17 @@ void rows_for(const Problem &p, int pass, int dv, int pad, int *krow, int *vrow,
 
 }  // namespace bwd
 
-size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad) {
+size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad, bool xt) {
     int krow, vrow, erow;
     bwd::rows_for(p, pass, dv, lds_pad, &krow, &vrow, &erow);
-    const size_t bytes =
-        (size_t)bwd::kb_lds_bytes(pass, !p.bf16, (int)p.chunk, (int)p.headdim, (int)p.dstate, dv, krow, vrow, erow);
+    const size_t bytes = (size_t)bwd::kb_lds_bytes(pass, !p.bf16, (int)p.chunk, (int)p.headdim, (int)p.dstate, dv,
+                                                   krow, vrow, erow, xt);
     return bytes <= kLdsPerCu ? bytes : 0;
 }
 
 hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t stream, const LaunchEvents &ev) {
     using namespace bwd;
-    const size_t lds = bwd_pass_lds(p, L.pass, L.dv, L.lds_pad);
+    const size_t lds = bwd_pass_lds(p, L.pass, L.dv, L.lds_pad, L.xt_lds != 0);
     if (lds == 0) return hipErrorInvalidValue;
     const int64_t dvtot = L.pass == kPassQ ? p.headdim : L.pass == kPassW ? L.dv : p.dstate;
     if (L.dv <= 0 || dvtot % L.dv != 0 || L.hb < 1 || L.hb > p.heads_per_group) return hipErrorInvalidValue;
@@ -80,6 +80,7 @@ hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t
         a.nhb = (int)((p.heads_per_group + L.hb - 1) / L.hb);
     }
     rows_for(p, L.pass, L.dv, L.lds_pad, &a.krow, &a.vrow, &a.erow);
+    a.xt_lds = L.xt_lds ? 1 : 0;
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * a.nhb * a.nvt;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -30,6 +30,7 @@ enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3 };
 struct BwdPlan {
     int dvq, padq;    // dx pass: headdim columns per block, LDS row padding
     int dvbc, padbc;  // dB and dC passes: dstate columns per block, padding
+    bool xtq, xtc;    // dx pass: x tile, dC pass: C tile staged in LDS
     int hb, nhb;      // dB and dC passes: heads per block, runs of heads per group
     int nvtq;         // dx pass: column tiles (headdim / dvq)
 };
@@ -43,6 +44,7 @@ bool make_bwd_plan(const Problem &p, BwdPlan *out) {
     q.dvq = (int)std::min<int64_t>(p.headdim, 64);
     q.padq = bwd_pass_lds(p, kPassQ, q.dvq, 8) != 0 ? 8 : 0;
     if (bwd_pass_lds(p, kPassQ, q.dvq, q.padq) == 0) return false;
+    q.xtq = bwd_pass_lds(p, kPassQ, q.dvq, q.padq, true) != 0;
     q.nvtq = (int)(p.headdim / q.dvq);
     q.dvbc = 0;
     for (int dv : {64, 32, 16}) {
@@ -58,6 +60,7 @@ bool make_bwd_plan(const Problem &p, BwdPlan *out) {
         if (q.dvbc != 0) break;
     }
     if (q.dvbc == 0) return false;
+    q.xtc = bwd_pass_lds(p, kPassC, q.dvbc, q.padbc, true) != 0;
     // heads per block of passes B and C: each block stages its group's V tile
     // once and then one head after another; the partial sums it leaves per
     // run of heads cost memory traffic.  One block per CU (LDS), 256 CUs:
@@ -255,21 +258,25 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         L.dv = q.dvq;
         L.hb = 1;
         L.lds_pad = q.padq;
+        L.xt_lds = q.xtq ? 1 : 0;
         if (launch_bwd_pass(p, L, stream, events_of(6)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassB;
         L.out = fp(lay.dbp);
         L.dv = q.dvbc;
         L.hb = q.hb;
         L.lds_pad = q.padbc;
+        L.xt_lds = 0;
         if (launch_bwd_pass(p, L, stream, events_of(7)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassC;
         L.out = fp(lay.dcp);
+        L.xt_lds = q.xtc ? 1 : 0;
         if (launch_bwd_pass(p, L, stream, events_of(8)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassW;
         L.out = nullptr;
         L.dv = 16;
         L.hb = 1;
         L.lds_pad = bwd_pass_lds(p, kPassW, 16, 8) != 0 ? 8 : 0;
+        L.xt_lds = 0;
         if (launch_bwd_pass(p, L, stream, events_of(9)) != hipSuccess) return SSD_ERROR_LAUNCH;
         const BwdTokens tk{fp(lay.xq), fp(lay.xqi), fp(lay.dyx), fp(lay.cdi),
                            reinterpret_cast<const double *>(ws + lay.wcol), reinterpret_cast<const double *>(ws + lay.wrow),

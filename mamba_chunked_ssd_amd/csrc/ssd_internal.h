@@ -141,6 +141,7 @@ struct BwdPassLaunch {
     int dv;      // columns per block (16, 32 or 64)
     int hb;      // heads per block
     int lds_pad; // LDS row padding in elements (0 or 8)
+    int xt_lds;  // dx pass: x tile, dC pass: C tile staged in LDS (needs the room)
 };
 // Column tiles of the dB and dC passes that their registers hold without
 // spilling (the rule of kb_pass_inst.h's bc_dv_ok).
@@ -148,7 +149,7 @@ inline bool bwd_dv_ok(bool bf16, int64_t P, int dv) {
     return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
 }
 // LDS bytes a pass block needs; 0 if it does not fit one CU.
-size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad);
+size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad, bool xt = false);
 hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t stream, const LaunchEvents &ev);
 
 // The per-token partial sums the passes leave, (batch, nheads, Lp, parts).

@@ -62,14 +62,16 @@ hipError_t launch_bwd_carry(const Problem &, const float *, const void *, G2View
     return hipSuccess;
 }
 // the LDS rule of the pass kernels: tables, K (passes 1, 2), V, state tile
-size_t bwd_pass_lds(const Problem &p, int pass, int dv, int pad) {
+size_t bwd_pass_lds(const Problem &p, int pass, int dv, int pad, bool xt) {
     const int64_t esz = p.bf16 ? 2 : 4;
     const int64_t T = p.chunk, P = p.headdim;
-    int64_t bytes = 12 * T;
+    int64_t bytes = 16 * T;
     if (pass != 0) bytes += T * (P + pad) * esz;
+    if (pass == 3) return bytes <= (int64_t)kLdsPerCu ? (size_t)bytes : 0;
     bytes += T * (dv + pad) * esz;
     const int64_t erow = pass == 0 ? (p.dstate + 31) / 32 * 32 + pad : dv + pad;
     bytes += (pass == 0 ? dv : P) * erow * 4;
+    if (xt && (pass == 0 || pass == 2)) bytes += T * (dv + pad) * esz;
     return bytes <= (int64_t)kLdsPerCu ? (size_t)bytes : 0;
 }
 hipError_t launch_bwd_pass(const Problem &, const BwdPassLaunch &, hipStream_t, const LaunchEvents &) {
