@@ -86,6 +86,17 @@ namespace bwd {
 
 enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3 };
 
+// 16-row strips per wave (kb_spw, shared with the host in ssd_internal.h):
+// 2 pairs strip w with strip n - 1 - w (T/32 waves, the pair's K and V
+// fragments read once for both); 1 gives one strip per wave (T/16 waves, more
+// waves per SIMD to hide latency, the per-SIMD work staying even: SIMD s holds
+// the strips s, s + 4, s + 8, ...).  Measured at the 2.7B layer: one strip
+// per wave for the dx and dB passes (121 -> 93 and 117 -> 93 us), two for the
+// dC pass (more registers: one strip per wave spills), the W sums (two blocks
+// per CU instead of one), and every pass with fp32 inputs (three-term
+// fragments: one strip per wave spills).
+__host__ __device__ constexpr int kb_threads(int pass, bool bf16, int T) { return 64 * (T / 16) / bwd_spw(pass, bf16); }
+
 struct PassArgs {
     const void *x, *dy, *Bm, *Cm;  // inputs, element type In
     const float *G2hi, *G2lo, *DT;  // (batch, nheads, Lp)
@@ -97,7 +108,7 @@ struct PassArgs {
     // per-token partial sums, each (batch, nheads, Lp, parts):
     float *xq, *xqi, *dyx;          // pass Q (parts = its dv-tiles): x . q, x . (state term of q), dy . x
     float *cdi;                     // pass C (parts = its dv-tiles): C . (state term of dC)
-    double *wcol, *wrow;            // pass W: W's column sums (1 part), row sums (T/32 parts)
+    double *wcol, *wrow;            // pass W: W's column sums (1 part), row sums (one part per wave)
     int64_t seqlen, Lp;
     int batch, NH, P, N, G, HPG, T, NC, hb, nhb, nvt;
     int krow, vrow, erow;           // LDS row strides (elements)
@@ -296,14 +307,15 @@ __device__ __forceinline__ float lds1(const uint16_t *p) { return bf16_to_f32(*p
 __device__ __forceinline__ float lds1(const float *p) { return *p; }
 
 template <typename In, int NKQ, int DV, int PASS>
-__global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
+__global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value, 256)) void kb_pass(PassArgs a) {
     typedef Io<In> IO;
     typedef typename IO::Lds L;
+    constexpr int kSPW = bwd_spw(PASS, std::is_same<In, uint16_t>::value);
     constexpr int NI = IO::NI, NF = IO::NF, NP = IO::NP;
     constexpr int NCT = DV / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     const int T = a.T, n = T / 16;
-    const int tid = threadIdx.x, nthr = 2 * T;
+    const int tid = threadIdx.x, nthr = kb_threads(PASS, std::is_same<In, uint16_t>::value, T);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so strip logic stays scalar
     const int l = tid & 63, g4 = l >> 4, l16 = l & 15;
 
@@ -351,10 +363,10 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
     }
 
     // strips of this wave and their (pass B, C) accumulators over the heads
-    const int strips[2] = {w, n - 1 - w};
-    floatx4 acc[2][NCT];
+    const int strips[2] = {w, kSPW == 2 ? n - 1 - w : w};
+    floatx4 acc[kSPW][NCT];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < kSPW; ++k)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) acc[k][ct] = zero4();
 
@@ -405,12 +417,14 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
 
         // 1. per strip: Q fragments (rows 16 I + l16, 32 kk + 8 g4 ..), the
         //    row's decay tables, and the state term, which starts O
-        Frag<NI> qf[2][NKQ];
-        floatx4 O[2][NCT];  // the state term first, then the chunk's own tokens on top
-        float grh[2], grl[2], rfac[2];
-        double rowacc[2] = {0.0, 0.0};  // pass W: sums over this lane's keys s of W[s][r]
+        Frag<NI> qf[kSPW][NKQ];
+        floatx4 O[kSPW][NCT];  // the state term first, then the chunk's own tokens on top
+        float grh[kSPW], grl[kSPW], rfac[kSPW];
+        double rowacc[kSPW];  // pass W: sums over this lane's keys s of W[s][r]
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kSPW; ++k) rowacc[k] = 0.0;
+#pragma unroll
+        for (int k = 0; k < kSPW; ++k) {
             const int I = strips[k];
             const int r = 16 * I + l16;  // this lane's row for the score / A-operand layout
             if constexpr (PASS != kPassQ) {
@@ -518,7 +532,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
 
         // 2. the key-strip pairs, each pair's K and V fragments read once for
         //    both row strips of the wave
-        const int I0 = strips[0], I1 = strips[1];  // I0 < I1
+        const int I0 = strips[0], I1 = strips[kSPW - 1];  // I0 <= I1
         const int jlo = PASS == kPassC ? 0 : (I0 & ~1);
         const int jhi = PASS == kPassC ? (I1 & ~1) : n - 2;  // inclusive, even
         const int64_t stb = (((int64_t)b * a.NC + c) * a.G + g) * (int64_t)(n * (n + 1) / 2);
@@ -540,9 +554,9 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
             }
             // the scores of both strips first (or their tiles' loads, pass Q),
             // so that one strip's MFMA latency hides behind the other's VALU work
-            floatx4 Sall[2][2];
+            floatx4 Sall[kSPW][2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kSPW; ++k) {
                 const int I = strips[k];
                 const bool act = !(PASS == kPassC ? (J0 > (I & ~1)) : (J0 + 1 < I));
 #pragma unroll
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                 }
             }
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kSPW; ++k) {
                 const int I = strips[k];
                 if (PASS == kPassC ? (J0 > (I & ~1)) : (J0 + 1 < I)) continue;  // no live key strip
                 const int r = 16 * I + l16;
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
 
         // 3. per strip: outputs
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kSPW; ++k) {
             const int I = strips[k];
             const int r = 16 * I + l16;
             if constexpr (PASS == kPassW) {
@@ -707,7 +721,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
                 // sums over this wave's rows r of W[s][r] (W's row s), one part per wave
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    a.wrow[(bh * a.Lp + t0 + 16 * l16 + 4 * g4 + i) * (T / 32) + w] = colacc[i];
+                    a.wrow[(bh * a.Lp + t0 + 16 * l16 + 4 * g4 + i) * (T / 16 / kSPW) + w] = colacc[i];
             }
         }
     }
@@ -715,7 +729,7 @@ __global__ __launch_bounds__(512) void kb_pass(PassArgs a) {
     if constexpr (PASS == kPassB || PASS == kPassC) {
         // this run of heads' partial sum: (hblk, batch, Lp, G, N)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kSPW; ++k) {
             const int I = strips[k];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -114,7 +114,7 @@ BwdLayout bwd_layout(const Problem &p, const BwdPlan &q) {
     l.dyx = take(tok * q.nvtq);
     l.cdi = take(tok * (p.dstate / q.dvbc));
     l.wcol = take(tok * 2);  // doubles
-    l.wrow = take(tok * 2 * (p.chunk / 32));
+    l.wrow = take(tok * 2 * bwd_pass_waves(kPassW, p.bf16, p.chunk));
     const size_t part = (size_t)q.nhb * p.batch * p.padded_len * p.ngroups * p.dstate * sizeof(float);
     l.dbp = take(part);
     l.dcp = take(part);
@@ -280,7 +280,7 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         if (launch_bwd_pass(p, L, stream, events_of(9)) != hipSuccess) return SSD_ERROR_LAUNCH;
         const BwdTokens tk{fp(lay.xq), fp(lay.xqi), fp(lay.dyx), fp(lay.cdi),
                            reinterpret_cast<const double *>(ws + lay.wcol), reinterpret_cast<const double *>(ws + lay.wrow),
-                           q.nvtq, (int)(p.dstate / q.dvbc), (int)(p.chunk / 32)};
+                           q.nvtq, (int)(p.dstate / q.dvbc), (int)bwd_pass_waves(kPassW, p.bf16, p.chunk)};
         if (launch_bwd_tokens(p, tk, DTf, Zp, A, ddt, fp(lay.dap), fp(lay.ddp), stream, events_of(10)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
     } else if (!skip(5) || !skip(6) || !skip(7) || !skip(8) || !skip(9) || !skip(10)) {

@@ -124,6 +124,12 @@ hipError_t launch_bwd_scores(const Problem &p, const void *B, const void *C, flo
 hipError_t launch_bwd_carry(const Problem &p, const float *U, const void *H, G2View G2, const float *dfinal,
                             void *E, float *Zp, float *dinit, hipStream_t stream, const LaunchEvents &ev);
 
+// Strips of 16 rows per wave of each backward pass (0 dx, 1 dB, 2 dC, 3 W
+// sums; 1 or 2, see kb_pass.h) for bf16 or fp32 inputs, and the waves of a
+// block (the W sums leave one part of their row sums per wave).
+__host__ __device__ constexpr int bwd_spw(int pass, bool bf16) { return bf16 && (pass == 0 || pass == 1) ? 1 : 2; }
+inline int64_t bwd_pass_waves(int pass, bool bf16, int64_t T) { return (T / 16) / bwd_spw(pass, bf16); }
+
 // One of the MFMA passes (kb_pass.h): 0 = dx and the per-token dot products,
 // 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16).
 struct BwdPassLaunch {
@@ -157,7 +163,7 @@ struct BwdTokens {
     const float *xq, *xqi, *dyx;  // dx pass: nq parts (its column tiles)
     const float *cdi;             // dC pass: nc parts
     const double *wcol;           // dB pass: 1 part
-    const double *wrow;           // dB pass: nw = chunk / 32 parts
+    const double *wrow;           // W sums: nw = bwd_pass_waves(chunk) parts
     int nq, nc, nw;
 };
 hipError_t launch_bwd_tokens(const Problem &p, const BwdTokens &tk, const float *DT, const float *Zp,
