@@ -167,14 +167,17 @@ __global__ __launch_bounds__(256) void kb_carry(const float *__restrict__ U, con
 // Per-token finish: one wave per (batch, chunk, head), T / 64 consecutive
 // tokens per lane.  The partial dot products of the passes are summed, da
 // formed with a suffix and a prefix scan over the chunk in fp64 (wave scans),
-// then ddt and the chunk's partial sums of dA and dD.
+// then ddt and the chunk's partial sums of dA and dD.  The parts are stored
+// part-major, so each lane reads one part of its tokens as one vector and
+// the loads of all parts are independent of one another (the kernel's time
+// is their latency, not their bytes).
 // ---------------------------------------------------------------------------
 struct TokParts {
     const float *xq, *xqi, *dyx;  // nq parts each
     const float *cdi;             // nc parts
-    const double *wcol;           // 1 part
-    const double *wrow;           // nw parts
-    int nq, nc, nw;
+    const double *wd;             // 1 part
+    int64_t ps;                   // elements of one part: batch * nheads * Lp
+    int nq, nc;
 };
 
 // inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (the
@@ -214,27 +217,58 @@ __global__ __launch_bounds__(256) void kb_tokens(TokParts tp, const float *__res
     const int T = 64 * E;
     const int64_t tb = (int64_t)c * T + lane * E;  // first token of this lane
 
-    double suf[E], pre[E], xqv[E], dtv[E];  // per token: suffix and prefix terms
+    // this lane's tokens of every part, summed in fp64 (all loads independent)
+    const int64_t it0 = bh * Lp + tb;
+    double xqv[E], xqiv[E], dyxv[E], cdv[E], dtv[E], wdv[E];
+    {
+        float d[E];
+        load_vec<E>(DT + it0, d);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            dtv[e] = d[e];
+            xqv[e] = xqiv[e] = dyxv[e] = cdv[e] = 0.0;
+        }
+        if constexpr (E == 1) {
+            wdv[0] = tp.wd[it0];
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; e += 2) {
+                const double2 w2 = *reinterpret_cast<const double2 *>(tp.wd + it0 + e);
+                wdv[e] = w2.x;
+                wdv[e + 1] = w2.y;
+            }
+        }
+    }
+#pragma unroll 2
+    for (int v = 0; v < tp.nq; ++v) {
+        float q[E], qi[E], yx[E];
+        load_vec<E>(tp.xq + v * tp.ps + it0, q);
+        load_vec<E>(tp.xqi + v * tp.ps + it0, qi);
+        load_vec<E>(tp.dyx + v * tp.ps + it0, yx);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            xqv[e] += q[e];
+            xqiv[e] += qi[e];
+            dyxv[e] += yx[e];
+        }
+    }
+#pragma unroll 4
+    for (int v = 0; v < tp.nc; ++v) {
+        float cd[E];
+        load_vec<E>(tp.cdi + v * tp.ps + it0, cd);
+#pragma unroll
+        for (int e = 0; e < E; ++e) cdv[e] += cd[e];
+    }
+    double suf[E], pre[E];  // per token: suffix and prefix terms
     double dyx = 0.0, lsuf = 0.0, lpre = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int64_t t = tb + e, it = bh * Lp + t;
-        double xq = 0.0, xqi = 0.0, cd = 0.0, wr = 0.0, wc = 0.0, d = 0.0;
-        if (t < seqlen) {
-            for (int v = 0; v < tp.nq; ++v) {
-                xq += tp.xq[it * tp.nq + v];
-                xqi += tp.xqi[it * tp.nq + v];
-                dyx += tp.dyx[it * tp.nq + v];
-            }
-            for (int v = 0; v < tp.nc; ++v) cd += tp.cdi[it * tp.nc + v];
-            for (int v = 0; v < tp.nw; ++v) wr += tp.wrow[it * tp.nw + v];
-            wc = tp.wcol[it];
-            d = DT[it];
+        if (tb + e >= seqlen) {  // padding tokens of the last chunk take no part
+            xqv[e] = xqiv[e] = dyxv[e] = cdv[e] = dtv[e] = wdv[e] = 0.0;
         }
-        xqv[e] = xq;
-        dtv[e] = d;
-        suf[e] = (wr - wc) + cd;
-        pre[e] = d * xqi;
+        dyx += dyxv[e];
+        suf[e] = wdv[e] + cdv[e];
+        pre[e] = dtv[e] * xqiv[e];
         lsuf += suf[e];
         lpre += pre[e];
     }
@@ -348,7 +382,7 @@ hipError_t launch_bwd_tokens(const Problem &p, const BwdTokens &tk, const float 
     if (total == 0) return hipSuccess;
     const int64_t blocks = (total + 3) / 4;
     const int nzw = (int)(p.headdim * p.dstate / 256);
-    TokParts tp{tk.xq, tk.xqi, tk.dyx, tk.cdi, tk.wcol, tk.wrow, tk.nq, tk.nc, tk.nw};
+    TokParts tp{tk.xq, tk.xqi, tk.dyx, tk.cdi, tk.wd, p.batch * p.nheads * p.padded_len, tk.nq, tk.nc};
 #define SSD_KB_TOK(EE)                                                                                        \
     launch_kernel(kb_tokens<EE>, dim3((unsigned)blocks), dim3(256), 0, stream, ev, tp, DT, Zp, A, ddt, dap, ddp, \
                   p.seqlen, p.padded_len, (int)p.nheads, (int)p.nchunks, nzw, total)

@@ -105,10 +105,11 @@ struct PassArgs {
     const float *ST;                // pass Q: score tiles
     const float *D;                 // pass Q: skip weights or null
     float *out;                     // pass Q: dx; passes B, C: partial sums per run of heads
-    // per-token partial sums, each (batch, nheads, Lp, parts):
+    // per-token partial sums, each (parts, batch, nheads, Lp), part-major so
+    // that the token pass reads each part as one coalesced vector:
     float *xq, *xqi, *dyx;          // pass Q (parts = its dv-tiles): x . q, x . (state term of q), dy . x
     float *cdi;                     // pass C (parts = its dv-tiles): C . (state term of dC)
-    double *wcol, *wrow;            // pass W: W's column sums (1 part), row sums (one part per wave)
+    double *wd;                     // pass W (one part): W's row sum minus its column sum
     int64_t seqlen, Lp;
     int batch, NH, P, N, G, HPG, T, NC, hb, nhb, nvt;
     int krow, vrow, erow;           // LDS row strides (elements)
@@ -123,7 +124,9 @@ __host__ __device__ inline int kb_lds_bytes(int pass, bool f32_in, int T, int P,
     const int esz = f32_in ? 4 : 2;
     int bytes = 16 * T;  // G2 hi, G2 lo, dt, key factors
     if (pass != kPassQ) bytes += T * krow * esz;
-    if (pass == kPassW) return bytes;
+    // pass W: one part per wave of W's row sums and the column sums, fp64,
+    // summed in the block before they are written
+    if (pass == kPassW) return bytes + 8 * T * (T / 16 / bwd_spw(kPassW, !f32_in) + 1);
     bytes += T * vrow * esz;
     const int erows = pass == kPassQ ? DV : P;
     bytes += erows * erow * 4;
@@ -342,6 +345,9 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
     unsigned char *ES = reinterpret_cast<unsigned char *>(VS + T * a.vrow);
     const int erows = PASS == kPassQ ? DV : a.P;
     L *XS = reinterpret_cast<L *>(ES + erows * a.erow * 4);  // x (pass Q) or C (pass C) tile, if staged
+    // pass W: nwv parts of W's row sums, then its column sums, T doubles each
+    const int nwv = T / 16 / kSPW;
+    double *wsum = reinterpret_cast<double *>(KS + T * a.krow);
 
     const In *xin = static_cast<const In *>(a.x);
     const In *dyin = static_cast<const In *>(a.dy);
@@ -391,6 +397,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             }
         }
         const int64_t rowbase = ((int64_t)b * a.seqlen + t0) * NHP + (int64_t)h * a.P;  // token t0, head h
+        const int64_t pbase = ((int64_t)vt * a.batch * a.NH + bh) * a.Lp + t0;        // part vt of the token sums
         const unsigned char *sbase =
             static_cast<const unsigned char *>(PASS == kPassC ? a.H : a.E) + (bh * a.NC + c) * ssz;
         if constexpr (PASS == kPassQ) {
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                     }
                     if (l16 == 0) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) a.xqi[(bh * a.Lp + t0 + 16 * I + 4 * g4 + i) * a.nvt + vt] = xs[i];
+                        for (int i = 0; i < 4; ++i) a.xqi[pbase + 16 * I + 4 * g4 + i] = xs[i];
                     }
                 }
                 if constexpr (PASS == kPassC) {
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                     }
                     if (l16 == 0) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) a.cdi[(bh * a.Lp + t0 + 16 * I + 4 * g4 + i) * a.nvt + vt] = cd[i];
+                        for (int i = 0; i < 4; ++i) a.cdi[pbase + 16 * I + 4 * g4 + i] = cd[i];
                     }
                 }
             }
@@ -671,7 +678,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                 double ra = rowacc[k];
                 ra += __shfl_xor(ra, 16, 64);
                 ra += __shfl_xor(ra, 32, 64);
-                if (g4 == 0) a.wcol[bh * a.Lp + t0 + r] = ra;
+                if (g4 == 0) wsum[T * nwv + r] = ra;
             } else if constexpr (PASS == kPassQ) {
                 float xq[4], dyx[4];
 #pragma unroll
@@ -702,7 +709,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int ro = 16 * I + 4 * g4 + i;
-                        const int64_t ti = (bh * a.Lp + t0 + ro) * a.nvt + vt;
+                        const int64_t ti = pbase + ro;
                         a.xq[ti] = xq[i];
                         a.dyx[ti] = dyx[i];
                     }
@@ -720,8 +727,16 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             if (l16 < n) {
                 // sums over this wave's rows r of W[s][r] (W's row s), one part per wave
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.wrow[(bh * a.Lp + t0 + 16 * l16 + 4 * g4 + i) * (T / 16 / kSPW) + w] = colacc[i];
+                for (int i = 0; i < 4; ++i) wsum[T * w + 16 * l16 + 4 * g4 + i] = colacc[i];
+            }
+            __syncthreads();
+            // the waves' parts in a fixed order, less the column sum: one
+            // double per token (the next head writes wsum only after the
+            // barriers at its start)
+            for (int t = tid; t < T; t += nthr) {
+                double rs = 0.0;
+                for (int v = 0; v < nwv; ++v) rs += wsum[T * v + t];
+                a.wd[bh * a.Lp + t0 + t] = rs - wsum[T * nwv + t];
             }
         }
     }

@@ -58,8 +58,7 @@ hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t
     a.xqi = L.xqi;
     a.dyx = L.dyx;
     a.cdi = L.cdi;
-    a.wcol = L.wcol;
-    a.wrow = L.wrow;
+    a.wd = L.wd;
     a.seqlen = p.seqlen;
     a.Lp = p.padded_len;
     a.batch = (int)p.batch;

@@ -29,14 +29,15 @@ enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3 };
 
 struct BwdPlan {
     int dvq, padq;    // dx pass: headdim columns per block, LDS row padding
-    int dvbc, padbc;  // dB and dC passes: dstate columns per block, padding
+    int dvb, padb;    // dB pass: dstate columns per block, padding
+    int dvc, padc;    // dC pass: dstate columns per block, padding
     bool xtq, xtc;    // dx pass: x tile, dC pass: C tile staged in LDS
     int hb, nhb;      // dB and dC passes: heads per block, runs of heads per group
     int nvtq;         // dx pass: column tiles (headdim / dvq)
 };
 
 struct BwdLayout {
-    size_t g2_hi, g2_lo, dt, w, wb, s, h, e, zp, st, xq, xqi, dyx, cdi, wcol, wrow, dbp, dcp, dap, ddp, total;
+    size_t g2_hi, g2_lo, dt, w, wb, s, h, e, zp, st, xq, xqi, dyx, cdi, wd, dbp, dcp, dap, ddp, total;
 };
 
 bool make_bwd_plan(const Problem &p, BwdPlan *out) {
@@ -46,28 +47,29 @@ bool make_bwd_plan(const Problem &p, BwdPlan *out) {
     if (bwd_pass_lds(p, kPassQ, q.dvq, q.padq) == 0) return false;
     q.xtq = bwd_pass_lds(p, kPassQ, q.dvq, q.padq, true) != 0;
     q.nvtq = (int)(p.headdim / q.dvq);
-    q.dvbc = 0;
-    for (int dv : {64, 32, 16}) {
-        if (!bwd_dv_ok(p.bf16, p.headdim, dv)) continue;
-        if (p.dstate % dv != 0) continue;
-        for (int pad : {8, 0}) {
-            if (bwd_pass_lds(p, kPassB, dv, pad) != 0 && bwd_pass_lds(p, kPassC, dv, pad) != 0) {
-                q.dvbc = dv;
-                q.padbc = pad;
-                break;
+    // widest dstate tile each pass's registers and one CU's LDS hold
+    auto widest = [&](int pass, int *dv_out, int *pad_out) {
+        for (int dv : {64, 32, 16}) {
+            if (!bwd_dv_ok(p.bf16, pass, p.headdim, dv) || p.dstate % dv != 0) continue;
+            for (int pad : {8, 0}) {
+                if (bwd_pass_lds(p, pass, dv, pad) != 0) {
+                    *dv_out = dv;
+                    *pad_out = pad;
+                    return true;
+                }
             }
         }
-        if (q.dvbc != 0) break;
-    }
-    if (q.dvbc == 0) return false;
-    q.xtc = bwd_pass_lds(p, kPassC, q.dvbc, q.padbc, true) != 0;
+        return false;
+    };
+    if (!widest(kPassB, &q.dvb, &q.padb) || !widest(kPassC, &q.dvc, &q.padc)) return false;
+    q.xtc = bwd_pass_lds(p, kPassC, q.dvc, q.padc, true) != 0;
     // heads per block of passes B and C: each block stages its group's V tile
     // once and then one head after another; the partial sums it leaves per
     // run of heads cost memory traffic.  One block per CU (LDS), 256 CUs:
     // the smallest makespan in rounds x (heads + 1), fewest runs on ties.
-    const int64_t base = p.batch * p.nchunks * p.ngroups * (p.dstate / q.dvbc);
+    const int64_t base = p.batch * p.nchunks * p.ngroups * (p.dstate / q.dvb);
     const int64_t hpg = p.heads_per_group;
-    const int64_t slots = 256 * std::max<int64_t>(1, (int64_t)(kLdsPerCu / bwd_pass_lds(p, kPassB, q.dvbc, q.padbc)));
+    const int64_t slots = 256 * std::max<int64_t>(1, (int64_t)(kLdsPerCu / bwd_pass_lds(p, kPassB, q.dvb, q.padb)));
     double best = std::numeric_limits<double>::max();
     int best_hb = (int)hpg;
     for (int64_t hb = hpg; hb >= 1; --hb) {
@@ -112,9 +114,8 @@ BwdLayout bwd_layout(const Problem &p, const BwdPlan &q) {
     l.xq = take(tok * q.nvtq);
     l.xqi = take(tok * q.nvtq);
     l.dyx = take(tok * q.nvtq);
-    l.cdi = take(tok * (p.dstate / q.dvbc));
-    l.wcol = take(tok * 2);  // doubles
-    l.wrow = take(tok * 2 * bwd_pass_waves(kPassW, p.bf16, p.chunk));
+    l.cdi = take(tok * (p.dstate / q.dvc));
+    l.wd = take(tok * 2);  // doubles
     const size_t part = (size_t)q.nhb * p.batch * p.padded_len * p.ngroups * p.dstate * sizeof(float);
     l.dbp = take(part);
     l.dcp = take(part);
@@ -129,10 +130,10 @@ ssd_status prepare(const ssd_shape *shape, int64_t chunk, Problem *p, BwdPlan *q
     if (st != SSD_OK) return st;
     if (shape->flags != 0) return SSD_ERROR_INVALID_VALUE;
     if (!make_bwd_plan(*p, q)) return SSD_ERROR_UNSUPPORTED;
-    if (bwd_pass_lds(*p, kPassW, 16, 8) == 0) return SSD_ERROR_UNSUPPORTED;
+    if (bwd_pass_lds(*p, kPassW, 16, 0) == 0) return SSD_ERROR_UNSUPPORTED;
     // the passes address one chunk's rows of dy / x / B / C with 32-bit
     // LDS-sized loops and int block counts
-    if (p->batch * p->nchunks * p->ngroups * q->nhb * (p->dstate / q->dvbc) > 0x7fffffff)
+    if (p->batch * p->nchunks * p->ngroups * q->nhb * (p->dstate / std::min(q->dvb, q->dvc)) > 0x7fffffff)
         return SSD_ERROR_UNSUPPORTED;
     *l = bwd_layout(*p, *q);
     return SSD_OK;
@@ -251,8 +252,7 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         L.xqi = fp(lay.xqi);
         L.dyx = fp(lay.dyx);
         L.cdi = fp(lay.cdi);
-        L.wcol = reinterpret_cast<double *>(ws + lay.wcol);
-        L.wrow = reinterpret_cast<double *>(ws + lay.wrow);
+        L.wd = reinterpret_cast<double *>(ws + lay.wd);
         L.pass = kPassQ;
         L.out = dx;
         L.dv = q.dvq;
@@ -262,13 +262,15 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         if (launch_bwd_pass(p, L, stream, events_of(6)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassB;
         L.out = fp(lay.dbp);
-        L.dv = q.dvbc;
+        L.dv = q.dvb;
         L.hb = q.hb;
-        L.lds_pad = q.padbc;
+        L.lds_pad = q.padb;
         L.xt_lds = 0;
         if (launch_bwd_pass(p, L, stream, events_of(7)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassC;
         L.out = fp(lay.dcp);
+        L.dv = q.dvc;
+        L.lds_pad = q.padc;
         L.xt_lds = q.xtc ? 1 : 0;
         if (launch_bwd_pass(p, L, stream, events_of(8)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassW;
@@ -279,8 +281,7 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         L.xt_lds = 0;
         if (launch_bwd_pass(p, L, stream, events_of(9)) != hipSuccess) return SSD_ERROR_LAUNCH;
         const BwdTokens tk{fp(lay.xq), fp(lay.xqi), fp(lay.dyx), fp(lay.cdi),
-                           reinterpret_cast<const double *>(ws + lay.wcol), reinterpret_cast<const double *>(ws + lay.wrow),
-                           q.nvtq, (int)(p.dstate / q.dvbc), (int)bwd_pass_waves(kPassW, p.bf16, p.chunk)};
+                           reinterpret_cast<const double *>(ws + lay.wd), q.nvtq, (int)(p.dstate / q.dvc)};
         if (launch_bwd_tokens(p, tk, DTf, Zp, A, ddt, fp(lay.dap), fp(lay.ddp), stream, events_of(10)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
     } else if (!skip(5) || !skip(6) || !skip(7) || !skip(8) || !skip(9) || !skip(10)) {

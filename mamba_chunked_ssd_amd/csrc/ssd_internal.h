@@ -125,10 +125,8 @@ hipError_t launch_bwd_carry(const Problem &p, const float *U, const void *H, G2V
                             void *E, float *Zp, float *dinit, hipStream_t stream, const LaunchEvents &ev);
 
 // Strips of 16 rows per wave of each backward pass (0 dx, 1 dB, 2 dC, 3 W
-// sums; 1 or 2, see kb_pass.h) for bf16 or fp32 inputs, and the waves of a
-// block (the W sums leave one part of their row sums per wave).
+// sums; 1 or 2, see kb_pass.h) for bf16 or fp32 inputs.
 __host__ __device__ constexpr int bwd_spw(int pass, bool bf16) { return bf16 && (pass == 0 || pass == 1) ? 1 : 2; }
-inline int64_t bwd_pass_waves(int pass, bool bf16, int64_t T) { return (T / 16) / bwd_spw(pass, bf16); }
 
 // One of the MFMA passes (kb_pass.h): 0 = dx and the per-token dot products,
 // 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16).
@@ -143,28 +141,28 @@ struct BwdPassLaunch {
     const float *D;
     float *out;
     float *xq, *xqi, *dyx, *cdi;  // per-token partial sums (kb_pass.h)
-    double *wcol, *wrow;
+    double *wd;
     int dv;      // columns per block (16, 32 or 64)
     int hb;      // heads per block
     int lds_pad; // LDS row padding in elements (0 or 8)
     int xt_lds;  // dx pass: x tile, dC pass: C tile staged in LDS (needs the room)
 };
-// Column tiles of the dB and dC passes that their registers hold without
-// spilling (the rule of kb_pass_inst.h's bc_dv_ok).
-inline bool bwd_dv_ok(bool bf16, int64_t P, int dv) {
+// Column tiles of the dB (pass 1) and dC (pass 2) passes that their
+// registers hold without spilling (the rule of kb_pass_inst.h's bc_dv_ok).
+inline bool bwd_dv_ok(bool bf16, int pass, int64_t P, int dv) {
+    (void)pass;
     return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
 }
 // LDS bytes a pass block needs; 0 if it does not fit one CU.
 size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad, bool xt = false);
 hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t stream, const LaunchEvents &ev);
 
-// The per-token partial sums the passes leave, (batch, nheads, Lp, parts).
+// The per-token partial sums the passes leave, (parts, batch, nheads, Lp).
 struct BwdTokens {
     const float *xq, *xqi, *dyx;  // dx pass: nq parts (its column tiles)
     const float *cdi;             // dC pass: nc parts
-    const double *wcol;           // dB pass: 1 part
-    const double *wrow;           // W sums: nw = bwd_pass_waves(chunk) parts
-    int nq, nc, nw;
+    const double *wd;             // W sums: W's row sum minus its column sum, 1 part
+    int nq, nc;
 };
 hipError_t launch_bwd_tokens(const Problem &p, const BwdTokens &tk, const float *DT, const float *Zp,
                              const float *A, float *ddt, float *dap, float *ddp, hipStream_t stream,
