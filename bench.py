@@ -48,13 +48,18 @@ MEASURED_TRAFFIC = {
         ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'e0b38472eef460b1', 45015.9, 81960.0),
     ("mamba2_2p7b_layer_bf16", "f32", "chunk_state", "fused"): (
         ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), 'd335e9eacd803fb6', 24143.0, 48386.0),
+    # backward (the y dtype and state path do not apply)
+    ("mamba2_2p7b_layer_bf16", None, "bwd:dC_pass", None): (
+        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h'), '3644302dc4394f65', 71697.0, 18944.0),
 }
 
 
 def measured_traffic(workload: str, y_dtype: str, stage: str, plan: dict | None = None):
     """HBM bytes per launch of ``stage`` if counters exist for its current sources."""
     import hashlib
-    ent = MEASURED_TRAFFIC.get((workload, y_dtype, stage, (plan or {}).get("state_path", "split")))
+    key = (workload, None, stage, None) if stage.startswith("bwd:") else (
+        workload, y_dtype, stage, (plan or {}).get("state_path", "split"))
+    ent = MEASURED_TRAFFIC.get(key)
     if ent is None:
         return None
     files, digest, fetch_kib, write_kib = ent
@@ -264,8 +269,8 @@ def bwd_stage_model(w) -> dict:
     bwd_bc = 2.0 * units * (tri * P + tri * N + T * P * N)
     m["dB_pass"] = (2 * x + bc + states + 4 * B * L * G * N, bwd_bc)
     m["dC_pass"] = (2 * x + 2 * bc + states + 4 * B * L * G * N + 4 * tok_h, bwd_bc)
-    m["w_sums"] = (2 * x + st + 8 * tok_h * (1 + T // 32), 2.0 * units * tri * P)
-    m["token_finish"] = (4 * 4 * tok_h + 8 * tok_h * (1 + T // 32) + 4 * tok_h, 0.0)
+    m["w_sums"] = (2 * x + st + 8 * tok_h, 2.0 * units * tri * P)
+    m["token_finish"] = ((4 * 4 + 8 + 4) * tok_h, 0.0)
     m["reduce"] = (2 * 4 * B * L * G * N * 2, 0.0)
     return m
 
@@ -340,8 +345,9 @@ def backward_bench(hip, w, inp, t, dev, steps=10, warmup=3) -> dict:
         "dominant": dom,
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(achieved / peak, 4),
-                     "flops": flops, "bytes": byts, "traffic": None,
-                     "model": "bwd_stage_model: algorithmic flops of the dominant stage's contractions"},
+                     "flops": flops, "bytes": byts, "traffic": measured_traffic(w.name, None, "bwd:" + dom),
+                     "model": "bwd_stage_model: algorithmic HBM bytes and contraction flops of the dominant "
+                              "stage; bound is the larger of the two floors"},
     }
 
 

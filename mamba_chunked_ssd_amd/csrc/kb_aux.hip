@@ -172,6 +172,18 @@ __global__ __launch_bounds__(256) void kb_carry(const float *__restrict__ U, con
 // the loads of all parts are independent of one another (the kernel's time
 // is their latency, not their bytes).
 // ---------------------------------------------------------------------------
+// E consecutive floats as one vector load (p aligned to 4 E bytes)
+template <int E>
+__device__ __forceinline__ void load_vec(const float *p, float (&v)[E]) {
+    const typename VecF<E>::type t = *reinterpret_cast<const typename VecF<E>::type *>(p);
+    if constexpr (E == 1) {
+        v[0] = t;
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = t[e];
+    }
+}
+
 struct TokParts {
     const float *xq, *xqi, *dyx;  // nq parts each
     const float *cdi;             // nc parts

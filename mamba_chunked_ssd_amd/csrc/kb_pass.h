@@ -322,9 +322,25 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so strip logic stays scalar
     const int l = tid & 63, g4 = l >> 4, l16 = l & 15;
 
-    int64_t u = blockIdx.x;
-    const int vt = (int)(u % a.nvt);
-    u /= a.nvt;
+    // The column tiles of one (batch, chunk, group, run of heads) read the
+    // same rows of x and dy.  Workgroups are dealt to the 8 XCDs in turn, so
+    // the tiles of one run are placed 8 dispatch slots apart: on one XCD,
+    // where the second tile's reads hit that XCD's L2 (the grid's tail past a
+    // multiple of 8 runs is laid out plainly).
+    int64_t u;
+    int vt;
+    {
+        const int64_t bx = blockIdx.x, nfull = ((int64_t)gridDim.x / a.nvt) / 8 * 8;
+        if (bx < nfull * a.nvt) {
+            const int64_t s = bx >> 3;
+            u = (s / a.nvt) * 8 + (bx & 7);
+            vt = (int)(s % a.nvt);
+        } else {
+            const int64_t r = bx - nfull * a.nvt;
+            u = nfull + r / a.nvt;
+            vt = (int)(r % a.nvt);
+        }
+    }
     const int hblk = (int)(u % a.nhb);
     u /= a.nhb;
     const int g = (int)(u % a.G);

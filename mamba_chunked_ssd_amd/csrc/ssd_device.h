@@ -66,18 +66,6 @@ struct VecF<2> { typedef floatx2 type; };
 template <>
 struct VecF<4> { typedef floatx4 type; };
 
-// E consecutive floats as one vector load (p aligned to 4 E bytes)
-template <int E>
-__device__ __forceinline__ void load_vec(const float *p, float (&v)[E]) {
-    const typename VecF<E>::type t = *reinterpret_cast<const typename VecF<E>::type *>(p);
-    if constexpr (E == 1) {
-        v[0] = t;
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = t[e];
-    }
-}
-
 template <int E>
 __device__ __forceinline__ void store_vec(float *p, const float (&v)[E]) {
     typename VecF<E>::type t;
