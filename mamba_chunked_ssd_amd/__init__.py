@@ -363,7 +363,7 @@ def chunk_scan_bwd(x, dt, A, B, C, D, dy, chunk_size: int = 256, initial_states=
     dtype), and optionally
     ``d_final_states`` (dL/dh_final, float32).  Returns a dict of float32
     tensors ``dx, ddt, dA, dB, dC`` and, when requested, ``dD`` and
-    ``d_initial_states``.  ``events``: 22 raw hipEvent_t handles (a start and
+    ``d_initial_states``.  ``events``: 24 raw hipEvent_t handles (a start and
     stop per stage of :data:`BWD_STAGES`).
     """
     torch = _torch()

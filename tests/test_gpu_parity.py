@@ -159,6 +159,9 @@ DEFAULT_MULTIHEAD = [
     ((2, 2048, 80, 64, 128, 1, 256), "f32", 2, 3),
     ((2, 1024, 64, 128, 256, 8, 128), "f32", 2, 3),
     ((2, 1024, 64, 128, 256, 8, 128), "bf16", 2, 3),
+    # chunk 256 with dstate 256 (the chunk output re-reads C per head): at
+    # least four blocks per chunk
+    ((1, 4096, 32, 64, 256, 1, 256), "bf16", 1, 2),
 ]
 
 
