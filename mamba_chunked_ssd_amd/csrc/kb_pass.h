@@ -40,14 +40,15 @@
 //   pass B: Q = x, K = dy, V = C (dv = dstate), anti-causal, Hm = E_c^T;
 //   pass W: pass B's scores x_k . dy_s alone, decayed and times the score
 //           tiles and dt_k: the entries of W, whose row and column sums it
-//           accumulates in fp64 (no V, no state term);
+//           accumulates (fp64 for fp32 problems, fp32 for bf16; no V, no
+//           state term);
 //   pass C: Q = dy, K = x, V = B, w_s = dt_s, causal, Hm = h_c^T, e_r = G2_r;
 //           C_r . (its state term) gives the second sum's terms;
 // and pass Q's state term dotted with x_r the third's.
 //
 // Design for gfx950.  One block per (batch, chunk, group, run of heads,
-// dv-tile), T/32 waves; wave w owns the row strips w and T/16 - 1 - w (16 rows
-// each), so the triangular work is even across waves.  Per head the block
+// dv-tile); each wave owns one or two 16-row strips (below), so the
+// triangular work is even across waves.  Per head the block
 // stages K, V and the state Hm into LDS; Q fragments come straight from
 // memory into registers.  For a strip and a pair of key strips the scores
 // arrive in the MFMA output layout (lane = row, four keys per lane), are
@@ -314,6 +315,13 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
     typedef Io<In> IO;
     typedef typename IO::Lds L;
     constexpr int kSPW = bwd_spw(PASS, std::is_same<In, uint16_t>::value);
+    // pass W: what the W entries are summed in.  The row and column sums are
+    // differenced later, and the difference's sums over the chunk cancel
+    // heavily: fp32 problems sum in fp64 (fp32 sums per 16-token tile left dA
+    // errors up to 4e-4 of its rms, over the 1e-4 bound; fp64 sums 2e-7);
+    // bf16 problems sum in fp32 (dA error 1.2e-5 of its rms, against a 2e-2
+    // bound; emulated on a bf16 problem of the 2.7B layer's head shapes).
+    typedef typename std::conditional<std::is_same<In, uint16_t>::value, float, double>::type WAcc;
     constexpr int NI = IO::NI, NF = IO::NF, NP = IO::NP;
     constexpr int NCT = DV / 16;
     extern __shared__ __align__(16) unsigned char lds[];
@@ -436,16 +444,16 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
         const float Dh = (PASS == kPassQ && a.D != nullptr) ? a.D[h] : 0.f;
         // pass W: sums of W[s][r] over this wave's rows r, for the keys
         // s = 16 J + 4 g4 + i of key strip J = l16
-        double colacc[4] = {0.0, 0.0, 0.0, 0.0};
+        WAcc colacc[4] = {0, 0, 0, 0};
 
         // 1. per strip: Q fragments (rows 16 I + l16, 32 kk + 8 g4 ..), the
         //    row's decay tables, and the state term, which starts O
         Frag<NI> qf[kSPW][NKQ];
         floatx4 O[kSPW][NCT];  // the state term first, then the chunk's own tokens on top
         float grh[kSPW], grl[kSPW], rfac[kSPW];
-        double rowacc[kSPW];  // pass W: sums over this lane's keys s of W[s][r]
+        WAcc rowacc[kSPW];  // pass W: sums over this lane's keys s of W[s][r]
 #pragma unroll
-        for (int k = 0; k < kSPW; ++k) rowacc[k] = 0.0;
+        for (int k = 0; k < kSPW; ++k) rowacc[k] = 0;
 #pragma unroll
         for (int k = 0; k < kSPW; ++k) {
             const int I = strips[k];
@@ -657,15 +665,14 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                             // W[s][r] = (x_r . dy_s) exp2(G2_s - G2_r) (B_r . C_s) dt_r for this
                             // lane's row r and keys s = 16 J + 4 g4 + i: sums over s stay in
                             // the lane, sums over the strip's 16 rows go to lane l16 = J
-                            // (entries in fp32, their sums in fp64: the row and column
-                            // sums are differenced later, where fp32 sums lose digits)
+                            // (entries in fp32, their sums in WAcc)
                             const int tile = I * n - (I * (I - 1)) / 2 + (J - I);
                             const floatx4 sc = *reinterpret_cast<const floatx4 *>(a.ST + ((stb + tile) * 64 + l) * 4);
                             const float dtr = dtt[r];
-                            double wv[4];
+                            WAcc wv[4];
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                wv[i] = (double)(pv[4 * jj + i] * sc[i] * dtr);
+                                wv[i] = (WAcc)(pv[4 * jj + i] * sc[i] * dtr);
                                 rowacc[k] += wv[i];
                             }
 #pragma unroll
@@ -691,10 +698,10 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             if constexpr (PASS == kPassW) {
                 // sum over s of W[s][r] (W's column r): this lane's keys, then
                 // the 4 lane groups
-                double ra = rowacc[k];
+                WAcc ra = rowacc[k];
                 ra += __shfl_xor(ra, 16, 64);
                 ra += __shfl_xor(ra, 32, 64);
-                if (g4 == 0) wsum[T * nwv + r] = ra;
+                if (g4 == 0) wsum[T * nwv + r] = (double)ra;
             } else if constexpr (PASS == kPassQ) {
                 float xq[4], dyx[4];
 #pragma unroll
@@ -743,7 +750,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             if (l16 < n) {
                 // sums over this wave's rows r of W[s][r] (W's row s), one part per wave
 #pragma unroll
-                for (int i = 0; i < 4; ++i) wsum[T * w + 16 * l16 + 4 * g4 + i] = colacc[i];
+                for (int i = 0; i < 4; ++i) wsum[T * w + 16 * l16 + 4 * g4 + i] = (double)colacc[i];
             }
             __syncthreads();
             // the waves' parts in a fixed order, less the column sum: one
