@@ -169,13 +169,15 @@ Plan make_plan(const Problem &p) {
     // The fused state launch (bf16) walks the chunks of one (batch, head,
     // 64 dstate columns) per block in order: it saves the s_c round trip
     // through memory but keeps only that many blocks busy.  Measured on
-    // MI355X it wins once those blocks fill the CUs (2.7B-shaped layer: 320
-    // blocks, 36.6 us against 37.6 us for the two split launches; 8 x 4096
-    // tokens: 281 us against 340 us) and loses below (65 536 tokens, 32
-    // heads, dstate 256: 128 blocks, 666 us against 426 us).
+    // MI355X it wins with two or more blocks per CU (8 x 4096 tokens: 1280
+    // blocks, 281-300 us against 334-340 us for the two split launches),
+    // ties with one to two (2.7B-shaped layer: 320 blocks, 86.0 against
+    // 86.2 us per forward pass, but 55.6 against 48.9 us from a cold cache)
+    // and loses below (65 536 tokens, 32 heads, dstate 256: 128 blocks, 666
+    // us against 426 us).
     plan.fused_cols = 64;
     plan.fused_state = p.nchunks > 0 && state_fused_supported(p, 64) &&
-                       p.batch * p.nheads * (p.dstate / 64) >= kNumCUs;
+                       p.batch * p.nheads * (p.dstate / 64) >= 2 * kNumCUs;
     if (!plan.fused_state) plan.fused_cols = (int)std::min<int64_t>(p.dstate, 64);
     return plan;
 }

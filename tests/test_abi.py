@@ -54,9 +54,14 @@ def test_stage_launches(lib):
     # every stage launches its own kernel when there are tokens (split state
     # path); under the fused state path the chunk-state launch also carries
     # the state, and the state-passing stage launches nothing
-    s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
+    # (8 x 4096 tokens: the fused path is the default; the 2.7B-shaped
+    # layer, one to two fused blocks per CU: the split path)
+    s = ssd.make_shape(8, 4096, 80, 64, 128, 1, "bf16")
     assert ssd.default_plan(s, 256).state_path == ssd.SSD_STATE_FUSED
     assert ssd.stage_launches(s, 256) == ("chunk_cumsum", "chunk_state", "chunk_out")
+    s = ssd.make_shape(2, 2048, 80, 64, 128, 1, "bf16")
+    assert ssd.default_plan(s, 256).state_path == ssd.SSD_STATE_SPLIT
+    assert ssd.stage_launches(s, 256) == ssd.STAGES
     assert ssd.stage_launches(s, 256, ssd.make_plan("split", 5, 5)) == ssd.STAGES
     assert ssd.stage_launches(s, 256, ssd.make_plan("fused", 5, 5, 32)) == (
         "chunk_cumsum", "chunk_state", "chunk_out")
