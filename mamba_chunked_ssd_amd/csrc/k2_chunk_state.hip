@@ -539,15 +539,18 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
                 Frags nxt;
                 if constexpr (ks + 1 < KS) nxt = read(ks + 1);
                 // hi products of every tile first, then lo: dependent MFMAs
-                // (same accumulator) are never adjacent
+                // (same accumulator) are never adjacent.  B is the A operand
+                // and x^T the B operand, so a tile comes out transposed: lane
+                // (l16, g4) holds the state's row 16 pt + l16, columns
+                // 16 nt + 4 g4 .. +3 -- one 16-byte store.
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) acc[pt][nt] = mfma_bf16(cur.h[pt], bfrag[ks][nt], acc[pt][nt]);
+                    for (int nt = 0; nt < 2; ++nt) acc[pt][nt] = mfma_bf16(bfrag[ks][nt], cur.h[pt], acc[pt][nt]);
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) acc[pt][nt] = mfma_bf16(cur.l[pt], bfrag[ks][nt], acc[pt][nt]);
+                    for (int nt = 0; nt < 2; ++nt) acc[pt][nt] = mfma_bf16(bfrag[ks][nt], cur.l[pt], acc[pt][nt]);
                 if constexpr (ks + 1 < KS) cur = nxt;
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -556,10 +559,9 @@ __global__ __launch_bounds__(64 * (kProducers + NCW)) void k2_chunk_state_bf16_w
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    const int n = 32 * cw + 16 * nt + ol16;
-                    if (n < N)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) out[(16 * pt + 4 * og4 + r) * N + n] = acc[pt][nt][r];
+                    const int n0 = 32 * cw + 16 * nt;  // dstate is a multiple of 16
+                    if (n0 < N)
+                        *reinterpret_cast<floatx4 *>(out + (16 * pt + ol16) * N + n0 + 4 * og4) = acc[pt][nt];
                 }
         }
         __syncthreads();
