@@ -87,16 +87,19 @@ namespace bwd {
 
 enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3 };
 
-// 16-row strips per wave (kb_spw, shared with the host in ssd_internal.h):
+// 16-row strips per wave (bwd_spw, shared with the host in ssd_internal.h):
 // 2 pairs strip w with strip n - 1 - w (T/32 waves, the pair's K and V
 // fragments read once for both); 1 gives one strip per wave (T/16 waves, more
 // waves per SIMD to hide latency, the per-SIMD work staying even: SIMD s holds
 // the strips s, s + 4, s + 8, ...).  Measured at the 2.7B layer: one strip
-// per wave for the dx and dB passes (121 -> 93 and 117 -> 93 us), two for the
-// dC pass (more registers: one strip per wave spills), the W sums (two blocks
-// per CU instead of one), and every pass with fp32 inputs (three-term
-// fragments: one strip per wave spills).
-__host__ __device__ constexpr int kb_threads(int pass, bool bf16, int T) { return 64 * (T / 16) / bwd_spw(pass, bf16); }
+// per wave for the dx and dB passes (121 -> 93 and 117 -> 93 us) and for the
+// dC pass up to headdim 64 (136 -> 131 us, although its 128 registers then
+// spill some values); two for the W sums (two blocks per CU instead of one)
+// and every pass with fp32 inputs (three-term fragments: one strip per wave
+// spills heavily).
+__host__ __device__ constexpr int kb_threads(int pass, bool bf16, int nkq, int T) {
+    return 64 * (T / 16) / bwd_spw(pass, bf16, nkq);
+}
 
 struct PassArgs {
     const void *x, *dy, *Bm, *Cm;  // inputs, element type In
@@ -127,7 +130,7 @@ __host__ __device__ inline int kb_lds_bytes(int pass, bool f32_in, int T, int P,
     if (pass != kPassQ) bytes += T * krow * esz;
     // pass W: one part per wave of W's row sums and the column sums, fp64,
     // summed in the block before they are written
-    if (pass == kPassW) return bytes + 8 * T * (T / 16 / bwd_spw(kPassW, !f32_in) + 1);
+    if (pass == kPassW) return bytes + 8 * T * (T / 16 / bwd_spw(kPassW, !f32_in, P / 32) + 1);
     bytes += T * vrow * esz;
     const int erows = pass == kPassQ ? DV : P;
     bytes += erows * erow * 4;
@@ -311,10 +314,10 @@ __device__ __forceinline__ float lds1(const uint16_t *p) { return bf16_to_f32(*p
 __device__ __forceinline__ float lds1(const float *p) { return *p; }
 
 template <typename In, int NKQ, int DV, int PASS>
-__global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value, 256)) void kb_pass(PassArgs a) {
+__global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value, NKQ, 256)) void kb_pass(PassArgs a) {
     typedef Io<In> IO;
     typedef typename IO::Lds L;
-    constexpr int kSPW = bwd_spw(PASS, std::is_same<In, uint16_t>::value);
+    constexpr int kSPW = bwd_spw(PASS, std::is_same<In, uint16_t>::value, NKQ);
     // pass W: what the W entries are summed in.  The row and column sums are
     // differenced later, and the difference's sums over the chunk cancel
     // heavily: fp32 problems sum in fp64 (fp32 sums per 16-token tile left dA
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
     constexpr int NCT = DV / 16;
     extern __shared__ __align__(16) unsigned char lds[];
     const int T = a.T, n = T / 16;
-    const int tid = threadIdx.x, nthr = kb_threads(PASS, std::is_same<In, uint16_t>::value, T);
+    const int tid = threadIdx.x, nthr = kb_threads(PASS, std::is_same<In, uint16_t>::value, NKQ, T);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so strip logic stays scalar
     const int l = tid & 63, g4 = l >> 4, l16 = l & 15;
 

@@ -12,7 +12,7 @@ hipError_t launch_one(const PassArgs &a, unsigned blocks, size_t lds, hipStream_
     constexpr auto kern = kb_pass<In, NKQ, DV, PASS>;
     const hipError_t st = allow_lds<kern>(lds);
     if (st != hipSuccess) return st;
-    return launch_kernel(kern, dim3(blocks), dim3(kb_threads(PASS, std::is_same<In, uint16_t>::value, a.T)), lds, stream, ev, a);
+    return launch_kernel(kern, dim3(blocks), dim3(kb_threads(PASS, std::is_same<In, uint16_t>::value, NKQ, a.T)), lds, stream, ev, a);
 }
 
 // Whether passes B and C are built with `dv`-column tiles for this input type

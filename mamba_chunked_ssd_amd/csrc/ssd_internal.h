@@ -125,8 +125,11 @@ hipError_t launch_bwd_carry(const Problem &p, const float *U, const void *H, G2V
                             void *E, float *Zp, float *dinit, hipStream_t stream, const LaunchEvents &ev);
 
 // Strips of 16 rows per wave of each backward pass (0 dx, 1 dB, 2 dC, 3 W
-// sums; 1 or 2, see kb_pass.h) for bf16 or fp32 inputs.
-__host__ __device__ constexpr int bwd_spw(int pass, bool bf16) { return bf16 && (pass == 0 || pass == 1) ? 1 : 2; }
+// sums; 1 or 2, see kb_pass.h) for bf16 or fp32 inputs and a headdim of
+// 32 nkq.
+__host__ __device__ constexpr int bwd_spw(int pass, bool bf16, int nkq) {
+    return bf16 && (pass == 0 || pass == 1 || (pass == 2 && nkq <= 2)) ? 1 : 2;
+}
 
 // One of the MFMA passes (kb_pass.h): 0 = dx and the per-token dot products,
 // 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16).
