@@ -143,6 +143,56 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+def context(hip, dev) -> dict:
+    """What this machine reaches beside the datasheet peaks: a device copy of
+    1 GiB from a source that a second 1 GiB write has evicted from L2 and the
+    Infinity Cache (bytes read plus written over the copy's own events,
+    median of 5), and the GPU clocks rocm-smi reports (null if it cannot)."""
+    import subprocess
+    import torch
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    flush = torch.empty(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    times = []
+    for _ in range(5):
+        flush.fill_(2.0)
+        e0, e1 = hip.event(), hip.event()
+        hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(st))
+        dst.copy_(src)
+        hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(st))
+        hip.lib.hipEventSynchronize(ctypes.c_void_p(e1))
+        times.append(hip.elapsed_ms(e0, e1) * 1e-3)
+        hip.destroy(e0)
+        hip.destroy(e1)
+    del src, dst, flush
+    t = sorted(times)[len(times) // 2]
+    clocks = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        if r.returncode == 0:
+            card = next(iter(json.loads(r.stdout).values()))
+            clocks = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:  # the tool is context only
+        clocks = None
+    return {"copy_GB_s": round(2 * n * 4 / t / 1e9, 1), "copy_bytes": 2 * n * 4,
+            "copy_note": "torch device copy, 1 GiB read + 1 GiB written, cold source",
+            "gpu_clocks": clocks}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle, as it stands, on this host's cores: the whole workload,
     repeated (at least ``reps`` times) until ``min_seconds`` of CPU work."""
@@ -162,6 +212,9 @@ def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
         "value": w.tokens / med,
         "unit": "tokens/s",
         "cores": min(threads, ncores),
+        "cpu": cpu_model(),
+        # the recurrence's fp64 flops: 4 B L NH N P (state update and readout)
+        "fp64_GFLOP_s": round(4.0 * w.batch * w.seqlen * w.nheads * w.dstate * w.headdim / med / 1e9, 2),
         "kind": "oracle",
         "sample": "whole workload (%d tokens, all heads), fp64 sequential recurrence, median of %d runs "
                   "(%.3f s each, %.1f s in all); oracle built with gcc -O2 -fopenmp, no -march=native "
@@ -374,6 +427,8 @@ def main(argv=None):
                     help="timed steps of the backward pass (0: skip it)")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="batch of the recurrent decode-step measurement (0: skip it)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the measured copy bandwidth and the GPU clocks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy (for scaling rocprofv3 FETCH/WRITE counters)")
     a = ap.parse_args(argv)
@@ -575,6 +630,9 @@ def main(argv=None):
 
     if a.decode_batch > 0:
         out["decode"] = decode_bench(hip, w, a.decode_batch, dev)
+
+    if not a.no_context:
+        out["context"] = context(hip, dev)
 
     if a.bwd_steps > 0:
         out["backward"] = backward_bench(hip, w, inp, t, dev, steps=a.bwd_steps)
