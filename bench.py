@@ -50,7 +50,7 @@ MEASURED_TRAFFIC = {
         ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), 'd335e9eacd803fb6', 24143.0, 48386.0),
     # backward (the y dtype and state path do not apply)
     ("mamba2_2p7b_layer_bf16", None, "bwd:dC_pass", None): (
-        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h', 'ssd_internal.h'), '9ba135d6ed52a97f', 85933.3, 50688.0),
+        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h', 'ssd_internal.h'), '9063d51874cc4cdd', 85933.3, 50688.0),
 }
 
 

@@ -18,12 +18,12 @@ hipError_t launch_one(const PassArgs &a, unsigned blocks, size_t lds, hipStream_
 // Whether passes B and C are built with `dv`-column tiles for this input type
 // and headdim: the accumulators (strips per wave x dv / 16 per lane) beside
 // the Q fragments (headdim / 32 x one bf16 term, or three for fp32 inputs)
-// fit the waves' register budget (256 at two strips per wave, 128 at one,
-// where a block holds 16 waves) without spilling only up to this width.  The
-// same rule holds for both passes today; the host applies it too (bwd_dv_ok
-// in ssd_internal.h).
-__host__ __device__ constexpr bool bc_dv_ok(bool bf16, int PASS, int P, int dv) {
-    return (void)PASS, dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
+// fit the waves' registers (256 at two strips per wave, 128 at one, where a
+// block holds 16 waves; at one strip the widest tiles spill a few values)
+// only up to this width.  The host applies the same rule (bwd_dv_ok in
+// ssd_internal.h).
+__host__ __device__ constexpr bool bc_dv_ok(bool bf16, int P, int dv) {
+    return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
 }
 
 // passes B and C: headdim (32 k) and dv-tile dispatch
@@ -31,7 +31,7 @@ template <typename In, int PASS>
 hipError_t launch_bc(const PassArgs &a, int dv, unsigned blocks, size_t lds, hipStream_t stream,
                      const LaunchEvents &ev) {
 #define SSD_KB_DVX(NK, DVV)                                                                 \
-    if constexpr (bc_dv_ok(std::is_same<In, uint16_t>::value, PASS, 32 * NK, DVV))                \
+    if constexpr (bc_dv_ok(std::is_same<In, uint16_t>::value, 32 * NK, DVV))                \
         return launch_one<In, NK, DVV, PASS>(a, blocks, lds, stream, ev);                   \
     else                                                                                    \
         return hipErrorInvalidValue;

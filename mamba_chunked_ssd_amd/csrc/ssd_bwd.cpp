@@ -50,7 +50,7 @@ bool make_bwd_plan(const Problem &p, BwdPlan *out) {
     // widest dstate tile each pass's registers and one CU's LDS hold
     auto widest = [&](int pass, int *dv_out, int *pad_out) {
         for (int dv : {64, 32, 16}) {
-            if (!bwd_dv_ok(p.bf16, pass, p.headdim, dv) || p.dstate % dv != 0) continue;
+            if (!bwd_dv_ok(p.bf16, p.headdim, dv) || p.dstate % dv != 0) continue;
             for (int pad : {8, 0}) {
                 if (bwd_pass_lds(p, pass, dv, pad) != 0) {
                     *dv_out = dv;

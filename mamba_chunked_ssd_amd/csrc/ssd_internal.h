@@ -150,10 +150,9 @@ struct BwdPassLaunch {
     int lds_pad; // LDS row padding in elements (0 or 8)
     int xt_lds;  // dx pass: x tile, dC pass: C tile staged in LDS (needs the room)
 };
-// Column tiles of the dB (pass 1) and dC (pass 2) passes that their
-// registers hold without spilling (the rule of kb_pass_inst.h's bc_dv_ok).
-inline bool bwd_dv_ok(bool bf16, int pass, int64_t P, int dv) {
-    (void)pass;
+// Column tiles of the dB and dC passes that their registers hold (the rule
+// of kb_pass_inst.h's bc_dv_ok).
+inline bool bwd_dv_ok(bool bf16, int64_t P, int dv) {
     return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
 }
 // LDS bytes a pass block needs; 0 if it does not fit one CU.
