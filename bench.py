@@ -318,11 +318,23 @@ def bwd_stage_model(w) -> dict:
     m["adjoint_chunk_state"] = (x + bc + seq + states, 2.0 * B * L * NH * N * P)
     m["adjoint_carry"] = (3 * states + 4 * B * NH * P * N, 0.0)
     m["score_tiles"] = (2 * bc + st, 2.0 * B * NC * G * tri * N)
+    if w.dtype != "bf16":
+        # fp32 inputs: each head's decayed x . dy tiles are computed here once
+        # (x and dy read, the tiles and their transposes written), and the dB,
+        # dC and W passes read them instead of recomputing the scores
+        ptiles = 2 * 4 * units * (T // 16) * (T // 16 + 1) // 2 * 256
+        m["score_tiles"] = (2 * bc + st + 2 * x + ptiles, 2.0 * B * NC * G * tri * N + 2.0 * units * tri * P)
     m["dx_pass"] = (st + 2 * x + bc + states + 4 * tok_h * P + 3 * 4 * tok_h, 2.0 * units * (tri * P + T * N * P))
     bwd_bc = 2.0 * units * (tri * P + tri * N + T * P * N)
     m["dB_pass"] = (2 * x + bc + states + 4 * B * L * G * N, bwd_bc)
     m["dC_pass"] = (2 * x + 2 * bc + states + 4 * B * L * G * N + 4 * tok_h, bwd_bc)
     m["w_sums"] = (2 * x + st + 8 * tok_h, 2.0 * units * tri * P)
+    if w.dtype != "bf16":
+        ptile_one = 4 * units * (T // 16) * (T // 16 + 1) // 2 * 256
+        no_scores = 2.0 * units * (tri * N + T * P * N)
+        m["dB_pass"] = (x + ptile_one + bc + states + 4 * B * L * G * N, no_scores)
+        m["dC_pass"] = (x + ptile_one + 2 * bc + states + 4 * B * L * G * N + 4 * tok_h, no_scores)
+        m["w_sums"] = (ptile_one + st + 8 * tok_h, 0.0)
     m["token_finish"] = ((4 * 4 + 8 + 4) * tok_h, 0.0)
     m["reduce"] = (2 * 4 * B * L * G * N * 2, 0.0)
     return m

@@ -343,7 +343,9 @@ ssd_status ssd_chunk_scan_bwd(const ssd_shape *shape,
 /* As ssd_chunk_scan_bwd, with 2 * SSD_BWD_STAGES valid hipEvent_t recorded
  * by the stages' own dispatches (start, stop per stage), stages in order:
  * 0 cumsum, 1 chunk states, 2 state passing (the recomputed forward states),
- * 3 adjoint chunk terms, 4 reverse carry, 5 score tiles, 6 dx pass, 7 dB
+ * 3 adjoint chunk terms, 4 reverse carry, 5 score tiles (the B . C tiles
+ * of each group; for fp32 inputs also each head's decayed x . dy tiles, the
+ * stage's two events then spanning two launches), 6 dx pass, 7 dB
  * pass, 8 dC pass, 9 the sums of the decay-gradient matrix, 10 per-token
  * finish (ddt), 11 reductions (dB, dC, dA, dD).  A stage with nothing to do
  * records both its events back to back. */

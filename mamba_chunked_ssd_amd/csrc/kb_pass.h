@@ -85,7 +85,28 @@
 namespace ssd {
 namespace bwd {
 
-enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3 };
+enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3, kPassP = 4 };
+
+// fp32 problems: pass P stores each head's decayed scores once,
+//   P_ab = exp2(G2_b - G2_a) (x_a . dy_b),  a <= b (0 for a > b),
+// as 16 x 16 fp32 tiles (a-strip I <= b-strip J), row-major [a][b] for passes
+// B and W (row a, key b) and transposed times dt_a, [b][a], for pass C (row b,
+// key a), so that every pass reads its tile with one 16-byte load per lane;
+// passes B, C and W read them instead of staging K and recomputing the
+// scores with three-term splits.  That frees the
+// registers the three-term Q fragments held in the key loop and the LDS of the
+// K tile, so the fp32 dB and dC passes take 64-column dstate tiles instead of
+// 16 and do not redo the scores for each.  bf16 problems recompute the scores
+// (one-term fragments are cheap, and the tiles would cost more memory traffic
+// than they save).
+template <typename In, int PASS>
+__host__ __device__ constexpr bool kb_ptiles() {
+    return !std::is_same<In, uint16_t>::value && (PASS == kPassB || PASS == kPassC || PASS == kPassW);
+}
+// whether a pass stages the chunk's K rows in LDS
+__host__ __device__ constexpr bool kb_stages_k(int pass, bool f32_in) {
+    return pass == kPassP || (pass != kPassQ && !f32_in);
+}
 
 // 16-row strips per wave (bwd_spw, shared with the host in ssd_internal.h):
 // 2 pairs strip w with strip n - 1 - w (T/32 waves, the pair's K and V
@@ -114,10 +135,13 @@ struct PassArgs {
     float *xq, *xqi, *dyx;          // pass Q (parts = its dv-tiles): x . q, x . (state term of q), dy . x
     float *cdi;                     // pass C (parts = its dv-tiles): C . (state term of dC)
     double *wd;                     // pass W (one part): W's row sum minus its column sum
+    float *pt, *ptt;                // fp32 problems: the decayed score tiles of each (batch, head, chunk),
+                                    // row-major and transposed times dt
     int64_t seqlen, Lp;
     int batch, NH, P, N, G, HPG, T, NC, hb, nhb, nvt;
     int krow, vrow, erow;           // LDS row strides (elements)
     int xt_lds;                     // pass Q: x tile, pass C: C tile staged in LDS (else read from memory)
+    int *occ;                       // host only: when set, the launch reports blocks per CU instead
 };
 
 // LDS bytes of one block: tables (G2 hi, G2 lo, dt, key factors), K (passes B and C) and V
@@ -127,10 +151,11 @@ __host__ __device__ inline int kb_lds_bytes(int pass, bool f32_in, int T, int P,
                                             int vrow, int erow, bool xt) {
     const int esz = f32_in ? 4 : 2;
     int bytes = 16 * T;  // G2 hi, G2 lo, dt, key factors
-    if (pass != kPassQ) bytes += T * krow * esz;
+    if (kb_stages_k(pass, f32_in)) bytes += T * krow * esz;
     // pass W: one part per wave of W's row sums and the column sums, fp64,
     // summed in the block before they are written
     if (pass == kPassW) return bytes + 8 * T * (T / 16 / bwd_spw(kPassW, !f32_in, P / 32) + 1);
+    if (pass == kPassP) return bytes;
     bytes += T * vrow * esz;
     const int erows = pass == kPassQ ? DV : P;
     bytes += erows * erow * 4;
@@ -325,6 +350,8 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
     // bf16 problems sum in fp32 (dA error 1.2e-5 of its rms, against a 2e-2
     // bound; emulated on a bf16 problem of the 2.7B layer's head shapes).
     typedef typename std::conditional<std::is_same<In, uint16_t>::value, float, double>::type WAcc;
+    constexpr bool kPT = kb_ptiles<In, PASS>();  // scores from the stored tiles
+    constexpr bool kKS = kb_stages_k(PASS, !std::is_same<In, uint16_t>::value);
     constexpr int NI = IO::NI, NF = IO::NF, NP = IO::NP;
     constexpr int NCT = DV / 16;
     extern __shared__ __align__(16) unsigned char lds[];
@@ -368,13 +395,14 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
     float *dtt = g2l + T;
     float *kft = dtt + T;  // key factors of the off-diagonal tiles (see below)
     L *KS = reinterpret_cast<L *>(kft + T);
-    L *VS = KS + (PASS == kPassQ ? 0 : T * a.krow);
+    const int kelems = kKS ? T * a.krow : 0;
+    L *VS = KS + kelems;
     unsigned char *ES = reinterpret_cast<unsigned char *>(VS + T * a.vrow);
     const int erows = PASS == kPassQ ? DV : a.P;
     L *XS = reinterpret_cast<L *>(ES + erows * a.erow * 4);  // x (pass Q) or C (pass C) tile, if staged
     // pass W: nwv parts of W's row sums, then its column sums, T doubles each
     const int nwv = T / 16 / kSPW;
-    double *wsum = reinterpret_cast<double *>(KS + T * a.krow);
+    double *wsum = reinterpret_cast<double *>(KS + kelems);
 
     const In *xin = static_cast<const In *>(a.x);
     const In *dyin = static_cast<const In *>(a.dy);
@@ -427,6 +455,9 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
         const int64_t pbase = ((int64_t)vt * a.batch * a.NH + bh) * a.Lp + t0;        // part vt of the token sums
         const unsigned char *sbase =
             static_cast<const unsigned char *>(PASS == kPassC ? a.H : a.E) + (bh * a.NC + c) * ssz;
+        // this head's stored score tiles (fp32 problems), and their transposes
+        float *ptile = a.pt + (bh * a.NC + c) * (int64_t)(n * (n + 1) / 2) * 256;
+        float *ptilet = a.ptt + (bh * a.NC + c) * (int64_t)(n * (n + 1) / 2) * 256;
         if constexpr (PASS == kPassQ) {
             stage_rows<L>(VS, a.vrow, reinterpret_cast<const L *>(dyin + rowbase + vt * DV), NHP, T, vrows, DV, DV,
                           tid, nthr);
@@ -436,10 +467,11 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             // E_c rows p of this dv-tile, all dstate columns (zero past dstate)
             stage_state<In>(ES, a.erow, sbase, a.P, a.N, vt * DV, DV, 0, (a.N + 31) & ~31, a.N, tid, nthr);
         } else {
-            stage_rows<L>(KS, a.krow, reinterpret_cast<const L *>((PASS == kPassC ? xin : dyin) + rowbase), NHP, T,
-                          vrows, a.P, a.P, tid, nthr);
+            if constexpr (kKS)
+                stage_rows<L>(KS, a.krow, reinterpret_cast<const L *>((PASS == kPassC ? xin : dyin) + rowbase), NHP,
+                              T, vrows, a.P, a.P, tid, nthr);
             // E_c (pass B) or h_c (pass C): all rows p, the tile's columns
-            if constexpr (PASS != kPassW)
+            if constexpr (PASS == kPassB || PASS == kPassC)
                 stage_state<In>(ES, a.erow, sbase, a.P, a.N, 0, a.P, vt * DV, DV, DV, tid, nthr);
         }
         __syncthreads();
@@ -461,7 +493,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
         for (int k = 0; k < kSPW; ++k) {
             const int I = strips[k];
             const int r = 16 * I + l16;  // this lane's row for the score / A-operand layout
-            if constexpr (PASS != kPassQ) {
+            if constexpr (PASS != kPassQ && !(kPT && PASS == kPassW)) {
                 const In *qsrc = (PASS == kPassC ? dyin : xin) + rowbase + (int64_t)r * NHP + 8 * g4;
 #pragma unroll
                 for (int kk = 0; kk < NKQ; ++kk) {
@@ -475,7 +507,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             // decay between this lane's row and the near end of its strip (<= 1)
             rfac[k] = PASS == kPassC ? fast_exp2((grh[k] - g2h[16 * I]) + (grl[k] - g2l[16 * I]))
                                      : fast_exp2((g2h[16 * I + 15] - grh[k]) + (g2l[16 * I + 15] - grl[k]));
-            if constexpr (PASS != kPassW) {
+            if constexpr (PASS != kPassW && PASS != kPassP) {
                 // state term: Oi = Q Hm^T, scaled per row by exp2(e_r)
                 floatx4 Oi[NCT];
 #pragma unroll
@@ -574,12 +606,12 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
             // the pair's V fragments and (bf16) K fragments of its two key
             // strips, read once for both strips of the wave
             Frag<NI> vf[NCT];
-            if constexpr (PASS != kPassW) {
+            if constexpr (PASS != kPassW && PASS != kPassP) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) vf[ct] = IO::col8(VS, a.vrow, 16 * J0, 16 * J0 + 16, 16 * ct, g4, l16);
             }
             Frag<NI> kfr[2][NKQ];
-            if constexpr (PASS != kPassQ && NI == 1) {
+            if constexpr (kKS && NI == 1) {
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -597,7 +629,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                 for (int jj = 0; jj < 2; ++jj) {
                     const int J = J0 + jj;
                     floatx4 S = zero4();
-                    if (act && (PASS == kPassC ? (J <= I) : (J >= I))) {
+                    if (!kPT && act && (PASS == kPassC ? (J <= I) : (J >= I))) {
                         if constexpr (PASS == kPassQ) {
                             const int tile = I * n - (I * (I - 1)) / 2 + (J - I);
                             S = *reinterpret_cast<const floatx4 *>(a.ST + ((stb + tile) * 64 + l) * 4);
@@ -627,7 +659,27 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                     const int J = J0 + jj;
                     const floatx4 S = Sall[k][jj];
                     const bool live = PASS == kPassC ? (J <= I) : (J >= I);
-                    if (J == I) {
+                    if constexpr (kPT) {
+                        // the stored tiles: (I, J) row-major for passes B and W
+                        // (row r = a, key s = b); (J, I) transposed, times dt_s, for
+                        // pass C (row r = b, key s = a).  Entries with a > b are 0.
+                        if (live) {
+                            if constexpr (PASS == kPassC) {
+                                const floatx4 v = *reinterpret_cast<const floatx4 *>(
+                                    ptilet + (J * n - (J * (J - 1)) / 2 + (I - J)) * 256 + l16 * 16 + 4 * g4);
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) pv[4 * jj + i] = v[i];
+                            } else {
+                                const floatx4 v = *reinterpret_cast<const floatx4 *>(
+                                    ptile + (I * n - (I * (I - 1)) / 2 + (J - I)) * 256 + l16 * 16 + 4 * g4);
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) pv[4 * jj + i] = v[i];
+                            }
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) pv[4 * jj + i] = 0.f;
+                        }
+                    } else if (J == I) {
                         // the diagonal tile: exact exponents, masked (select before exp2)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -685,7 +737,22 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                         }
                     }
                 }
-                if constexpr (PASS != kPassW) {
+                if constexpr (PASS == kPassP) {
+                    // store the decayed scores: tile (I, J), row a = r, keys b;
+                    // and the transposed tile, [b][a], times dt_a
+                    const float da = dtt[r];
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int J = J0 + jj;
+                        if (J >= I) {
+                            const int64_t to = (I * n - (I * (I - 1)) / 2 + (J - I)) * 256;
+                            *reinterpret_cast<floatx4 *>(ptile + to + l16 * 16 + 4 * g4) =
+                                floatx4{pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) ptilet[to + (4 * g4 + i) * 16 + l16] = pv[4 * jj + i] * da;
+                        }
+                    }
+                } else if constexpr (PASS != kPassW) {
                     const Frag<NP> pf = split8<NP>(pv);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) O[k][ct] = mmf<NP, NI>(pf, vf[ct], O[k][ct]);
@@ -740,7 +807,7 @@ __global__ __launch_bounds__(kb_threads(PASS, std::is_same<In, uint16_t>::value,
                         a.dyx[ti] = dyx[i];
                     }
                 }
-            } else {
+            } else if constexpr (PASS == kPassB || PASS == kPassC) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float sc = PASS == kPassB ? dtt[16 * I + 4 * g4 + i] : 1.f;

@@ -12,18 +12,22 @@ hipError_t launch_one(const PassArgs &a, unsigned blocks, size_t lds, hipStream_
     constexpr auto kern = kb_pass<In, NKQ, DV, PASS>;
     const hipError_t st = allow_lds<kern>(lds);
     if (st != hipSuccess) return st;
-    return launch_kernel(kern, dim3(blocks), dim3(kb_threads(PASS, std::is_same<In, uint16_t>::value, NKQ, a.T)), lds, stream, ev, a);
+    const int threads = kb_threads(PASS, std::is_same<In, uint16_t>::value, NKQ, a.T);
+    if (a.occ != nullptr)  // blocks per CU at this LDS size and the kernel's registers
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occ, kern, threads, lds);
+    return launch_kernel(kern, dim3(blocks), dim3(threads), lds, stream, ev, a);
 }
 
 // Whether passes B and C are built with `dv`-column tiles for this input type
-// and headdim: the accumulators (strips per wave x dv / 16 per lane) beside
-// the Q fragments (headdim / 32 x one bf16 term, or three for fp32 inputs)
-// fit the waves' registers (256 at two strips per wave, 128 at one, where a
-// block holds 16 waves; at one strip the widest tiles spill a few values)
-// only up to this width.  The host applies the same rule (bwd_dv_ok in
-// ssd_internal.h).
+// and headdim.  bf16: the accumulators (strips per wave x dv / 16 per lane)
+// beside the Q fragments (headdim / 32, one bf16 term) fit the waves'
+// registers (256 at two strips per wave, 128 at one, where a block holds 16
+// waves; at one strip the widest tiles spill a few values) only up to this
+// width.  fp32: the scores come from the stored tiles, so the three-term Q
+// fragments live only for the state term and 64 columns fit.  The host
+// applies the same rule (bwd_dv_ok in ssd_internal.h).
 __host__ __device__ constexpr bool bc_dv_ok(bool bf16, int P, int dv) {
-    return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
+    return dv <= (bf16 ? (P <= 64 ? 64 : 32) : 64);
 }
 
 // passes B and C: headdim (32 k) and dv-tile dispatch
@@ -61,6 +65,7 @@ hipError_t launch_pass_c(const PassArgs &a, bool bf16, int dv, unsigned blocks, 
                          const LaunchEvents &ev);
 hipError_t launch_pass_w(const PassArgs &a, bool bf16, unsigned blocks, size_t lds, hipStream_t stream,
                          const LaunchEvents &ev);
+hipError_t launch_pass_p(const PassArgs &a, unsigned blocks, size_t lds, hipStream_t stream, const LaunchEvents &ev);
 
 }  // namespace bwd
 }  // namespace ssd

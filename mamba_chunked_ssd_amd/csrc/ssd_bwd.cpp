@@ -9,7 +9,8 @@
 //   3     u_c = sum_r exp(G_r) dy_r C_r^T with the forward's chunk-state
 //         kernel (dy as x, C as B);
 //   4     the reverse carry of the state gradient (kb_aux.hip);
-//   5     the per-group score tiles B_r . C_s (kb_aux.hip);
+//   5     the per-group score tiles B_r . C_s (kb_aux.hip) and, for fp32
+//         problems, each head's decayed x . dy tiles (kb_pass.h, pass P);
 //   6-9   the dx, dB and dC passes and the sums of W (kb_pass.h);
 //   10-11 ddt and the reductions of dB, dC, dA, dD (kb_aux.hip).
 #include <hip/hip_runtime_api.h>
@@ -25,19 +26,18 @@
 namespace ssd {
 namespace {
 
-enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3 };
+enum { kPassQ = 0, kPassB = 1, kPassC = 2, kPassW = 3, kPassP = 4 };
 
 struct BwdPlan {
     int dvq, padq;    // dx pass: headdim columns per block, LDS row padding
     int dvb, padb;    // dB pass: dstate columns per block, padding
     int dvc, padc;    // dC pass: dstate columns per block, padding
-    bool xtq, xtc;    // dx pass: x tile, dC pass: C tile staged in LDS
     int hb, nhb;      // dB and dC passes: heads per block, runs of heads per group
     int nvtq;         // dx pass: column tiles (headdim / dvq)
 };
 
 struct BwdLayout {
-    size_t g2_hi, g2_lo, dt, w, wb, s, h, e, zp, st, xq, xqi, dyx, cdi, wd, dbp, dcp, dap, ddp, total;
+    size_t g2_hi, g2_lo, dt, w, wb, s, h, e, zp, st, pt, ptt, xq, xqi, dyx, cdi, wd, dbp, dcp, dap, ddp, total;
 };
 
 bool make_bwd_plan(const Problem &p, BwdPlan *out) {
@@ -45,7 +45,6 @@ bool make_bwd_plan(const Problem &p, BwdPlan *out) {
     q.dvq = (int)std::min<int64_t>(p.headdim, 64);
     q.padq = bwd_pass_lds(p, kPassQ, q.dvq, 8) != 0 ? 8 : 0;
     if (bwd_pass_lds(p, kPassQ, q.dvq, q.padq) == 0) return false;
-    q.xtq = bwd_pass_lds(p, kPassQ, q.dvq, q.padq, true) != 0;
     q.nvtq = (int)(p.headdim / q.dvq);
     // widest dstate tile each pass's registers and one CU's LDS hold
     auto widest = [&](int pass, int *dv_out, int *pad_out) {
@@ -62,7 +61,6 @@ bool make_bwd_plan(const Problem &p, BwdPlan *out) {
         return false;
     };
     if (!widest(kPassB, &q.dvb, &q.padb) || !widest(kPassC, &q.dvc, &q.padc)) return false;
-    q.xtc = bwd_pass_lds(p, kPassC, q.dvc, q.padc, true) != 0;
     // heads per block of passes B and C: each block stages its group's V tile
     // once and then one head after another; the partial sums it leaves per
     // run of heads cost memory traffic.  One block per CU (LDS), 256 CUs:
@@ -110,6 +108,9 @@ BwdLayout bwd_layout(const Problem &p, const BwdPlan &q) {
     l.e = take(states);
     l.zp = take((size_t)p.batch * p.nheads * p.nchunks * (p.headdim * p.dstate / 256) * sizeof(float));
     l.st = take((size_t)p.batch * p.nchunks * p.ngroups * (n * (n + 1) / 2) * 256 * sizeof(float));
+    // fp32 problems: every head's decayed score tiles (kb_pass.h, pass P)
+    l.pt = take(p.bf16 ? 0 : (size_t)p.batch * p.nheads * p.nchunks * (n * (n + 1) / 2) * 256 * sizeof(float));
+    l.ptt = take(p.bf16 ? 0 : (size_t)p.batch * p.nheads * p.nchunks * (n * (n + 1) / 2) * 256 * sizeof(float));
     const size_t tok = (size_t)p.batch * p.nheads * p.padded_len * sizeof(float);
     l.xq = take(tok * q.nvtq);
     l.xqi = take(tok * q.nvtq);
@@ -131,6 +132,7 @@ ssd_status prepare(const ssd_shape *shape, int64_t chunk, Problem *p, BwdPlan *q
     if (shape->flags != 0) return SSD_ERROR_INVALID_VALUE;
     if (!make_bwd_plan(*p, q)) return SSD_ERROR_UNSUPPORTED;
     if (bwd_pass_lds(*p, kPassW, 16, 0) == 0) return SSD_ERROR_UNSUPPORTED;
+    if (!p->bf16 && bwd_pass_lds(*p, kPassP, 16, 0) == 0) return SSD_ERROR_UNSUPPORTED;
     // the passes address one chunk's rows of dy / x / B / C with 32-bit
     // LDS-sized loops and int block counts
     if (p->batch * p->nchunks * p->ngroups * q->nhb * (p->dstate / std::min(q->dvb, q->dvc)) > 0x7fffffff)
@@ -235,7 +237,6 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         return SSD_ERROR_LAUNCH;
     }
     if (run) {
-        if (launch_bwd_scores(p, B, C, fp(lay.st), stream, events_of(5)) != hipSuccess) return SSD_ERROR_LAUNCH;
         BwdPassLaunch L;
         std::memset(&L, 0, sizeof(L));
         L.x = x;
@@ -253,12 +254,44 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         L.dyx = fp(lay.dyx);
         L.cdi = fp(lay.cdi);
         L.wd = reinterpret_cast<double *>(ws + lay.wd);
+        L.pt = fp(lay.pt);
+        // the dx and dC passes' epilogue tile (x or C) is staged in LDS where
+        // it fits and costs the pass no block per CU (the runtime's occupancy
+        // from the kernel's registers and LDS); else it is read from memory
+        auto xt_pays = [&](BwdPassLaunch Lx) {
+            Lx.xt_lds = 1;
+            if (bwd_pass_lds(p, Lx.pass, Lx.dv, Lx.lds_pad, true) == 0) return false;
+            const int with = bwd_pass_blocks_per_cu(p, Lx);
+            Lx.xt_lds = 0;
+            const int without = bwd_pass_blocks_per_cu(p, Lx);
+            return with == 0 || without == 0 || with >= without;
+        };
+        L.ptt = fp(lay.ptt);
+        // stage 5: the score tiles B . C per group, and for fp32 problems the
+        // decayed x . dy tiles per head (the stage's events span both launches)
+        {
+            const LaunchEvents ev5 = events_of(5);
+            if (p.bf16) {
+                if (launch_bwd_scores(p, B, C, fp(lay.st), stream, ev5) != hipSuccess) return SSD_ERROR_LAUNCH;
+            } else {
+                if (launch_bwd_scores(p, B, C, fp(lay.st), stream, LaunchEvents{ev5.start, nullptr}) != hipSuccess)
+                    return SSD_ERROR_LAUNCH;
+                L.pass = kPassP;
+                L.out = nullptr;
+                L.dv = 16;
+                L.hb = 1;
+                L.lds_pad = bwd_pass_lds(p, kPassP, 16, 8) != 0 ? 8 : 0;
+                L.xt_lds = 0;
+                if (launch_bwd_pass(p, L, stream, LaunchEvents{nullptr, ev5.stop}) != hipSuccess)
+                    return SSD_ERROR_LAUNCH;
+            }
+        }
         L.pass = kPassQ;
         L.out = dx;
         L.dv = q.dvq;
         L.hb = 1;
         L.lds_pad = q.padq;
-        L.xt_lds = q.xtq ? 1 : 0;
+        L.xt_lds = xt_pays(L) ? 1 : 0;
         if (launch_bwd_pass(p, L, stream, events_of(6)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassB;
         L.out = fp(lay.dbp);
@@ -271,7 +304,7 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         L.out = fp(lay.dcp);
         L.dv = q.dvc;
         L.lds_pad = q.padc;
-        L.xt_lds = q.xtc ? 1 : 0;
+        L.xt_lds = xt_pays(L) ? 1 : 0;
         if (launch_bwd_pass(p, L, stream, events_of(8)) != hipSuccess) return SSD_ERROR_LAUNCH;
         L.pass = kPassW;
         L.out = nullptr;

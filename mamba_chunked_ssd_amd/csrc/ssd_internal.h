@@ -132,7 +132,8 @@ __host__ __device__ constexpr int bwd_spw(int pass, bool bf16, int nkq) {
 }
 
 // One of the MFMA passes (kb_pass.h): 0 = dx and the per-token dot products,
-// 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16).
+// 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16),
+// 4 = the decayed score tiles of fp32 problems (dv 16, unused).
 struct BwdPassLaunch {
     int pass;
     const void *x, *dy, *B, *C;
@@ -145,6 +146,7 @@ struct BwdPassLaunch {
     float *out;
     float *xq, *xqi, *dyx, *cdi;  // per-token partial sums (kb_pass.h)
     double *wd;
+    float *pt, *ptt;  // fp32 problems: decayed score tiles and their transposes (written by pass 4, read by 1-3)
     int dv;      // columns per block (16, 32 or 64)
     int hb;      // heads per block
     int lds_pad; // LDS row padding in elements (0 or 8)
@@ -153,11 +155,14 @@ struct BwdPassLaunch {
 // Column tiles of the dB and dC passes that their registers hold (the rule
 // of kb_pass_inst.h's bc_dv_ok).
 inline bool bwd_dv_ok(bool bf16, int64_t P, int dv) {
-    return dv <= (bf16 ? (P <= 64 ? 64 : 32) : (P <= 64 ? 32 : 16));
+    return dv <= (bf16 ? (P <= 64 ? 64 : 32) : 64);
 }
 // LDS bytes a pass block needs; 0 if it does not fit one CU.
 size_t bwd_pass_lds(const Problem &p, int pass, int dv, int lds_pad, bool xt = false);
 hipError_t launch_bwd_pass(const Problem &p, const BwdPassLaunch &L, hipStream_t stream, const LaunchEvents &ev);
+// Blocks of a pass (as launch_bwd_pass would run it) that one CU holds at
+// once, from the kernel's registers and LDS; 0 if the runtime cannot say.
+int bwd_pass_blocks_per_cu(const Problem &p, const BwdPassLaunch &L);
 
 // The per-token partial sums the passes leave, (parts, batch, nheads, Lp).
 struct BwdTokens {

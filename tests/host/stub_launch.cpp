@@ -61,13 +61,15 @@ hipError_t launch_bwd_carry(const Problem &, const float *, const void *, G2View
     g_bwd_launches++;
     return hipSuccess;
 }
-// the LDS rule of the pass kernels: tables, K (passes 1, 2), V, state tile
+// the LDS rule of the pass kernels: tables, K (pass 4, and passes 1-3 of bf16
+// problems), the W sums' parts (pass 3), V, state tile
 size_t bwd_pass_lds(const Problem &p, int pass, int dv, int pad, bool xt) {
     const int64_t esz = p.bf16 ? 2 : 4;
     const int64_t T = p.chunk, P = p.headdim;
     int64_t bytes = 16 * T;
-    if (pass != 0) bytes += T * (P + pad) * esz;
-    if (pass == 3) return bytes <= (int64_t)kLdsPerCu ? (size_t)bytes : 0;
+    if (pass == 4 || (pass != 0 && p.bf16)) bytes += T * (P + pad) * esz;
+    if (pass == 3) bytes += 8 * T * (T / 32 + 1);
+    if (pass == 3 || pass == 4) return bytes <= (int64_t)kLdsPerCu ? (size_t)bytes : 0;
     bytes += T * (dv + pad) * esz;
     const int64_t erow = pass == 0 ? (p.dstate + 31) / 32 * 32 + pad : dv + pad;
     bytes += (pass == 0 ? dv : P) * erow * 4;
@@ -78,6 +80,7 @@ hipError_t launch_bwd_pass(const Problem &, const BwdPassLaunch &, hipStream_t, 
     g_bwd_launches++;
     return hipSuccess;
 }
+int bwd_pass_blocks_per_cu(const Problem &, const BwdPassLaunch &) { return 0; }
 hipError_t launch_bwd_tokens(const Problem &, const BwdTokens &, const float *, const float *, const float *, float *,
                              float *, float *, hipStream_t, const LaunchEvents &) {
     g_bwd_launches++;
