@@ -130,6 +130,10 @@ hipError_t launch_bwd_carry(const Problem &p, const float *U, const void *H, G2V
 __host__ __device__ constexpr int bwd_spw(int pass, bool bf16, int nkq) {
     return bf16 && (pass == 0 || pass == 1 || (pass == 2 && nkq <= 2)) ? 1 : 2;
 }
+// waves of one block of a backward pass
+inline int kb_pass_waves(const Problem &p, int pass) {
+    return (int)(p.chunk / 16) / bwd_spw(pass, p.bf16, (int)(p.headdim / 32));
+}
 
 // One of the MFMA passes (kb_pass.h): 0 = dx and the per-token dot products,
 // 1 = dB partials, 2 = dC partials, 3 = the row and column sums of W (dv 16),
