@@ -50,7 +50,7 @@ MEASURED_TRAFFIC = {
         ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), 'd335e9eacd803fb6', 24143.0, 48386.0),
     # backward (the y dtype and state path do not apply)
     ("mamba2_2p7b_layer_bf16", None, "bwd:dC_pass", None): (
-        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h', 'ssd_internal.h'), '9063d51874cc4cdd', 85933.3, 50688.0),
+        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h', 'ssd_internal.h'), '6b0e4799ddeb3f4a', 85605.8, 50688.0),
 }
 
 
@@ -143,12 +143,50 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+def gpu_clocks():
+    """Shader and memory clock levels of the first AMD GPU as the amdgpu
+    driver lists them in sysfs (pp_dpm_sclk, pp_dpm_mclk): the highest level
+    and the one marked current.  Read from files, not from a tool, so that no
+    child process starts after the GPU is in use."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        out = {}
+        for key in ("sclk", "mclk"):
+            try:
+                with open(os.path.join(dev, "pp_dpm_" + key)) as f:
+                    lines = [ln.strip() for ln in f if ":" in ln]
+            except OSError:
+                continue
+            mhz = []
+            cur = None
+            for ln in lines:
+                v = ln.split(":", 1)[1].strip()
+                num = "".join(ch for ch in v.split()[0] if ch.isdigit())
+                if not num:
+                    continue
+                mhz.append(int(num))
+                if v.endswith("*"):
+                    cur = int(num)
+            if mhz:
+                out[key + "_max_MHz"] = max(mhz)
+                out[key + "_current_MHz"] = cur
+        if out:
+            return out
+    return None
+
+
 def context(hip, dev) -> dict:
     """What this machine reaches beside the datasheet peaks: a device copy of
     1 GiB from a source that a second 1 GiB write has evicted from L2 and the
     Infinity Cache (bytes read plus written over the copy's own events,
-    median of 5), and the GPU clocks rocm-smi reports (null if it cannot)."""
-    import subprocess
+    median of 5), and the GPU clock levels the driver lists (null if it
+    cannot)."""
     import torch
     n = 1 << 28
     src = torch.empty(n, dtype=torch.float32, device=dev)
@@ -169,14 +207,7 @@ def context(hip, dev) -> dict:
         hip.destroy(e1)
     del src, dst, flush
     t = sorted(times)[len(times) // 2]
-    clocks = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        if r.returncode == 0:
-            card = next(iter(json.loads(r.stdout).values()))
-            clocks = {k: v for k, v in card.items() if "clock" in k.lower()}
-    except Exception:  # the tool is context only
-        clocks = None
+    clocks = gpu_clocks()
     return {"copy_GB_s": round(2 * n * 4 / t / 1e9, 1), "copy_bytes": 2 * n * 4,
             "copy_note": "torch device copy, 1 GiB read + 1 GiB written, cold source",
             "gpu_clocks": clocks}
@@ -193,9 +224,10 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
+def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0, single=None) -> dict:
     """The fp64 oracle, as it stands, on this host's cores: the whole workload,
-    repeated (at least ``reps`` times) until ``min_seconds`` of CPU work."""
+    repeated (at least ``reps`` times) until ``min_seconds`` of CPU work.
+    ``single``: the one-thread figures of single_thread_oracle, taken earlier."""
     import oracle
     ncores = len(os.sched_getaffinity(0))
     oracle.scan(inp["x"][:, :64], inp["dt"][:, :64], inp["A"], inp["B"][:, :64], inp["C"][:, :64])
@@ -207,7 +239,6 @@ def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
         times.append(time.perf_counter() - t0)
     med = float(sorted(times)[len(times) // 2])
     threads = int(os.environ.get("OMP_NUM_THREADS", ncores))
-    single = single_thread_oracle(w)
     return {
         "value": w.tokens / med,
         "unit": "tokens/s",
@@ -226,7 +257,8 @@ def cpu_baseline(w, inp, reps: int, min_seconds: float = 10.0) -> dict:
 def single_thread_oracle(w) -> dict:
     """The oracle on one thread (OMP_NUM_THREADS=1, in a child process so the
     OpenMP runtime starts with that setting) for the tiny workload and for
-    ``w``: tokens/s of one run each."""
+    ``w``: tokens/s of one run each.  Called before this process touches the
+    GPU: no program is started after that."""
     import subprocess
     out = {}
     for name in dict.fromkeys(["tiny_f32", w.name]):
@@ -456,10 +488,13 @@ def main(argv=None):
     import mamba_chunked_ssd_amd as ssd
     import ssd_inputs as si
 
+    w = si.BY_NAME[a.workload]
+    # the one-thread oracle runs in child processes, started before the GPU
+    # is initialised (torch.cuda.is_available() does that)
+    single = None if a.no_cpu_baseline else single_thread_oracle(w)
     if not torch.cuda.is_available():
         print("bench.py: no ROCm GPU visible", file=sys.stderr)
         return 2
-    w = si.BY_NAME[a.workload]
     inp = si.generate(w)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -650,7 +685,7 @@ def main(argv=None):
         out["backward"] = backward_bench(hip, w, inp, t, dev, steps=a.bwd_steps)
 
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_reps, a.cpu_seconds, single)
     print(json.dumps(out), flush=True)
     return 0
 
