@@ -84,11 +84,12 @@ def stage_model(w, y_bytes: int, fused: bool = False) -> dict:
     states = 4 * B * NH * NC * P * N
     init = 4 * B * NH * P * N if w.init_std > 0 else 0
     final = 4 * B * NH * P * N
-    # bf16, headdim 64, dstate 128: the state-passing launch also reads B and C
-    # and writes the chunks' C B^T tiles (T/32 x (T/16 + 2) tiles of 1 KiB per
-    # chunk and group), which the chunk output reads in place of B
+    # bf16, headdim 64, dstate 128 (or 256 at chunk 256): the state-passing
+    # launch also reads B and C and writes the chunks' C B^T tiles (T/32 x
+    # (T/16 + 2) tiles of 1 KiB per chunk and group), which the chunk output
+    # reads in place of B
     cb_tiles = B * NC * G * (T // 32) * (T // 16 + 2) * 1024 if (
-        w.dtype == "bf16" and P == 64 and N == 128) else 0
+        w.dtype == "bf16" and P == 64 and (N == 128 or (N == 256 and T == 256))) else 0
     bc = B * L * G * N * e
     m = {
         "chunk_cumsum": (tok_h * (e + 4), 0.0),

@@ -105,9 +105,10 @@ typedef struct {
  *       nchunks, headdim, dstate).  bf16 problems: per (batch, head, chunk) a
  *       hi plane then a lo plane of (headdim, dstate) bf16 with hi = bf16(h_c),
  *       lo = bf16(h_c - hi); always a region of its own.
- *   CB  bf16 problems with headdim 64 and dstate 128 only (otherwise empty:
- *       cb == total): the fp32 products S_ij = C_i . B_j of each chunk, per
- *       (batch, chunk, group) T/32 x (T/16 + 2) tiles of 64 lanes x 4 floats.
+ *   CB  bf16 problems with headdim 64 and dstate 128, or dstate 256 at chunk
+ *       256, only (otherwise empty: cb == total): the fp32 products
+ *       S_ij = C_i . B_j of each chunk, per (batch, chunk, group) T/32 x
+ *       (T/16 + 2) tiles of 64 lanes x 4 floats.
  *       Tile k of row w holds the 16 x 16 block (I, J) with I = w, J = k when
  *       k < b = (w + 2) & ~1, else I = T/16 - 1 - w, J = k - b; lane
  *       l = 16 q + m, element r holds S_ij for i = 16 I + m, j = 16 J + 4 q + r

@@ -42,8 +42,9 @@
 //    chunk-output stage reads (hi = bf16(h), lo = bf16(h - hi)); the final
 //    state is fp32.  Chunk decays exp2(G2_last) for 256 chunks at a time sit
 //    in registers (64 per register, read back with readlane).
-//  * For bf16 problems with headdim 64 and dstate 128, extra blocks at the
-//    front of the grid compute the chunk output's C B^T tiles.
+//  * For bf16 problems with headdim 64 and dstate 128 (or 256 at chunk 256),
+//    extra blocks at the front of the grid compute the chunk output's C B^T
+//    tiles.
 #include "k_cb_tiles.h"
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(64 * (P / 16 + 1)) void k23_state_fused_bf16(
     const float *__restrict__ G2hi, const float *__restrict__ G2lo, const float *__restrict__ init,
     uint16_t *__restrict__ H, float *__restrict__ final_states, int64_t L, int NH, int N, int G,
     int NC, int64_t Lp, int HPG, int ntiles, int nfused,
-    // C B^T tiles (headdim 64, dstate 128; ncb = 0 otherwise)
+    // C B^T tiles (the problems of uses_cb_tiles; ncb = 0 otherwise)
     const uint16_t *__restrict__ Cm, float *__restrict__ CB, int64_t cb_ntiles, int ncb) {
     using Cfg = FusedCfg<T, P, NT>;
     constexpr int NCW = Cfg::NCW, RING = Cfg::RING, KP = Cfg::KP, SPC = Cfg::SPC, MT = Cfg::MT;
@@ -158,7 +159,12 @@ __global__ __launch_bounds__(64 * (P / 16 + 1)) void k23_state_fused_bf16(
 
     if constexpr (P == 64) {
         if ((int)blockIdx.x < ncb) {
-            if (threadIdx.x < 256) cb_tiles<T>(Bm, Cm, CB, L, G, NC, cb_ntiles, ncb);
+            if (threadIdx.x < 256) {
+                if (N == 256)
+                    cb_tiles<T, 256>(Bm, Cm, CB, L, G, NC, cb_ntiles, ncb, blockIdx.x);
+                else
+                    cb_tiles<T, 128>(Bm, Cm, CB, L, G, NC, cb_ntiles, ncb, blockIdx.x);
+            }
             return;
         }
     }

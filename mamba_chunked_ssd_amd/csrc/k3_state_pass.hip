@@ -23,9 +23,10 @@
 //
 // The same launch also computes, in extra blocks at the front of the grid,
 // the C B^T tiles that the chunk output reads (bf16 problems with headdim 64
-// and dstate 128): a little MFMA work that depends only on B and C, so it runs
-// beside the memory-bound stream instead of on the chunk output's critical
-// path ("Mamba-2 architecture": the C B^T factor of the chunk output).
+// and dstate 128, or dstate 256 at chunk 256): MFMA work that depends only on
+// B and C, so it runs beside the memory-bound stream instead of on the chunk
+// output's critical path ("Mamba-2 architecture": the C B^T factor of the
+// chunk output).
 #include <climits>
 
 #include "k_cb_tiles.h"
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(256) void k3_state_pass(const float *S, float *H,
                                     blockIdx.x);
 }
 
-template <int T, int kDepth>
+// kRows: dstate 256, the tiles by slot rows (cb_rows; `ntiles` counts its
+// tasks); otherwise dstate 128, one tile per wave step (cb_tiles).
+template <int T, int kDepth, bool kRows>
 __global__ __launch_bounds__(256) void k3_state_pass_cb(const float *S, float *H,
                                                         const float *__restrict__ G2hi,
                                                         const float *__restrict__ G2lo,
@@ -111,11 +114,16 @@ __global__ __launch_bounds__(256) void k3_state_pass_cb(const float *S, float *H
                                                         const uint16_t *__restrict__ Cm,
                                                         float *__restrict__ CB, int64_t seqlen,
                                                         int G, int64_t ntiles, int ncb) {
-    if ((int)blockIdx.x < ncb)
-        cb_tiles<T>(Bm, Cm, CB, seqlen, G, nchunks, ntiles, ncb);
-    else
+    const int bx = (int)blockIdx.x;
+    if (bx < ncb) {
+        if constexpr (kRows)
+            cb_rows<T, 256>(Bm, Cm, CB, seqlen, G, nchunks, ntiles, ncb, bx);
+        else
+            cb_tiles<T, 128>(Bm, Cm, CB, seqlen, G, nchunks, ntiles, ncb, bx);
+    } else {
         state_pass_body<kDepth, true>(S, H, G2hi, G2lo, init, final_states, n_vec, pn_vec, nchunks, Lp,
-                                      T, (int64_t)blockIdx.x - ncb);
+                                      T, (int64_t)bx - ncb);
+    }
 }
 
 }  // namespace
@@ -133,22 +141,30 @@ hipError_t launch_state_pass(const Problem &p, const float *S, float *H, G2View 
     const bool deep = p.nchunks > 128;
     const int64_t ntiles = (uses_cb_tiles(p) && CB != nullptr) ? p.batch * p.nchunks * p.ngroups * cb_slots(p.chunk) : 0;
     if (ntiles > 0) {
-        const int64_t ncb = (ntiles + 4 * kCbPerWave - 1) / (4 * kCbPerWave);
-        if (blocks + ncb > INT_MAX) return hipErrorInvalidValue;
+        // dstate 256: one wave per slot row (cb_rows), else kCbPerWave tiles per wave
+        const bool rows = p.dstate == 256;
+        const int64_t units = rows ? p.batch * p.nchunks * p.ngroups * (p.chunk / 32) : ntiles;
+        const int64_t ncb = rows ? (units + 3) / 4 : (ntiles + 4 * kCbPerWave - 1) / (4 * kCbPerWave);
+        // the tile blocks first, then the stream's.  (Placed after the stream,
+        // the tiles were no faster at 65 536 tokens, 32 heads, dstate 256:
+        // the deep stream's 512 blocks fill every CU.)
+        const int64_t total = ncb + blocks;
+        if (total > INT_MAX) return hipErrorInvalidValue;
         const auto *Bm = static_cast<const uint16_t *>(B);
         const auto *Cm = static_cast<const uint16_t *>(C);
-#define SSD_K3_CB(TT, DD)                                                                            \
-    launch_kernel(k3_state_pass_cb<TT, DD>, dim3((unsigned)(blocks + ncb)), dim3(256), 0, stream, ev,  \
-                  S, H, G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len, Bm, \
-                  Cm, CB, p.seqlen, (int)p.ngroups, ntiles, (int)ncb)
-#define SSD_K3_CB_T(TT)          \
-    if (deep)                    \
-        SSD_K3_CB(TT, kDeep);    \
-    else                         \
-        SSD_K3_CB(TT, kShallow);
-        switch (p.chunk) {
-            case 64: SSD_K3_CB_T(64); break;
-            case 128: SSD_K3_CB_T(128); break;
+#define SSD_K3_CB(TT, DD, RR)                                                                          \
+    launch_kernel(k3_state_pass_cb<TT, DD, RR>, dim3((unsigned)total), dim3(256), 0, stream, ev, S, H,   \
+                  G2.hi, G2.lo, init, final_states, n_vec, pn_vec, p.nchunks, p.padded_len, Bm, Cm, CB, \
+                  p.seqlen, (int)p.ngroups, units, (int)ncb)
+#define SSD_K3_CB_T(TT)                                                    \
+    if (deep) {                                                            \
+        if (rows) SSD_K3_CB(TT, kDeep, true); else SSD_K3_CB(TT, kDeep, false); \
+    } else {                                                               \
+        if (rows) SSD_K3_CB(TT, kShallow, true); else SSD_K3_CB(TT, kShallow, false); \
+    }
+        switch (p.chunk) {  // slot rows only at chunk 256 (uses_cb_tiles)
+            case 64: if (deep) SSD_K3_CB(64, kDeep, false); else SSD_K3_CB(64, kShallow, false); break;
+            case 128: if (deep) SSD_K3_CB(128, kDeep, false); else SSD_K3_CB(128, kShallow, false); break;
             case 256: SSD_K3_CB_T(256); break;
             default: return hipErrorInvalidValue;
         }

@@ -1065,7 +1065,8 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path with asynchronous copies (headdim 64, dstate 128)
+// bf16 path with asynchronous copies (headdim 64; dstate 128, or 256 at chunk
+// 256)
 // ---------------------------------------------------------------------------
 // Same computation and tile assignment as k4_chunk_out_bf16, with the per-head
 // data moved by the hardware: the x rows and the h_c hi/lo planes of head
@@ -1080,19 +1081,32 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_f32(
 // skip term's x in the MFMA output layout.  C fragments live in registers.
 // Rows past the sequence end read as zero (the buffer resource ends at the
 // chunk's last valid row).
+//
+// At dstate 256 the h_c planes (64 KiB) fit only once beside the two x
+// buffers, and the C fragments take 64 registers per lane: the h_c planes are
+// single-buffered, every wave takes the inter-chunk term first, and the
+// next head's h_c copies go out after a block barrier behind it, landing
+// during the intra-chunk term; the x rows and tables stay double-buffered.
+// The C fragments then never leave registers, where the general kernel
+// re-reads them from L2 in every head.
 namespace acfg {
-constexpr int P = 64, N = 128, NK = N / 32, PT = P / 16;
+constexpr int P = 64, PT = P / 16;
 }
 
-template <int T>
+template <int T, int N>
 struct AsyncLds {
+    static constexpr bool h_single = N > 128;                 // one h_c buffer
     static constexpr size_t x = (size_t)T * acfg::P * 2;      // row-major x tile
-    static constexpr size_t plane = (size_t)acfg::P * acfg::N * 2;  // one h_c plane
-    static constexpr size_t buf = x + 2 * plane;              // one head's x and h_c
+    static constexpr size_t plane = (size_t)acfg::P * N * 2;  // one h_c plane
+    static constexpr size_t hb = 2 * plane;                   // one head's h_c planes
     static constexpr size_t tab = Tables<T>::bytes;
-    static constexpr size_t total = 2 * buf + 2 * tab;
+    // buffer k's x tile and h_c planes (dstate 128: x and h_c of one head side
+    // by side; dstate 256: both x tiles, then the h_c planes), then the tables
+    static constexpr size_t xoff(int k) { return h_single ? k * x : k * (x + hb); }
+    static constexpr size_t hoff(int k) { return h_single ? 2 * x : k * (x + hb) + x; }
+    static constexpr size_t tab0 = h_single ? 2 * x + hb : 2 * (x + hb);  // buffer k's tables at tab0 + k tab
+    static constexpr size_t total = tab0 + 2 * tab;
     static_assert(total <= kLdsBytes, "async chunk-output LDS budget");
-    static_assert((size_t)T * acfg::N * 2 <= buf, "B rows staged in one buffer");
 };
 
 // x tile (128-byte token rows): 16-byte chunk c of row t is stored at chunk
@@ -1113,40 +1127,47 @@ __device__ __forceinline__ void store_quad(const floatx4 &v, __amdgpu_buffer_rsr
     store_out4<OutT>(yr, lane_off + 16 * I * NHP * ES + 16 * pt * ES, NHP * ES, yv);
 }
 
-// acc holds this head's tile on return.  For the first-half waves it holds
-// the previous head's finished tile on entry, stored through yprev, spread
-// over the inter-chunk MFMAs and the first intra-chunk pairs (a resource of 0
-// bytes drops the stores); the second-half waves store their tile after the
-// call.  pre(s), s = 0 .. 8 (first-half waves), issues piece s of the next
-// head's copies: x and h_c pieces in the inter-chunk steps, the G2 / dt copies
-// after them.  Issued any later, the copies land after the head's MFMAs and
-// the end-of-head wait shows their latency; the stores, which need not land
-// early, are spread further so that the memory queue never fills and blocks
-// the MFMA issue.
-template <int T, int W, typename OutT, typename Pre>
+// acc holds this head's tile on return.  dstate 128: for the first-half
+// waves it holds the previous head's finished tile on entry, stored through
+// yprev, spread over the inter-chunk MFMAs and the first intra-chunk pairs (a
+// resource of 0 bytes drops the stores); the second-half waves store their
+// tile after the call.  pre(s), s = 0 .. 8 (first-half waves), issues piece s
+// of the next head's copies: x and h_c pieces in the inter-chunk steps, the
+// G2 / dt copies after them.  Issued any later, the copies land after the
+// head's MFMAs and the end-of-head wait shows their latency; the stores, which
+// need not land early, are spread further so that the memory queue never
+// fills and blocks the MFMA issue.  dstate 256 (single h_c buffer): every wave
+// stores its tile after the call; the x and G2 / dt pieces go out in the
+// inter-chunk steps, the h_c pieces over the first intra-chunk pairs, after
+// the block barrier that ends every wave's reads of h_c.
+template <int T, int N, int W, typename OutT, typename Pre>
 __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
-                                                const u32x4 (&cfr)[2][acfg::NK],
+                                                const u32x4 (&cfr)[2][N / 32],
                                                 const unsigned char *xt, const unsigned char *hp,
                                                 const Tables<T> &tb, float Dh, int l16, int g4,
                                                 floatx4 (&acc)[2][acfg::PT],
                                                 __amdgpu_buffer_rsrc_t yprev, int NHP, Pre &&pre) {
     using WT = WaveTiles<T, W>;
-    using LD = AsyncLds<T>;
-    constexpr int PT = acfg::PT, NK = acfg::NK;
+    using LD = AsyncLds<T, N>;
+    constexpr int PT = acfg::PT, NK = N / 32;
     constexpr int I0 = WT::I0, I1 = WT::I1;
-    constexpr int XROW = acfg::P * 2, HROW = acfg::N * 2;
-    static_assert(NK == PT, "one (row tile, column tile) pair of stores per step and tile");
+    constexpr int XROW = acfg::P * 2, HROW = N * 2;
+    constexpr bool kSingle = LD::h_single;
+    constexpr bool kIssuer = W < T / 64;  // the waves that issue the next head's copies
+    // the previous head's tile stored during this head (dstate 128, issuers)
+    constexpr bool kDefer = !kSingle && kIssuer;
+    static_assert(kSingle || NK == PT, "one (row tile, column tile) pair of stores per step and tile");
 
     // Waves of the first half take the inter-chunk term first, with the next
     // head's copies and the previous head's stores; waves of the second half
     // (which share SIMDs with the first) take the VALU-heavy intra-chunk term
     // first and store their tile at the end, so each SIMD overlaps one wave's
     // memory traffic with the other's VALU work.
-    constexpr bool kIntraFirst = W >= T / 64;
-    floatx4 prev[2][PT];
+    constexpr bool kIntraFirst = !kSingle && W >= T / 64;
+    floatx4 prev[kDefer ? 2 : 1][kDefer ? PT : 1];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-        if constexpr (!kIntraFirst) {
+        if constexpr (kDefer) {
             prev[0][pt] = acc[0][pt];
             prev[1][pt] = acc[1][pt];
         }
@@ -1173,13 +1194,15 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) a[ii][pt] = mfma_bf16(cfr[ii][ks], hl[pt], a[ii][pt]);
-            if constexpr (!kIntraFirst) {
+            if constexpr (kDefer) {
                 pre(ks);
                 pre(4 + ks);
                 store_quad<OutT>(prev[0][ks], yprev, NHP, I0, ks, l16, g4);
+            } else if constexpr (kSingle && kIssuer && ks % 2 == 0) {
+                pre(ks / 2);  // x pieces only: h_c is still being read
             }
         });
-        if constexpr (!kIntraFirst) pre(8);
+        if constexpr (kIssuer) pre(8);
     };
     // exp2(G2_i) of rows i = 16 I + 4 g4 + r
     auto e2_rows = [&](int ii) {
@@ -1200,6 +1223,7 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kSingle) __syncthreads();  // every wave is done reading this head's h_c
 
     // ---- intra-chunk term
     float mk;  // tile-pair factor of slot k = lane, read back wave-uniformly
@@ -1232,6 +1256,7 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         }
     }
     constexpr int NP = WT::NSLOT / 2;
+    static_assert(!kSingle || NP >= 4, "the h_c pieces go out over the first four pairs");
     struct AOps {
         u32x4 hi, lo;
         u32x4 xb[PT];
@@ -1263,33 +1288,43 @@ __device__ __forceinline__ void head_wave_async(const floatx4 (&S)[T / 16 + 2],
         }
         return o;
     };
+    // dstate 128: the operands of pair q + 1 are built during the MFMAs of
+    // pair q.  dstate 256: the C fragments leave no registers for a second
+    // operand set; each pair's operands are built just before its MFMAs, and
+    // the other wave of the SIMD fills the gap.
     AOps cur = prep(std::integral_constant<int, WT::pair_order(0)>{});
     static_for<NP>([&](auto qc) {
         constexpr int q = WT::pair_order(decltype(qc)::value);
         constexpr int ii = 2 * q < WT::base1 ? 0 : 1;
         constexpr int qn = decltype(qc)::value + 1;
+        if constexpr (kSingle && decltype(qc)::value > 0) cur = prep(std::integral_constant<int, q>{});
         AOps nxt;
-        if constexpr (qn < NP) nxt = prep(std::integral_constant<int, WT::pair_order(qn < NP ? qn : 0)>{});
+        if constexpr (!kSingle && qn < NP)
+            nxt = prep(std::integral_constant<int, WT::pair_order(qn < NP ? qn : 0)>{});
         // the previous head's second row tile goes out over the first pairs
-        if constexpr (!kIntraFirst && decltype(qc)::value < PT)
+        if constexpr (kDefer && decltype(qc)::value < PT)
             store_quad<OutT>(prev[1][decltype(qc)::value], yprev, NHP, I1, decltype(qc)::value, l16, g4);
+        // single h_c buffer: the next head's h_c copies over the first pairs
+        if constexpr (kSingle && kIssuer && decltype(qc)::value < 4) pre(4 + decltype(qc)::value);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.hi, cur.xb[pt], acc[ii][pt]);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ii][pt] = mfma_bf16(cur.lo, cur.xb[pt], acc[ii][pt]);
-        if constexpr (qn < NP) cur = nxt;
-        // Interleave the next pair's VALU work with this pair's MFMAs: a
-        // wave64 VALU op takes 4 cycles and an MFMA 16, so four or five of
-        // them run under each MFMA instead of waiting for the whole group.
+        if constexpr (!kSingle) {
+            if constexpr (qn < NP) cur = nxt;
+            // Interleave the next pair's VALU work with this pair's MFMAs: a
+            // wave64 VALU op takes 4 cycles and an MFMA 16, so four or five of
+            // them run under each MFMA instead of waiting for the whole group.
 #pragma unroll
-        for (int k = 0; k < 2 * PT; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+            for (int k = 0; k < 2 * PT; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     });
     static_for<PT>([&](auto kc) {  // stores left over when there are fewer pairs than tiles
-        if constexpr (!kIntraFirst && decltype(kc)::value >= NP)
+        if constexpr (kDefer && decltype(kc)::value >= NP)
             store_quad<OutT>(prev[1][decltype(kc)::value], yprev, NHP, I1, decltype(kc)::value, l16, g4);
     });
     if constexpr (kIntraFirst) {
@@ -1340,14 +1375,14 @@ __device__ __forceinline__ void token_derived(const Tables<T> &tb, int t) {
     tb.cf[t] = fast_exp2((geh - gh) + (gel - gl)) * tb.dt[t];
 }
 
-template <int T, typename OutT>
+template <int T, int N, typename OutT>
 __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     const uint16_t *__restrict__ x, const float *__restrict__ CBt,
     const uint16_t *__restrict__ Cm, const float *__restrict__ G2hi, const float *__restrict__ G2lo,
     const float *__restrict__ DT, const float *__restrict__ Dv, const uint16_t *__restrict__ H,
     OutT *__restrict__ y, int64_t L, int NH, int G, int NC, int64_t Lp, int HPG, int HB, int nhb) {
-    using LD = AsyncLds<T>;
-    constexpr int P = acfg::P, N = acfg::N, NK = acfg::NK, PT = acfg::PT;
+    using LD = AsyncLds<T, N>;
+    constexpr int P = acfg::P, NK = N / 32, PT = acfg::PT;
     constexpr int NT16 = T / 16;
     constexpr int NSLOT = NT16 + 2;
     constexpr int NW = T / 32;
@@ -1373,13 +1408,13 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     const int NHP = NH * P;
     const uint16_t *Cc = Cm + ((b * L + t0) * G + gi) * N;
 
-    auto tables = [&](int k) {
-        return Tables<T>(reinterpret_cast<float *>(lds + 2 * LD::buf + k * LD::tab));
-    };
+    // (a constant offset from lds plus k tab: the table reads then pair up)
+    auto tables = [&](int k) { return Tables<T>(reinterpret_cast<float *>(lds + LD::tab0 + k * LD::tab)); };
     // ---- copies of one head's x rows, h_c planes, G2 pair and dt into buffer k.
     // x: 1-KiB blocks of 8 token rows; lane l takes 16-byte chunk l % 8 of row
     // 8 q + l / 8, from the global chunk that the row's swizzle puts there.
-    // h_c: 1-KiB blocks of 4 headdim rows of one plane, XOR-swizzled by row.
+    // h_c: 1-KiB blocks of 1024 / (2 N) rows of the two stacked planes, the
+    // 16-byte chunks XOR-swizzled by row.
     // G2 / dt: waves w < T / 64 copy tokens 64 w .. +63 (which they also
     // derive the tables of).
     const uint32_t x_bytes = (uint32_t)(((rows - 1) * NHP + P) * 2);
@@ -1391,11 +1426,15 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
     constexpr int XPW = XQ / MW, HPW = HQ / MW;  // copies per issuing wave
     static_assert(XQ % MW == 0 && HQ % MW == 0 && XPW % 4 == 0 && HPW % 4 == 0, "copy split");
     static_assert(T / 64 == MW, "the issuing waves also derive the tables");
+    constexpr int HCPR = N / 8;                  // 16-byte chunks per h_c row
+    constexpr int HRPK = 64 / HCPR;              // h_c rows per 1-KiB block
+    constexpr int HCSH = N == 128 ? 4 : 5;       // log2(HCPR)
+    static_assert(HCPR == 1 << HCSH, "h_c row chunks");
     auto issue_piece = [&](int h, int k, int s) {
         const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // < MW
         int ln = tid & 63;
         asm volatile("" : "+v"(ln));
-        const uint32_t xb = lds_addr(lds + k * LD::buf);
+        const uint32_t xb = lds_addr(lds + LD::xoff(k));
         if (s < 4) {
             const i32x4 xd = buffer_desc(x + ((b * L + t0) * NH + h) * P, x_bytes);
             const int xr = ln >> 3, xl = ((ln & 7) ^ xswz(ln >> 3)) * 16;
@@ -1407,11 +1446,12 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
         } else if (s < 8) {
             const i32x4 hd = buffer_desc(H + (((int64_t)b * NH + h) * NC + c) * (int64_t)2 * P * N,
                                          (uint32_t)(2 * LD::plane));
+            const uint32_t hbase = LD::h_single ? lds_addr(lds + LD::hoff(k)) : xb + (uint32_t)LD::x;
 #pragma unroll
             for (int kk = (s - 4) * (HPW / 4); kk < (s - 3) * (HPW / 4); ++kk) {
                 const int qh = wu + kk * MW;
-                const int row = 4 * qh + (ln >> 4);  // row of the two stacked planes
-                lds_dma_x4(hd, xb + LD::x + qh * 1024, row * (2 * N) + (((ln & 15) ^ (row & 15)) << 4));
+                const int row = HRPK * qh + (ln >> HCSH);  // row of the two stacked planes
+                lds_dma_x4(hd, hbase + qh * 1024, row * (2 * N) + (((ln & (HCPR - 1)) ^ (row & 15)) << 4));
             }
         } else {
             const int64_t hoff = ((int64_t)b * NH + h) * Lp + t0;
@@ -1471,24 +1511,27 @@ __global__ __launch_bounds__(2 * T) void k4_chunk_out_bf16_async(
         auto pre = [&](int s) {
             if (more) issue_piece(h + 1, cur ^ 1, s);
         };
-        const unsigned char *xt = lds + cur * LD::buf;
         const float Dh = (Dv != nullptr) ? Dv[h] : 0.f;
-        // the previous head's y goes out during this head's first MFMAs
+        // dstate 128: the previous head's y goes out during this head's first MFMAs
         const auto yprev = buffer_rsrc(y + ((b * L + t0) * NH + (i > 0 ? h - 1 : h)) * P,
-                                       i > 0 ? y_bytes : 0u);
+                                       (!LD::h_single && i > 0) ? y_bytes : 0u);
         dispatch_wave<NW>(id.w, [&](auto wc) {
-            head_wave_async<T, decltype(wc)::value, OutT>(S, cfr, xt, xt + LD::x, tables(cur), Dh,
-                                                          id.l16, id.g4, acc, yprev, NHP, pre);
+            head_wave_async<T, N, decltype(wc)::value, OutT>(S, cfr, lds + LD::xoff(cur), lds + LD::hoff(cur),
+                                                             tables(cur), Dh, id.l16, id.g4, acc, yprev, NHP,
+                                                             pre);
         });
         if (issuer) {
             lds_dma_wait();  // this wave's copies of the next head have landed
             if (more) token_derived(tables(cur ^ 1), tid);
+            if constexpr (LD::h_single)
+                store_tile<OutT>(acc, y_head(h), NHP, id.w, NT16 - 1 - id.w, id.l16, id.g4);
         } else {
             store_tile<OutT>(acc, y_head(h), NHP, id.w, NT16 - 1 - id.w, id.l16, id.g4);
         }
         __syncthreads();
     }
-    if (h_begin < h_end && w < MW) store_tile<OutT>(acc, y_head(h_end - 1), NHP, I0, I1, l16, g4);
+    if (!LD::h_single && h_begin < h_end && w < MW)
+        store_tile<OutT>(acc, y_head(h_end - 1), NHP, I0, I1, l16, g4);
 }
 
 // ---------------------------------------------------------------------------
@@ -1527,12 +1570,12 @@ hipError_t launch_f32_in(const Problem &p, int HB, int nhb, int64_t blocks, cons
     return hipGetLastError();
 }
 
-template <int T, typename OutT>
+template <int T, int N, typename OutT>
 hipError_t launch_bf16_async(const Problem &p, int HB, int nhb, int64_t blocks, const void *x,
                              const void *B, const void *C, const float *CB, G2View G2, const float *DT, const float *D,
                              const float *H, void *y, hipStream_t stream, const LaunchEvents &ev) {
-    constexpr auto kern = k4_chunk_out_bf16_async<T, OutT>;
-    constexpr size_t lds = AsyncLds<T>::total;
+    constexpr auto kern = k4_chunk_out_bf16_async<T, N, OutT>;
+    constexpr size_t lds = AsyncLds<T, N>::total;
     if (allow_lds<kern>(lds) != hipSuccess) return hipErrorInvalidValue;
     launch_kernel(kern, dim3((unsigned)blocks), dim3(2 * T), lds, stream, ev,
                   static_cast<const uint16_t *>(x), CB, static_cast<const uint16_t *>(C), G2.hi,
@@ -1552,9 +1595,14 @@ hipError_t launch_tp(const Problem &p, const Plan &plan, const void *x, const vo
     const int64_t blocks = p.batch * p.nchunks * p.ngroups * nhb;
     if (blocks == 0) return hipSuccess;
     if constexpr (sizeof(InT) == 2) {
-        if constexpr (P == acfg::P)
-            if (uses_cb_tiles(p))
-                return launch_bf16_async<T, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
+        if constexpr (P == acfg::P) {
+            if (uses_cb_tiles(p) && p.dstate == 128)
+                return launch_bf16_async<T, 128, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
+            if constexpr (T == 256)
+                if (uses_cb_tiles(p) && p.dstate == 256)
+                    return launch_bf16_async<T, 256, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y,
+                                                           stream, ev);
+        }
         if (p.dstate <= 128)
             return launch_bf16_in<T, P, 4, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);
         return launch_bf16_in<T, P, 8, OutT>(p, HB, nhb, blocks, x, B, C, CB, G2, DT, D, H, y, stream, ev);

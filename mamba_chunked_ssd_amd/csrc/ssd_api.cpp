@@ -157,13 +157,15 @@ Plan make_plan(const Problem &p) {
     Plan plan;
     plan.k2_heads_per_block = pick_heads_per_block(p, chunk_state_blocks_per_cu(p) * kNumCUs, 1.0);
     plan.k4_heads_per_block = pick_heads_per_block(p, kNumCUs, 1.0);
-    // The bf16 chunk output at chunk 256 with dstate > 128 re-reads the
-    // chunk's C rows (T x dstate bf16: 128 KiB at dstate 256) in every head.
-    // A chunk's blocks are consecutive, so they run at the same time on one
-    // XCD; with at least four of them C is read from that XCD's L2 instead of
-    // from memory for each head.  Measured on MI355X (65 536 tokens, 32 heads,
-    // dstate 256): 8 heads per block 477-514 us against 521-540 us with 32.
-    if (p.bf16 && p.chunk == 256 && p.dstate > 128 && p.heads_per_group >= 4)
+    // The general bf16 chunk output at chunk 256 with dstate > 128 re-reads
+    // the chunk's C rows (T x dstate bf16: 128 KiB at dstate 256) in every
+    // head.  A chunk's blocks are consecutive, so they run at the same time on
+    // one XCD; with at least four of them C is read from that XCD's L2 instead
+    // of from memory for each head.  Measured on MI355X with that kernel
+    // (65 536 tokens, 32 heads, headdim 64, dstate 256): 8 heads per block
+    // 477-514 us against 521-540 us with 32.  The kernel with asynchronous
+    // copies (uses_cb_tiles) keeps C in registers and needs no such cap.
+    if (p.bf16 && p.chunk == 256 && p.dstate > 128 && p.heads_per_group >= 4 && !uses_cb_tiles(p))
         plan.k4_heads_per_block =
             std::min<int>(plan.k4_heads_per_block, (int)((p.heads_per_group + 3) / 4));
     // The fused state launch (bf16) walks the chunks of one (batch, head,

@@ -35,11 +35,14 @@ struct Plan {
 
 Plan make_plan(const Problem &p);
 
-// bf16 problems with headdim 64 and dstate 128 take the chunk-output kernel
-// with asynchronous copies; it reads the chunk's C B^T tiles, which stage 3
-// writes once per (batch, chunk, group) into the workspace: cb_slots(T) tiles
-// of 64 lanes x 4 floats each (the layout is described in include/ssd.h).
-inline bool uses_cb_tiles(const Problem &p) { return p.bf16 && p.headdim == 64 && p.dstate == 128; }
+// bf16 problems with headdim 64 and dstate 128, or dstate 256 at chunk 256,
+// take the chunk-output kernel with asynchronous copies; it reads the chunk's
+// C B^T tiles, which stage 3 writes once per (batch, chunk, group) into the
+// workspace: cb_slots(T) tiles of 64 lanes x 4 floats each (the layout is
+// described in include/ssd.h).
+inline bool uses_cb_tiles(const Problem &p) {
+    return p.bf16 && p.headdim == 64 && (p.dstate == 128 || (p.dstate == 256 && p.chunk == 256));
+}
 inline int64_t cb_slots(int64_t T) { return (T / 32) * (T / 16 + 2); }
 
 // Each launcher enqueues one kernel on `stream` and returns hipSuccess or the

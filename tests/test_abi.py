@@ -119,10 +119,14 @@ def test_workspace_size_formula(lib):
             assert lay.w == 3 * up(seq) and lay.s == 4 * up(seq)
             assert (lay.h == lay.s) != own_h
             assert lay.cb == want - up(cb)
-    # no tiles for other head / state sizes
-    for kw in (dict(headdim=32), dict(dstate=64)):
-        lay = ssd.workspace_layout(shape(**kw), 256)
+    # no tiles for other head / state sizes; dstate 256 has them at chunk 256 only
+    for kw, T in ((dict(headdim=32), 256), (dict(dstate=64), 256), (dict(dstate=256), 128),
+                  (dict(dstate=256, dtype="f32"), 256)):
+        lay = ssd.workspace_layout(shape(**kw), T)
         assert lay.cb == lay.total
+    lay = ssd.workspace_layout(shape(dstate=256), 256)
+    nc = -(-1000 // 256)
+    assert lay.total - lay.cb == (2 * nc * 2 * 8 * 18 * 1024 + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("bad", [

@@ -41,9 +41,11 @@ STAGE_SHAPES = [
     (1, 600, 8, 64, 128, 1, 128),
     (2, 1000, 6, 64, 128, 2, 256),
     # chunk 256 with dstate > 128 or headdim 128: the chunk output re-reads C
-    # per head and copies h_c asynchronously; ragged tails, dstate not a
-    # multiple of 32
+    # per head and copies h_c asynchronously (bf16 headdim 64 / dstate 256:
+    # the kernel with asynchronous copies and a single h_c buffer); ragged
+    # tails, dstate not a multiple of 32
     (1, 389, 3, 64, 144, 1, 256),
+    (2, 600, 2, 64, 256, 1, 256),
     (1, 700, 2, 32, 256, 1, 256),
     (1, 300, 2, 128, 96, 1, 256),
 ]
@@ -68,10 +70,11 @@ def check_stages(inp, dtype, T, plan=None, label=""):
     # chunk-state weights exp(G_last - G_t) dt_t (fp64 exponent, fp32 exp2)
     Wref = oracle.chunk_state_weights(inp["dt"], inp["A"], T)
     assert nerr(out["W"], Wref) < 1e-5, ("W", nerr(out["W"], Wref))
-    # C B^T tiles (bf16, headdim 64, dstate 128): fp32 sums of exact bf16
-    # products, lower block triangle (blocks past the diagonal are zero).
-    # Bound per entry: n fp32 additions, |err| <= n 2^-24 sum_k |C_ik B_jk|.
-    if dtype == "bf16" and p == 64 and n == 128:
+    # C B^T tiles (bf16, headdim 64, dstate 128, or 256 at chunk 256): fp32
+    # sums of exact bf16 products, lower block triangle (blocks past the
+    # diagonal are zero).  Bound per entry: n fp32 additions,
+    # |err| <= n 2^-24 sum_k |C_ik B_jk|.
+    if dtype == "bf16" and p == 64 and (n == 128 or (n == 256 and T == 256)):
         blk = np.arange(T) // 16
         lower = (blk[:, None] >= blk[None, :])
         cb = oracle.chunk_cb(inp["B"], inp["C"], T) * lower
@@ -130,6 +133,8 @@ MULTIHEAD_CASES = [
     ((1, 520, 8, 128, 256, 2, 128), 4, 3),
     ((1, 389, 6, 64, 144, 1, 256), 2, 4),
     ((1, 700, 6, 32, 256, 1, 256), 5, 2),
+    ((1, 700, 8, 64, 256, 1, 256), 3, 3),
+    ((2, 300, 5, 64, 256, 1, 256), 2, 5),
     ((1, 300, 6, 128, 96, 1, 256), 3, 6),
     ((2, 130, 8, 128, 80, 2, 64), 2, 3),
     ((1, 1000, 12, 64, 64, 1, 128), 6, 5),
@@ -159,8 +164,8 @@ DEFAULT_MULTIHEAD = [
     ((2, 2048, 80, 64, 128, 1, 256), "f32", 2, 3),
     ((2, 1024, 64, 128, 256, 8, 128), "f32", 2, 3),
     ((2, 1024, 64, 128, 256, 8, 128), "bf16", 2, 3),
-    # chunk 256 with dstate 256 (the chunk output re-reads C per head): at
-    # least four blocks per chunk
+    # chunk 256 with dstate 256 (bf16: the chunk output with a single h_c
+    # buffer)
     ((1, 4096, 32, 64, 256, 1, 256), "bf16", 1, 2),
 ]
 
@@ -253,13 +258,14 @@ def test_grouped_workload_full_size_by_blocks():
 
 
 @pytest.mark.parametrize("T", [64, 256])
-@pytest.mark.parametrize("pn", [(64, 128), (32, 256), (128, 96)], ids=lambda v: "p%d_n%d" % v)
+@pytest.mark.parametrize("pn", [(64, 128), (64, 256), (32, 256), (128, 96)], ids=lambda v: "p%d_n%d" % v)
 def test_bf16_y_output_is_rounded_result(T, pn):
     """A bf16 y is the fp32 result rounded once: per element within the bf16
     unit roundoff 2^-8 (8 significant bits) of |y| plus the fp32 path's own
-    error, bounded here by 1e-3 rms(y).  Headdim 64 / dstate 128 takes the
-    chunk-output kernel with asynchronous copies; the other two the general
-    bf16 kernel (at chunk 256 the variant that re-reads C per head)."""
+    error, bounded here by 1e-3 rms(y).  Headdim 64 / dstate 128 (and 256 at
+    chunk 256) takes the chunk-output kernel with asynchronous copies; the
+    others the general bf16 kernel (at chunk 256 the variant that re-reads C
+    per head)."""
     p, n = pn
     w = si.small(dtype="bf16", batch=2, seqlen=600, nheads=4, headdim=p, dstate=n, ngroups=1,
                  chunk_size=T, dt_mu=-2.0, init_std=0.1, seed=11)
