@@ -43,14 +43,16 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, y dtype, stage, state path): (sources, sha256[:16], FETCH KiB, WRITE KiB)
     ("mamba2_2p7b_layer_bf16", "f32", "chunk_out", "fused"): (
-        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'e0b38472eef460b1', 45015.9, 81961.0),
+        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'a6a4318efe91604f', 45009.5, 81957.0),
     ("mamba2_2p7b_layer_bf16", "f32", "chunk_out", "split"): (
-        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'e0b38472eef460b1', 45015.9, 81960.0),
+        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'a6a4318efe91604f', 45009.5, 81958.0),
     ("mamba2_2p7b_layer_bf16", "f32", "chunk_state", "fused"): (
-        ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), 'd335e9eacd803fb6', 24143.0, 48386.0),
+        ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), '54391ad12670190e', 24174.8, 48388.2),
+    ("long_seq_bf16", "f32", "chunk_out", "split"): (
+        ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'a6a4318efe91604f', 453119.5, 596848.0),
     # backward (the y dtype and state path do not apply)
     ("mamba2_2p7b_layer_bf16", None, "bwd:dC_pass", None): (
-        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h', 'ssd_internal.h'), '6b0e4799ddeb3f4a', 85605.8, 50688.0),
+        ('kb_pass.h', 'kb_pass_c.hip', 'kb_pass_inst.h', 'ssd_device.h', 'ssd_internal.h'), '6e517063a58e48e9', 85605.8, 50688.0),
 }
 
 
