@@ -1,12 +1,12 @@
 // k_cb_tiles.h -- the C B^T tiles that the chunk output with asynchronous
 // copies reads (bf16 inputs, headdim 64, dstate 128, or dstate 256 at chunk
-// 256; uses_cb_tiles), computed by extra
-// blocks at the front of the launch that carries the state across chunks
-// (the state-passing launch, or the fused state launch): a little MFMA work
-// that depends only on B and C, so it runs beside the memory-bound state
-// stream instead of on the chunk output's critical path ("Accelerating
-// Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA CUDA Tile",
-// section "Mamba-2 architecture": the C B^T factor of the chunk output).
+// 256; uses_cb_tiles), computed by extra blocks at the front of the launch that
+// carries the state across chunks (the state-passing launch, or the fused state
+// launch): a little MFMA work that depends only on B and C, so it runs beside
+// the memory-bound state stream instead of on the chunk output's critical path
+// ("Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+// CUDA Tile", section "Mamba-2 architecture": the C B^T factor of the chunk
+// output).
 #pragma once
 
 #include "ssd_device.h"
@@ -14,16 +14,17 @@
 
 namespace ssd {
 
-// C B^T tiles for the chunk-output stage (bf16 B and C, dstate N = 128 or
-// 256, a template argument): tile (w, k) of (batch, chunk, group) is the 16 x 16 block (I, J) of
-// S_ij = C_i . B_j that the chunk output's wave w keeps in its slot k: I = w,
-// J = k for k < (w + 2) & ~1, else I = T/16 - 1 - w and J = k minus that.
-// N / 32 MFMAs over dstate, loaded and issued 128 dstate entries at a time
-// (the same registers at either N), in the MFMA output layout (lane 16 q + m
-// holds S_{16I+m, 16J+4q+r}, r = 0..3), one float4 per lane, 1 KiB per tile.
-// Blocks past the diagonal are written as zero.  Each wave takes kCbPerWave
-// tiles; these blocks run at the front of a state launch's grid, beside its
-// memory-bound work.  bid: the block's index among the ncb tile blocks.
+// C B^T tiles for the chunk-output stage (bf16 B and C, dstate N = 128 or 256,
+// a template argument): tile (w, k) of (batch, chunk, group) is the 16 x 16
+// block (I, J) of S_ij = C_i . B_j that the chunk output's wave w keeps in its
+// slot k: I = w, J = k for k < (w + 2) & ~1, else I = T/16 - 1 - w and J = k
+// minus that.  N / 32 MFMAs over dstate, loaded and issued 128 dstate entries
+// at a time (the same registers at either N), in the MFMA output layout
+// (lane 16 q + m holds S_{16I+m, 16J+4q+r}, r = 0..3), one float4 per lane,
+// 1 KiB per tile.  Blocks past the diagonal are written as zero.  Each wave takes
+// kCbPerWave tiles; these blocks run at the front of a state launch's grid,
+// beside its memory-bound work.  bid: the block's index among the ncb tile
+// blocks.
 constexpr int kCbPerWave = 4;
 
 // Blocks of 256 threads that compute `ntiles` tiles.
