@@ -7,11 +7,15 @@
 // and stored.  It is kept in base-2 units (G2 = log2(e) G) so that the later
 // stages use the native exp2.
 //
-// Design for gfx950: one wave per (batch, chunk, head), four heads per block,
-// so a layer launches batch x nchunks x nheads / 4 blocks (hundreds) rather
-// than one block per 16 heads.  Every lane sums T/64 consecutive tokens
-// serially, the 64 lane totals are scanned with wave shuffles, and each lane
-// adds its exclusive prefix.  The sum runs in fp64 and is stored as two
+// Design for gfx950: one wave per (batch, chunk, head), eight heads per block.
+// The block first copies its chunk's dt for its eight heads into LDS with
+// consecutive threads on consecutive heads of one token (dt is token-major,
+// so a wave's load covers 8 tokens x 8 heads instead of 64 tokens of one head
+// scattered over 64 rows); then every lane sums T/64 consecutive tokens of its
+// wave's head serially, the 64 lane totals are scanned with wave shuffles,
+// and each lane adds its exclusive prefix.  (Measured on MI355X: 13.3 -> 11.2
+// us at 65 536 tokens x 32 heads, 24.1 -> 20.5 us for the grouped fp32
+// workload, unchanged at the 2.7B-shaped layer, where the launch dominates.)  The sum runs in fp64 and is stored as two
 // floats, G2 = hi + lo: within a chunk |G2| can reach thousands while the
 // later stages exponentiate differences G2_i - G2_j of nearby tokens, and
 // (hi_i - hi_j) + (lo_i - lo_j) keeps those differences accurate to fp32
@@ -33,7 +37,7 @@
 namespace ssd {
 namespace {
 
-constexpr int kHeadsPerBlock = 4;
+constexpr int kHeadsPerBlock = 8;
 
 template <typename Tin>
 __device__ __forceinline__ float load_dt(const Tin *p);
@@ -52,13 +56,24 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void k1_cumsum(
     const int h = blockIdx.y * kHeadsPerBlock + (threadIdx.x >> 6);
     const int64_t b = blockIdx.z;
     const int lane = threadIdx.x & 63;
+    // the chunk's dt of this block's heads, [head][token]; tokens past seqlen
+    // and heads past nheads as 0
+    __shared__ float dts[kHeadsPerBlock][T + 1];
+    {
+        const int h0 = blockIdx.y * kHeadsPerBlock;
+        for (int idx = threadIdx.x; idx < T * kHeadsPerBlock; idx += 64 * kHeadsPerBlock) {
+            const int tt = idx / kHeadsPerBlock, hh = idx % kHeadsPerBlock;
+            const int64_t t = (int64_t)c * T + tt;
+            dts[hh][tt] = (t < seqlen && h0 + hh < nheads) ? load_dt(dt + (b * seqlen + t) * nheads + h0 + hh) : 0.f;
+        }
+    }
+    __syncthreads();
     if (h >= nheads) return;  // wave-uniform; no barrier follows
 
     const int64_t t0 = (int64_t)c * T + lane * E;
     float d[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        d[e] = (t0 + e < seqlen) ? load_dt(dt + (b * seqlen + t0 + e) * nheads + h) : 0.f;
+    for (int e = 0; e < E; ++e) d[e] = dts[threadIdx.x >> 6][lane * E + e];
     float hi[E], lo[E], wt[E];
     chunk_cumsum_wave<E>(d, A[h], lane, hi, lo, wt);
     const int64_t base = (b * nheads + h) * Lp + t0;
