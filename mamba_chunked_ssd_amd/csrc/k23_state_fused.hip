@@ -67,15 +67,12 @@ struct FusedCfg {
     static constexpr int KP = XB / 1024 + BB / 1024 + 1;  // producer copy instructions per slab
     static constexpr int SPC = T / kSlab;       // slabs per chunk
     static constexpr int MT = NT / 16;          // 16-column dstate tiles
-    // ring depth: as deep as LDS allows while three blocks share a CU (at
-    // least 3 slots, which at headdim 128 leaves room for two), at most 8,
-    // with every wait immediate (RING - 2) * KP in the vmcnt field.  Three
-    // blocks of 3 slots ran the 64-column tiles faster than two of 4 (2.7B
-    // layer 37.0 against 38.3 us, 8 x 4096 tokens 309 against 315 us).
+    // ring depth: as deep as LDS allows while two blocks share a CU, at most
+    // 8 slots, with every wait immediate (RING - 2) * KP in the vmcnt field
     static constexpr int pick_ring() {
         int best = 3;
         for (int r = 3; r <= 8; ++r)
-            if (3 * r * SLOT <= (int)kLdsPerCu && (r - 2) * KP <= 63) best = r;
+            if (2 * r * SLOT <= (int)kLdsPerCu && (r - 2) * KP <= 63) best = r;
         return best;
     }
     static constexpr int RING = pick_ring();

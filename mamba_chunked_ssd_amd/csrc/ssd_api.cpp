@@ -173,10 +173,11 @@ Plan make_plan(const Problem &p) {
     // through memory but keeps only that many blocks busy.  Measured on
     // MI355X it wins with two or more blocks per CU (8 x 4096 tokens: 1280
     // blocks, 281-300 us against 334-340 us for the two split launches),
-    // ties with one to two (2.7B-shaped layer: 320 blocks, 86.0 against
-    // 86.2 us per forward pass, but 55.6 against 48.9 us from a cold cache)
-    // and loses below (65 536 tokens, 32 heads, dstate 256: 128 blocks, 666
-    // us against 426 us).
+    // is faster warm but slower cold with one to two (2.7B-shaped layer: 320
+    // blocks, 77.5 against 79.4 us per forward pass with steps back to back,
+    // 98-99 against 91-94 us summed over the stages from a cold cache) and
+    // loses below (65 536 tokens, 32 heads, dstate 256: 128 blocks, 666 us
+    // against 426 us).
     plan.fused_cols = 64;
     plan.fused_state = p.nchunks > 0 && state_fused_supported(p, 64) &&
                        p.batch * p.nheads * (p.dstate / 64) >= 2 * kNumCUs;
