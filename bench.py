@@ -48,6 +48,8 @@ MEASURED_TRAFFIC = {
         ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'a6a4318efe91604f', 45009.5, 81958.0),
     ("mamba2_2p7b_layer_bf16", "f32", "chunk_state", "fused"): (
         ('k23_state_fused.hip', 'k_cb_tiles.h', 'ssd_device.h'), '9fcae62bce07bffa', 24185.4, 48387.9),
+    ("grouped_f32", "f32", "chunk_out", "split"): (
+        ('k4_chunk_out.h', 'k4_out_f32.hip', 'ssd_device.h'), '4ceaad19d8c20f43', 5792109.0, 2097153.0),
     ("long_seq_bf16", "f32", "chunk_out", "split"): (
         ('k4_chunk_out.h', 'k4_out_bf16_f32.hip', 'ssd_device.h'), 'a6a4318efe91604f', 453119.5, 596848.0),
     # backward (the y dtype and state path do not apply)
