@@ -14,7 +14,8 @@ dominant kernel, and the fp64 CPU oracle timed on this host as a reference
 baseline.  Beside the forward's figures the line carries the recurrent decode
 step ("decode") and the backward pass ("backward": ssd_chunk_scan_bwd on the
 same workload with seeded upstream gradients, its stages and the roofline of
-its slowest stage).
+its slowest stage, and the same calls reading one forward call's kept
+chunk-start states instead of recomputing them).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -410,6 +411,30 @@ def backward_bench(hip, w, inp, t, dev, steps=10, warmup=3) -> dict:
     hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     hip.lib.hipEventSynchronize(ctypes.c_void_p(e1))
     total_us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+
+    # the same calls reading the chunk-start states that one forward call
+    # kept in its workspace (ssd_chunk_scan_bwd_saved) instead of
+    # recomputing them
+    kshape = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype, True)
+    fws = torch.empty(ssd.workspace_size(kshape, w.chunk_size), dtype=torch.uint8, device=dev)
+    ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=w.chunk_size,
+                       initial_states=t["h0"], workspace=fws, keep_intermediates=True)
+
+    def call_saved():
+        return ssd.chunk_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], dy, chunk_size=w.chunk_size,
+                                  initial_states=t["h0"], d_final_states=dfin, workspace=ws,
+                                  saved_workspace=fws)
+
+    for _ in range(warmup):
+        call_saved()
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    for _ in range(steps):
+        call_saved()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    hip.lib.hipEventSynchronize(ctypes.c_void_p(e1))
+    saved_us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    del fws
     hip.destroy(e0)
     hip.destroy(e1)
     evs = [[hip.event() for _ in range(2 * len(names))] for _ in range(steps)]
@@ -443,6 +468,10 @@ def backward_bench(hip, w, inp, t, dev, steps=10, warmup=3) -> dict:
         "unit": "tokens/s",
         "us_per_step": round(total_us, 2),
         "steps": steps,
+        "saved_states": {"value": round(w.tokens / (saved_us * 1e-6), 1), "unit": "tokens/s",
+                         "us_per_step": round(saved_us, 2),
+                         "note": "ssd_chunk_scan_bwd_saved: the chunk-start states read from one forward "
+                                 "call's workspace (SSD_FLAG_KEEP_INTERMEDIATES), not recomputed"},
         "stages": stages,
         "dominant": dom,
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,

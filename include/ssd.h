@@ -360,6 +360,36 @@ ssd_status ssd_chunk_scan_bwd_profiled(const ssd_shape *shape,
                                        float *d_initial_states,
                                        void *workspace, size_t workspace_bytes, void *stream,
                                        void *const *stage_events);
+/* As ssd_chunk_scan_bwd, reusing the chunk-start states h_c of a forward
+ * call instead of recomputing them (the same gradients of the same section
+ * of the pages; stages 1 and 2 launch nothing).
+ *   fwd_workspace        the workspace of a forward call (any
+ *                        ssd_chunk_scan_fwd entry point, any plan) made on
+ *                        the same x, dt, A, B, initial_states and chunk size,
+ *                        with SSD_FLAG_KEEP_INTERMEDIATES in its shape's
+ *                        flags, and not written since; 256-byte aligned.  Its
+ *                        H region (ssd_chunk_scan_fwd_workspace_layout of
+ *                        that shape) is read, nothing in it is written, and
+ *                        it must not overlap an output or `workspace`.
+ *                        NULL => SSD_ERROR_INVALID_VALUE.
+ *   fwd_workspace_bytes  at least that layout's total, else
+ *                        SSD_ERROR_WORKSPACE.
+ *   stage_events         NULL, or 2 * SSD_BWD_STAGES events as in
+ *                        ssd_chunk_scan_bwd_profiled (stages 1 and 2 record
+ *                        their pairs back to back).
+ * Everything else as ssd_chunk_scan_bwd, whose workspace it still takes.  The
+ * library cannot check that fwd_workspace belongs to these inputs: states of
+ * other inputs give the gradients of that other forward pass's states. */
+ssd_status ssd_chunk_scan_bwd_saved(const ssd_shape *shape,
+                                    const void *x, const void *dt, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    int64_t chunk_size, const float *initial_states,
+                                    const void *dy, const float *d_final_states,
+                                    const void *fwd_workspace, size_t fwd_workspace_bytes,
+                                    float *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                                    float *d_initial_states,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *stage_events);
 
 /* Static, human-readable description of a status code. */
 const char *ssd_status_string(ssd_status status);

@@ -52,6 +52,7 @@ EXPORTS = [
     "ssd_chunk_scan_bwd_workspace_size",
     "ssd_chunk_scan_bwd",
     "ssd_chunk_scan_bwd_profiled",
+    "ssd_chunk_scan_bwd_saved",
     "ssd_status_string",
     "ssd_version",
 ]
@@ -171,6 +172,10 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
         lib.ssd_chunk_scan_bwd_profiled.argtypes = bwd_args + [ctypes.POINTER(ctypes.c_void_p)]
         lib.ssd_chunk_scan_bwd_profiled.restype = ctypes.c_int
+        # as bwd_args, with the forward workspace and its size after d_final_states
+        lib.ssd_chunk_scan_bwd_saved.argtypes = bwd_args[:11] + [vp, sz] + bwd_args[11:] + [
+            ctypes.POINTER(ctypes.c_void_p)]
+        lib.ssd_chunk_scan_bwd_saved.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.argtypes = []
@@ -356,7 +361,7 @@ def bwd_workspace_size(shape: Shape, chunk_size: int) -> int:
 
 def chunk_scan_bwd(x, dt, A, B, C, D, dy, chunk_size: int = 256, initial_states=None,
                    d_final_states=None, *, want_dD: bool = True, want_d_initial: bool = True,
-                   workspace=None, stream=None, events=None):
+                   workspace=None, stream=None, events=None, saved_workspace=None):
     """Gradients through :func:`chunk_scan_fwd` (``ssd_chunk_scan_bwd``).
 
     Inputs as passed to :func:`chunk_scan_fwd`, plus ``dy`` (dL/dy, the input
@@ -364,7 +369,10 @@ def chunk_scan_bwd(x, dt, A, B, C, D, dy, chunk_size: int = 256, initial_states=
     ``d_final_states`` (dL/dh_final, float32).  Returns a dict of float32
     tensors ``dx, ddt, dA, dB, dC`` and, when requested, ``dD`` and
     ``d_initial_states``.  ``events``: 24 raw hipEvent_t handles (a start and
-    stop per stage of :data:`BWD_STAGES`).
+    stop per stage of :data:`BWD_STAGES`).  ``saved_workspace``: the workspace
+    of a :func:`chunk_scan_fwd` call on the same inputs made with
+    ``keep_intermediates=True``; its chunk-start states are then read instead
+    of recomputed (``ssd_chunk_scan_bwd_saved``).
     """
     torch = _torch()
     lib = load_library()
@@ -413,13 +421,21 @@ def chunk_scan_bwd(x, dt, A, B, C, D, dy, chunk_size: int = 256, initial_states=
             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
             _ptr(out.get("d_initial_states")), _ptr(workspace), workspace.numel() * workspace.element_size(),
             ctypes.c_void_p(s)]
-    if events is None:
-        st = lib.ssd_chunk_scan_bwd(*args)
-        where = "ssd_chunk_scan_bwd"
-    else:
+    ev = None
+    if events is not None:
         if len(events) != 2 * len(BWD_STAGES):
             raise ValueError("events: a (start, stop) pair for each of the %d stages" % len(BWD_STAGES))
         ev = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
+    if saved_workspace is not None:
+        if saved_workspace.device != dev:
+            raise ValueError("saved_workspace must be on %s" % dev)
+        saved = [_ptr(saved_workspace), saved_workspace.numel() * saved_workspace.element_size()]
+        st = lib.ssd_chunk_scan_bwd_saved(*(args[:11] + saved + args[11:]), ev)
+        where = "ssd_chunk_scan_bwd_saved"
+    elif ev is None:
+        st = lib.ssd_chunk_scan_bwd(*args)
+        where = "ssd_chunk_scan_bwd"
+    else:
         st = lib.ssd_chunk_scan_bwd_profiled(*args, ev)
         where = "ssd_chunk_scan_bwd_profiled"
     if st != 0:

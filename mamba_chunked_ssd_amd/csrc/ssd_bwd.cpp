@@ -5,7 +5,8 @@
 // Stages (the kernels are described where they are defined):
 //   0-2   the forward's cumsum (plus the adjoint weights exp(G)), chunk
 //         states and state passing, recomputed: the chunk-start states h_c
-//         and the final state;
+//         and the final state (with a forward call's kept states, stage 0
+//         only, h_c read from that call's workspace);
 //   3     u_c = sum_r exp(G_r) dy_r C_r^T with the forward's chunk-state
 //         kernel (dy as x, C as B);
 //   4     the reverse carry of the state gradient (kb_aux.hip);
@@ -158,8 +159,8 @@ ssd_status prepare(const ssd_shape *shape, int64_t chunk, Problem *p, BwdPlan *q
 ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const float *A, const void *B,
                     const void *C, const float *D, int64_t chunk_size, const float *init, const void *dy,
                     const float *dfinal, float *dx, float *ddt, float *dA, float *dB, float *dC,
-                    float *dD, float *dinit, void *workspace, size_t workspace_bytes, void *stream_handle,
-                    void *const *events) {
+                    float *dD, float *dinit, void *workspace, size_t workspace_bytes, const void *fwd_ws,
+                    size_t fwd_ws_bytes, void *stream_handle, void *const *events) {
     Problem p;
     BwdPlan q;
     BwdLayout lay;
@@ -179,6 +180,20 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
     if (A == nullptr || dA == nullptr) return SSD_ERROR_INVALID_VALUE;
     if (lay.total > 0 && p.batch > 0 && workspace == nullptr) return SSD_ERROR_WORKSPACE;
     if (workspace_bytes < lay.total) return SSD_ERROR_WORKSPACE;
+    // a forward call's kept intermediates: its chunk-start states h_c, at the
+    // offset of the forward layout with SSD_FLAG_KEEP_INTERMEDIATES
+    const unsigned char *saved_h = nullptr;
+    size_t saved_h_bytes = 0;
+    if (fwd_ws != nullptr) {
+        ssd_shape keep = *shape;
+        keep.flags = SSD_FLAG_KEEP_INTERMEDIATES;
+        ssd_workspace_layout fl;
+        if (ssd_chunk_scan_fwd_workspace_layout(&keep, chunk_size, &fl) != SSD_OK) return SSD_ERROR_INVALID_VALUE;
+        if (fwd_ws_bytes < fl.total) return SSD_ERROR_WORKSPACE;
+        if (!aligned(fwd_ws, kAlign)) return SSD_ERROR_MISALIGNED;
+        saved_h = static_cast<const unsigned char *>(fwd_ws) + fl.h;
+        saved_h_bytes = (size_t)p.batch * p.nheads * p.nchunks * p.headdim * p.dstate * sizeof(float);
+    }
     if (events != nullptr)
         for (int i = 0; i < 2 * SSD_BWD_STAGES; ++i)
             if (events[i] == nullptr) return SSD_ERROR_INVALID_VALUE;
@@ -191,7 +206,8 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
     const Range ins[] = {range_of(x, x_elems * esz),  range_of(dt, dt_elems * esz),
                          range_of(A, hd_bytes),       range_of(B, bc_elems * esz),
                          range_of(C, bc_elems * esz), range_of(D, D ? hd_bytes : 0),
-                         range_of(init, init ? st_bytes : 0), range_of(dy, x_elems * esz), range_of(dfinal, dfinal ? st_bytes : 0)};
+                         range_of(init, init ? st_bytes : 0), range_of(dy, x_elems * esz), range_of(dfinal, dfinal ? st_bytes : 0),
+                         range_of(saved_h, saved_h_bytes)};
     const Range outs[] = {range_of(dx, x_elems * 4),        range_of(ddt, dt_elems * 4),
                           range_of(dA, hd_bytes),           range_of(dB, bc_elems * 4),
                           range_of(dC, bc_elems * 4),       range_of(dD, dD ? hd_bytes : 0),
@@ -224,7 +240,7 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
     const G2View G2v{G2.hi, G2.lo};
     float *DTf = fp(lay.dt);
     float *S = fp(lay.s);
-    float *Hs = fp(lay.h);
+    const void *Hs = saved_h != nullptr ? static_cast<const void *>(saved_h) : static_cast<const void *>(fp(lay.h));
     void *E = ws + lay.e;
     float *Zp = fp(lay.zp);
 
@@ -233,10 +249,15 @@ ssd_status backward(const ssd_shape *shape, const void *x, const void *dt, const
         const Plan fplan = make_plan(p);
         if (launch_chunk_cumsum(p, dt, A, G2, DTf, fp(lay.w), stream, events_of(0), fp(lay.wb)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
-        if (launch_chunk_state(p, fplan, x, B, fp(lay.w), S, stream, events_of(1)) != hipSuccess)
+        if (saved_h == nullptr) {
+            if (launch_chunk_state(p, fplan, x, B, fp(lay.w), S, stream, events_of(1)) != hipSuccess)
+                return SSD_ERROR_LAUNCH;
+            if (launch_state_pass(p, S, fp(lay.h), G2v, init, nullptr, B, C, nullptr, stream, events_of(2)) !=
+                hipSuccess)
+                return SSD_ERROR_LAUNCH;
+        } else if (!skip(1) || !skip(2)) {
             return SSD_ERROR_LAUNCH;
-        if (launch_state_pass(p, S, Hs, G2v, init, nullptr, B, C, nullptr, stream, events_of(2)) != hipSuccess)
-            return SSD_ERROR_LAUNCH;
+        }
         // u_c into S's region (s_c has been consumed)
         if (launch_chunk_state(p, fplan, dy, C, fp(lay.wb), S, stream, events_of(3)) != hipSuccess)
             return SSD_ERROR_LAUNCH;
@@ -362,7 +383,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_shape *shape, const void *x, const void 
                               float *dA, float *dB, float *dC, float *dD, float *d_initial_states, void *workspace,
                               size_t workspace_bytes, void *stream) {
     return backward(shape, x, dt, A, B, C, D, chunk_size, initial_states, dy, d_final_states, dx, ddt, dA, dB, dC,
-                    dD, d_initial_states, workspace, workspace_bytes, stream, nullptr);
+                    dD, d_initial_states, workspace, workspace_bytes, nullptr, 0, stream, nullptr);
 }
 
 ssd_status ssd_chunk_scan_bwd_profiled(const ssd_shape *shape, const void *x, const void *dt, const float *A,
@@ -372,7 +393,19 @@ ssd_status ssd_chunk_scan_bwd_profiled(const ssd_shape *shape, const void *x, co
                                        size_t workspace_bytes, void *stream, void *const *stage_events) {
     if (stage_events == nullptr) return SSD_ERROR_INVALID_VALUE;
     return backward(shape, x, dt, A, B, C, D, chunk_size, initial_states, dy, d_final_states, dx, ddt, dA, dB, dC,
-                    dD, d_initial_states, workspace, workspace_bytes, stream, stage_events);
+                    dD, d_initial_states, workspace, workspace_bytes, nullptr, 0, stream, stage_events);
+}
+
+ssd_status ssd_chunk_scan_bwd_saved(const ssd_shape *shape, const void *x, const void *dt, const float *A,
+                                    const void *B, const void *C, const float *D, int64_t chunk_size,
+                                    const float *initial_states, const void *dy, const float *d_final_states,
+                                    const void *fwd_workspace, size_t fwd_workspace_bytes, float *dx, float *ddt,
+                                    float *dA, float *dB, float *dC, float *dD, float *d_initial_states,
+                                    void *workspace, size_t workspace_bytes, void *stream, void *const *stage_events) {
+    if (fwd_workspace == nullptr) return SSD_ERROR_INVALID_VALUE;
+    return backward(shape, x, dt, A, B, C, D, chunk_size, initial_states, dy, d_final_states, dx, ddt, dA, dB, dC,
+                    dD, d_initial_states, workspace, workspace_bytes, fwd_workspace, fwd_workspace_bytes, stream,
+                    stage_events);
 }
 
 }  // extern "C"

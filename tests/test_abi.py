@@ -376,3 +376,63 @@ def test_tune_rejects_before_any_device_work(lib):
     assert tune(T=96) == 2
     h = f()
     assert tune(init=h, fin=h) == 1   # the candidates would read each other's states
+
+
+def bwd_call(lib, s, T=256, saved=True, fwd_bytes=None, ws_bytes=None, **over):
+    """ssd_chunk_scan_bwd (saved=False) or ssd_chunk_scan_bwd_saved on fake
+    addresses; returns the status."""
+    f = Fake()
+    p = dict(x=f(), dt=f(), A=f(), B=f(), C=f(), D=f(), init=None, dy=f(), dfin=None, fwd=f(),
+             dx=f(), ddt=f(), dA=f(), dB=f(), dC=f(), dD=f(), dinit=None, ws=f())
+    p.update(over)
+    v = lambda k: None if p[k] is None else ctypes.c_void_p(p[k])  # noqa: E731
+    keep = ssd.make_shape(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups,
+                          "bf16" if s.dtype == 1 else "f32", True)
+    fb = ssd.workspace_size(keep, T) if fwd_bytes is None else fwd_bytes
+    wb = ssd.bwd_workspace_size(s, T) if ws_bytes is None else ws_bytes
+    head = [ctypes.byref(s), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), T, v("init"), v("dy"), v("dfin")]
+    tail = [v("dx"), v("ddt"), v("dA"), v("dB"), v("dC"), v("dD"), v("dinit"), v("ws"), wb, None]
+    if not saved:
+        return lib.ssd_chunk_scan_bwd(*head, *tail)
+    return lib.ssd_chunk_scan_bwd_saved(*head, v("fwd"), fb, *tail, None)
+
+
+@no_gpu
+def test_backward_rejects_before_launch(lib):
+    s = shape()
+    assert ssd.bwd_workspace_size(s, 256) > 0
+    for k in ("x", "dt", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC"):
+        assert bwd_call(lib, s, saved=False, **{k: None}) == 1, k
+    assert bwd_call(lib, s, saved=False, ws_bytes=ssd.bwd_workspace_size(s, 256) - 1) == 4
+    assert bwd_call(lib, s, saved=False, ws=None) == 4
+    assert bwd_call(lib, s, saved=False, T=96) == 2
+    assert bwd_call(lib, shape(keep=True), saved=False) == 1  # flags must be 0
+    f = Fake()
+    assert bwd_call(lib, s, saved=False, x=f(8)) == 3
+    out = f()
+    assert bwd_call(lib, s, saved=False, dB=out, dC=out) == 1  # outputs overlap
+
+
+@no_gpu
+def test_backward_with_saved_states_rejects_before_launch(lib):
+    s = shape()
+    keep = shape(keep=True)
+    need = ssd.workspace_size(keep, 256)
+    assert need > 0
+    assert bwd_call(lib, s, fwd=None) == 1
+    assert bwd_call(lib, s, fwd_bytes=need - 1) == 4
+    # the size a forward call without the flag needs is not enough at fp32
+    # (its H shares S's region there)
+    s32, k32 = shape(dtype="f32"), shape(dtype="f32", keep=True)
+    assert ssd.workspace_size(s32, 256) < ssd.workspace_size(k32, 256)
+    assert bwd_call(lib, s32, fwd_bytes=ssd.workspace_size(s32, 256)) == 4
+    f = Fake()
+    assert bwd_call(lib, s, fwd=f(16)) == 3
+    # the forward workspace is an input: it may not be an output or the workspace
+    w = f()
+    assert bwd_call(lib, s, fwd=w, ws=w) == 1
+    # an output inside the forward workspace's H region
+    h = f()
+    assert bwd_call(lib, s, fwd=h, dx=h + ssd.workspace_layout(keep, 256).h) == 1
+    assert bwd_call(lib, s, T=96) == 2
+    assert bwd_call(lib, shape(nheads=6, ngroups=4)) == 1

@@ -150,3 +150,50 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for k in runs[0]:
         assert torch.equal(runs[0][k], runs[1][k]), k
+
+
+# (dtype, forward plan or None for the default, batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
+SAVED_CASES = [
+    ("bf16", None, 2, 600, 8, 64, 128, 2, 256),     # the 2.7B layer's tile shape, ragged, grouped
+    ("bf16", "fused", 2, 600, 8, 64, 128, 2, 256),  # states from the fused state launch
+    ("f32", None, 1, 300, 4, 128, 48, 2, 128),      # fp32: H a region of its own only with the flag
+    ("bf16", None, 1, 129, 2, 32, 16, 1, 64),       # one token past a chunk
+]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=lambda c: "%s-%s-b%d-L%d-h%d-p%d-n%d-g%d-T%d" % c)
+def test_backward_from_saved_forward_states(case):
+    # the forward's kept chunk-start states in place of the recomputed ones:
+    # the gradients match the oracle's adjoint and the recomputing backward
+    dtype, plan, b, L, nh, p, n, g, T = case
+    w = si.small(dtype=dtype, batch=b, seqlen=L, nheads=nh, headdim=p, dstate=n, ngroups=g, chunk_size=T,
+                 dt_mu=-1.0, init_std=0.1, seed=2300 + L + n)
+    print("bwd saved case", case, flush=True)
+    inp = si.generate(w)
+    cot = si.cotangents(w)
+    t = to_device(inp, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dy = torch.from_numpy(cot["dy"]).cuda().to(tdt)
+    dfin = torch.from_numpy(cot["dfinal"]).cuda()
+    shape = ssd.make_shape(b, L, nh, p, n, g, dtype, True)
+    fws = torch.empty(ssd.workspace_size(shape, T), dtype=torch.uint8, device="cuda")
+    fplan = None if plan is None else ssd.make_plan(plan, 1, 1, 64)
+    ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=T, initial_states=t["h0"],
+                       workspace=fws, keep_intermediates=True, plan=fplan)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], dy)
+    kw = dict(chunk_size=T, initial_states=t["h0"], d_final_states=dfin)
+    saved = ssd.chunk_scan_bwd(*args, **kw, saved_workspace=fws)
+    plain = ssd.chunk_scan_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    got = {k: v.double().cpu().numpy() for k, v in saved.items()}
+    ref = oracle.scan_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                          cot["dy"], cot["dfinal"])
+    ref["d_initial_states"] = ref.pop("dh0")
+    _check(got, ref, dtype, str(case))
+    # the same states give the same gradients; the fused launch's states
+    # differ from the split path's in rounding only
+    for k in plain:
+        a, e = saved[k].double(), plain[k].double()
+        scale = max(float(e.pow(2).mean().sqrt()), 1e-30)
+        d = float((a - e).abs().max()) / scale
+        assert d <= (1e-3 if plan == "fused" else 1e-6), (k, d)
