@@ -363,8 +363,9 @@ ssd_status ssd_chunk_scan_bwd_profiled(const ssd_shape *shape,
 /* As ssd_chunk_scan_bwd, reusing the chunk-start states h_c of a forward
  * call instead of recomputing them (the same gradients of the same section
  * of the pages; stages 1 and 2 launch nothing).
- *   fwd_workspace        the workspace of a forward call (any
- *                        ssd_chunk_scan_fwd entry point, any plan) made on
+ *   fwd_workspace        the workspace of a forward call (an
+ *                        ssd_chunk_scan_fwd entry point that takes the
+ *                        caller's workspace, any plan) made on
  *                        the same x, dt, A, B, initial_states and chunk size,
  *                        with SSD_FLAG_KEEP_INTERMEDIATES in its shape's
  *                        flags, and not written since; 256-byte aligned.  Its
