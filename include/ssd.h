@@ -64,8 +64,9 @@ typedef enum {
 } ssd_status;
 
 /* Keep the per-chunk input states s_c and the chunk-start states h_c in two
- * separate workspace regions (tests read both).  Without it the state-passing
- * stage overwrites s_c with h_c in place. */
+ * separate workspace regions (tests read both; ssd_chunk_scan_bwd_saved reads
+ * h_c).  Without it the state-passing stage of fp32 problems overwrites s_c
+ * with h_c in place. */
 enum { SSD_FLAG_KEEP_INTERMEDIATES = 1u };
 
 typedef struct {
