@@ -197,3 +197,47 @@ def test_backward_from_saved_forward_states(case):
         scale = max(float(e.pow(2).mean().sqrt()), 1e-30)
         d = float((a - e).abs().max()) / scale
         assert d <= (1e-3 if plan == "fused" else 1e-6), (k, d)
+
+
+def test_backward_saved_with_stage_events():
+    # the saved-states call with a (start, stop) event pair per stage: the
+    # same gradients as without events; the two stages it skips record their
+    # pairs back to back
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2 * len(ssd.BWD_STAGES)):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        evs.append(h.value)
+    w = si.small(dtype="bf16", batch=1, seqlen=600, nheads=4, headdim=64, dstate=128, ngroups=1, chunk_size=256,
+                 dt_mu=-1.0, init_std=0.1, seed=2411)
+    inp = si.generate(w)
+    cot = si.cotangents(w)
+    t = to_device(inp, "bf16")
+    dy = torch.from_numpy(cot["dy"]).cuda().to(torch.bfloat16)
+    dfin = torch.from_numpy(cot["dfinal"]).cuda()
+    shape = ssd.make_shape(1, 600, 4, 64, 128, 1, "bf16", True)
+    fws = torch.empty(ssd.workspace_size(shape, 256), dtype=torch.uint8, device="cuda")
+    ssd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk_size=256, initial_states=t["h0"],
+                       workspace=fws, keep_intermediates=True)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], dy)
+    kw = dict(chunk_size=256, initial_states=t["h0"], d_final_states=dfin, saved_workspace=fws)
+    plain = ssd.chunk_scan_bwd(*args, **kw)
+    timed = ssd.chunk_scan_bwd(*args, **kw, events=evs)
+    torch.cuda.synchronize()
+    try:
+        for k in plain:
+            assert torch.equal(plain[k], timed[k]), k
+        ms = []
+        for i in range(len(ssd.BWD_STAGES)):
+            m = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(m), evs[2 * i], evs[2 * i + 1]) == 0
+            ms.append(m.value)
+        assert all(v >= 0 for v in ms), ms
+        assert ms[1] < 0.05 and ms[2] < 0.05, ms  # skipped: back-to-back records
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
